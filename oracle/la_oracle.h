@@ -1,0 +1,56 @@
+/*
+ * fp64 CPU oracle for causal linear attention (TEST INFRASTRUCTURE ONLY).
+ *
+ * Only the tests, the smoke check and the benchmark's CPU-baseline leg may
+ * call this library.  It shares no code or header with the HIP library.
+ *
+ * What it computes (per document and head, tokens t of that document only):
+ *     KV_t = sum_{s <= t} k_s^T v_s            (d x d, key index i, value index j)
+ *     o_t  = q_t . KV_t = sum_{s <= t} (q_t . k_s) v_s
+ * Linear attention without softmax, written with the "right product" and a
+ * recursively updated key-value product: "MiniMax-01技术报告解读（一）模型架构"
+ * (CSDN) and "MiniMax-01技术报告解读" (qingkelab), section 2.2 线性注意力.
+ * The state starts from kv_in (or zero) at every document start: packed
+ * samples are independent ("MiniMax-01技术报告解读", §3.2 item 1 数据打包 and
+ * item 4 变长特征支持).
+ *
+ * Input dtype codes: 0 = bf16 bit patterns (uint16), 1 = fp32, 2 = fp64.
+ * Layouts: q, k, v, o token-major [T, H, d]; states [num_seqs, H, d, d] with
+ * element (i = key, j = value) at i * d + j.  Return 0 on success, -1 on
+ * invalid arguments.
+ */
+#ifndef LA_ORACLE_H
+#define LA_ORACLE_H
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Form (b): token-by-token recurrent right product, heads [h0, h1).
+ * o (may be NULL): fp64 [T, h1 - h0, d].  kv_in / kv_out (may be NULL):
+ * fp64 [num_seqs, H, d, d] (only heads h0..h1-1 are read / written).
+ * nthreads <= 0 uses every online core. */
+int ora_recurrent(const void* q, const void* k, const void* v, int dtype, const int32_t* cu_seqlens,
+                  int32_t num_seqs, int32_t H, int32_t d, int32_t h0, int32_t h1, const double* kv_in,
+                  double* o, double* kv_out, int nthreads);
+
+/* Form (a): quadratic masked left product, every head, one thread.  For tiny
+ * inputs only: O(n^2 d) per document and head. */
+int ora_quadratic(const void* q, const void* k, const void* v, int dtype, const int32_t* cu_seqlens,
+                  int32_t num_seqs, int32_t H, int32_t d, const double* kv_in, double* o, double* kv_out);
+
+/* One decode step for npairs independent (sequence, head) pairs:
+ *     S <- S + k^T v ;  o = q . S      (update first, then read)
+ * q, k, v [npairs, d] (dtype code), S fp64 [npairs, d, d] in place, o fp64
+ * [npairs, d] (may be NULL). */
+int ora_decode_step(const void* q, const void* k, const void* v, int dtype, int64_t npairs, int32_t d,
+                    double* S, double* o, int nthreads);
+
+/* Threads the last call used (for reporting). */
+int ora_last_threads(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

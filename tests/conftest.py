@@ -1,0 +1,29 @@
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+
+def pytest_configure(config):
+    config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU; runs the HIP library")
+    config.addinivalue_line("markers", "slow: full-size workloads (minutes of host time)")
+
+
+@pytest.fixture(scope="session")
+def oracle_lib():
+    import oracle
+
+    oracle.build()
+    return oracle.load()
+
+
+@pytest.fixture(scope="session")
+def inputs_lib():
+    import la_inputs
+
+    la_inputs.build()
+    return la_inputs

@@ -1,0 +1,296 @@
+"""Pins for the fp64 oracle (CPU only).
+
+The oracle is checked against things other than itself: a hand-worked example
+(tests/golden/hand_worked_d2.txt), closed forms that reduce to numpy routines
+(cumsum, tril, matmul), algebraic identities of the definition (left product
+== right product, split-then-resume, linearity, packed == separate), and the
+two forms against each other.  ``test_planted_mistakes`` rebuilds the oracle
+with one plausible mistake at a time and checks that some pin fails.
+
+Definition followed: "MiniMax-01技术报告解读（一）模型架构" / "MiniMax-01技术报告解读",
+§2.2 线性注意力 (right product, recursive key-value product, no softmax);
+packed documents are independent (§3.2 items 1 and 4); decode is a length-1
+step on the prefix key-value cache (§3.3 items 1-2).
+"""
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "hand_worked_d2.txt")
+TOL = 1e-12
+
+
+def _close(a, b, tol=TOL):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    scale = max(1.0, float(np.max(np.abs(b))) if b.size else 1.0)
+    return a.shape == b.shape and (a.size == 0 or float(np.max(np.abs(a - b))) <= tol * scale)
+
+
+def _rand(rng, T, H, d, dtype=np.float64):
+    return [rng.standard_normal((T, H, d)).astype(dtype) for _ in range(3)]
+
+
+def _golden():
+    rows = {}
+    with open(GOLDEN, encoding="utf-8") as f:
+        for line in f:
+            line = line.split("#", 1)[0].strip()
+            if not line:
+                continue
+            name, *vals = line.split()
+            rows[name] = [float(x) for x in vals]
+    return rows
+
+
+# ----------------------------------------------------------------- pins
+
+def pin_hand_worked(lib):
+    g = _golden()
+    toks = [g[f"tok{i}"] for i in range(1, 7)]
+    q = np.array([t[0:2] for t in toks]).reshape(6, 1, 2)
+    k = np.array([t[2:4] for t in toks]).reshape(6, 1, 2)
+    v = np.array([t[4:6] for t in toks]).reshape(6, 1, 2)
+    # documents: A = tokens 1..3, B = tokens 5..6 (token 4 is A's decode step)
+    qa, ka, va = q[[0, 1, 2, 4, 5]], k[[0, 1, 2, 4, 5]], v[[0, 1, 2, 4, 5]]
+    cu = np.array([0, 3, 5], dtype=np.int32)
+    exp_o = np.array([g["o1"], g["o2"], g["o3"], g["o5"], g["o6"]]).reshape(5, 1, 2)
+    exp_S = np.stack([np.array(g["S3"]).reshape(2, 2), np.array(g["S6"]).reshape(2, 2)]).reshape(2, 1, 2, 2)
+    o_b, s_b = oracle.recurrent(qa, ka, va, cu, lib=lib)
+    o_a, s_a = oracle.quadratic(qa, ka, va, cu, lib=lib)
+    ok = np.array_equal(o_b, exp_o) and np.array_equal(s_b, exp_S)
+    ok &= np.array_equal(o_a, exp_o) and np.array_equal(s_a, exp_S)
+    # decode step of document A from S3
+    S = np.array(g["S3"]).reshape(1, 2, 2).copy()
+    o4 = oracle.decode_step(q[3].reshape(1, 2), k[3].reshape(1, 2), v[3].reshape(1, 2), S, lib=lib)
+    ok &= np.array_equal(o4, np.array([g["o4"]])) and np.array_equal(S.reshape(4), np.array(g["S4"]))
+    return bool(ok)
+
+
+def pin_forms_agree(lib, seeds=range(4)):
+    for seed in seeds:
+        rng = np.random.default_rng(1000 + seed)
+        for n in (1, 2, 3, 7, 64):
+            for d in (1, 2, 16):
+                for H in (1, 2):
+                    q, k, v = _rand(rng, n, H, d)
+                    cu = np.array([0, n], dtype=np.int32)
+                    kv_in = rng.standard_normal((1, H, d, d)) if (seed % 2) else None
+                    ob, sb = oracle.recurrent(q, k, v, cu, kv_in=kv_in, lib=lib)
+                    oa, sa = oracle.quadratic(q, k, v, cu, kv_in=kv_in, lib=lib)
+                    if not (_close(ob, oa) and _close(sb, sa)):
+                        return False
+    # varlen with empty documents
+    rng = np.random.default_rng(7)
+    q, k, v = _rand(rng, 40, 2, 5)
+    cu = np.array([0, 0, 9, 9, 30, 40, 40], dtype=np.int32)
+    ob, sb = oracle.recurrent(q, k, v, cu, lib=lib)
+    oa, sa = oracle.quadratic(q, k, v, cu, lib=lib)
+    return _close(ob, oa) and _close(sb, sa)
+
+
+def pin_split_resume(lib):
+    rng = np.random.default_rng(11)
+    n, H, d = 24, 2, 6
+    q, k, v = _rand(rng, n, H, d)
+    o_full, s_full = oracle.recurrent(q, k, v, np.array([0, n], np.int32), lib=lib)
+    for m in range(0, n + 1):
+        _, s_m = oracle.recurrent(q[:m], k[:m], v[:m], np.array([0, m], np.int32), want_o=False, lib=lib)
+        o_t, s_t = oracle.recurrent(q[m:], k[m:], v[m:], np.array([0, n - m], np.int32), kv_in=s_m, lib=lib)
+        if not (_close(o_t, o_full[m:]) and _close(s_t, s_full)):
+            return False
+    return True
+
+
+def pin_closed_forms(lib):
+    rng = np.random.default_rng(5)
+    # n = 1: o = (q . k) v
+    q, k, v = _rand(rng, 1, 3, 8)
+    o, s = oracle.recurrent(q, k, v, np.array([0, 1], np.int32), lib=lib)
+    if not _close(o[0], np.einsum("hi,hi->h", q[0], k[0])[:, None] * v[0]):
+        return False
+    if not _close(s[0], np.einsum("hi,hj->hij", k[0], v[0])):
+        return False
+    # d = 1: O_t = q_t * cumsum(k_s v_s)
+    q, k, v = _rand(rng, 50, 1, 1)
+    o, _ = oracle.recurrent(q, k, v, np.array([0, 50], np.int32), lib=lib)
+    if not _close(o[:, 0, 0], q[:, 0, 0] * np.cumsum(k[:, 0, 0] * v[:, 0, 0])):
+        return False
+    # q_t = k_s = e_1: O_t = cumsum(v)
+    n, d = 33, 4
+    e1 = np.zeros((n, 1, d))
+    e1[:, 0, 0] = 1.0
+    v = rng.standard_normal((n, 1, d))
+    o, _ = oracle.recurrent(e1, e1.copy(), v, np.array([0, n], np.int32), lib=lib)
+    if not _close(o[:, 0, :], np.cumsum(v[:, 0, :], axis=0)):
+        return False
+    # V = I (n = d): O = tril(Q K^T) -- pins mask orientation and the diagonal
+    n = d = 9
+    q = rng.standard_normal((n, 1, d))
+    k = rng.standard_normal((n, 1, d))
+    eye = np.eye(n).reshape(n, 1, d)
+    for fn in (oracle.recurrent, oracle.quadratic):
+        o, _ = fn(q, k, eye, np.array([0, n], np.int32), lib=lib)
+        if not _close(o[:, 0, :], np.tril(q[:, 0, :] @ k[:, 0, :].T)):
+            return False
+    # kv_out = K^T V via numpy matmul
+    q, k, v = _rand(rng, 70, 2, 7)
+    _, s = oracle.recurrent(q, k, v, np.array([0, 70], np.int32), want_o=False, lib=lib)
+    for h in range(2):
+        if not _close(s[0, h], k[:, h, :].T @ v[:, h, :]):
+            return False
+    return True
+
+
+def pin_linearity(lib):
+    rng = np.random.default_rng(9)
+    q, k, v = _rand(rng, 30, 2, 5)
+    v2 = rng.standard_normal(v.shape)
+    q2 = rng.standard_normal(q.shape)
+    cu = np.array([0, 30], np.int32)
+    a, b = 1.75, -0.5
+    o1, _ = oracle.recurrent(q, k, v, cu, lib=lib)
+    o2, _ = oracle.recurrent(q, k, v2, cu, lib=lib)
+    o3, _ = oracle.recurrent(q, k, a * v + b * v2, cu, lib=lib)
+    if not _close(o3, a * o1 + b * o2, 1e-11):
+        return False
+    o4, _ = oracle.recurrent(q2, k, v, cu, lib=lib)
+    o5, _ = oracle.recurrent(a * q + b * q2, k, v, cu, lib=lib)
+    return _close(o5, a * o1 + b * o4, 1e-11)
+
+
+def pin_packed_equals_separate(lib):
+    rng = np.random.default_rng(13)
+    lens = [5, 0, 17, 1, 0, 9]
+    T = sum(lens)
+    q, k, v = _rand(rng, T, 3, 4)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    o, s = oracle.recurrent(q, k, v, cu, lib=lib)
+    for i, n in enumerate(lens):
+        a, b = cu[i], cu[i + 1]
+        oi, si = oracle.recurrent(q[a:b], k[a:b], v[a:b], np.array([0, n], np.int32), lib=lib)
+        if not (_close(o[a:b], oi) and _close(s[i], si[0])):
+            return False
+        if n == 0 and np.any(s[i] != 0):
+            return False
+    return True
+
+
+def pin_decode_continues_prefill(lib):
+    rng = np.random.default_rng(17)
+    n, H, d = 12, 2, 8
+    q, k, v = _rand(rng, n, H, d)
+    o_full, s_full = oracle.recurrent(q, k, v, np.array([0, n], np.int32), lib=lib)
+    m = 7
+    _, S = oracle.recurrent(q[:m], k[:m], v[:m], np.array([0, m], np.int32), want_o=False, lib=lib)
+    S = S[0].copy()
+    for t in range(m, n):
+        o_t = oracle.decode_step(q[t], k[t], v[t], S, lib=lib)
+        if not _close(o_t, o_full[t]):
+            return False
+    # closed form of one step: S' = S + k^T v, o = q . S'
+    S0 = rng.standard_normal((3, d, d))
+    qq, kk, vv = (rng.standard_normal((3, d)) for _ in range(3))
+    S1 = S0.copy()
+    o = oracle.decode_step(qq, kk, vv, S1, lib=lib)
+    ref_S = S0 + np.einsum("pi,pj->pij", kk, vv)
+    return _close(S1, ref_S) and _close(o, np.einsum("pi,pij->pj", qq, ref_S))
+
+
+PINS = [pin_hand_worked, pin_forms_agree, pin_split_resume, pin_closed_forms, pin_linearity,
+        pin_packed_equals_separate, pin_decode_continues_prefill]
+
+
+@pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
+def test_pin(oracle_lib, pin):
+    assert pin(oracle_lib)
+
+
+def test_dtype_widening_is_exact(oracle_lib):
+    """bf16 bit patterns and fp32 inputs give the same fp64 result as their exact values."""
+    rng = np.random.default_rng(3)
+    x = rng.standard_normal((20, 2, 8)).astype(np.float32)
+    bits = (x.view(np.uint32) >> 16).astype(np.uint16)  # truncation: exactly representable values
+    xb = (bits.astype(np.uint32) << 16).view(np.float32)
+    cu = np.array([0, 20], np.int32)
+    o16, s16 = oracle.recurrent(bits, bits, bits, cu)
+    o64, s64 = oracle.recurrent(xb.astype(np.float64), xb.astype(np.float64), xb.astype(np.float64), cu)
+    assert np.array_equal(o16, o64) and np.array_equal(s16, s64)
+    o32, _ = oracle.recurrent(x, x, x, cu)
+    o64b, _ = oracle.recurrent(x.astype(np.float64), x.astype(np.float64), x.astype(np.float64), cu)
+    assert np.array_equal(o32, o64b)
+
+
+def test_thread_count_invariance(oracle_lib):
+    rng = np.random.default_rng(21)
+    q, k, v = _rand(rng, 200, 3, 40)
+    cu = np.array([0, 50, 120, 200], np.int32)
+    a = oracle.recurrent(q, k, v, cu, nthreads=1)
+    b = oracle.recurrent(q, k, v, cu, nthreads=7)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_head_range(oracle_lib):
+    rng = np.random.default_rng(22)
+    q, k, v = _rand(rng, 30, 4, 6)
+    cu = np.array([0, 30], np.int32)
+    o, s = oracle.recurrent(q, k, v, cu)
+    o2, s2 = oracle.recurrent(q, k, v, cu, heads=(1, 3))
+    assert np.array_equal(o2, o[:, 1:3]) and np.array_equal(s2[:, 1:3], s[:, 1:3])
+
+
+# ------------------------------------------------------- planted mistakes
+
+# (description, regex in la_oracle.c, replacement).  Each is a plausible slip
+# when writing the method; each must make at least one pin fail.
+MUTANTS = [
+    ("recurrent: k replaced by q in the state update",
+     r"kk\[i\] \* vv\[jj\]", "qq[i] * vv[jj]"),
+    ("recurrent: state sign flipped",
+     r"S\[i \* ORA_COLS \+ jj\] \+= kk\[i\] \* vv\[jj\]", "S[i * ORA_COLS + jj] -= kk[i] * vv[jj]"),
+    ("recurrent: k and v swapped (transposed state)",
+     r"kk\[i\] = widen\(c->k,", "kk[i] = widen(c->v,"),
+    ("recurrent: no reset at document start",
+     r"for \(int64_t t = c->cu\[doc\];", "for (int64_t t = 0;"),
+    ("recurrent: output read from the wrong row of the state",
+     r"acc\[jj\] \+= qq\[i\] \* S\[i \* ORA_COLS \+ jj\]", "acc[jj] += qq[i] * S[((i + 1) % d) * ORA_COLS + jj]"),
+    ("quadratic: diagonal dropped from the causal mask",
+     r"for \(int64_t cc = 0; cc <= r; \+\+cc\)", "for (int64_t cc = 0; cc < r; ++cc)"),
+    ("quadratic: kv_in term dropped",
+     r"if \(kv_in\)\n(\s+)for \(int32_t i = 0; i < d; \+\+i\) acc \+= widen\(q",
+     "if (0)\n\\1for (int32_t i = 0; i < d; ++i) acc += widen(q"),
+    ("decode: k and v swapped",
+     r"double ki = widen\(c->k,", "double ki = widen(c->v,"),
+    ("decode: output read before the update",
+     r"/\* S <- S \+ k\^T v \*/\n(\s+)for \(int32_t i = 0; i < d; \+\+i\) \{\n(\s+)double ki",
+     "/* S <- S + k^T v */\n\\1if (c->o) for (int32_t j = 0; j < d; ++j) { double a0 = 0.0; for (int32_t i = 0; i < d; ++i) a0 += widen(c->q, c->dtype, row + i) * S[(size_t)i * d + j]; c->o[row + j] = a0; }\n\\1if (c->o) return;\n\\1for (int32_t i = 0; i < d; ++i) {\n\\2double ki"),
+]
+
+
+@pytest.mark.parametrize("desc,pat,rep", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_planted_mistakes(tmp_path, oracle_lib, desc, pat, rep):
+    src = open(oracle._SRC, encoding="utf-8").read()
+    mutated, n = re.subn(pat, rep, src, count=1)
+    assert n == 1, f"mutation pattern not found: {desc}"
+    msrc = tmp_path / "la_oracle.c"
+    msrc.write_text(mutated, encoding="utf-8")
+    import shutil
+    import subprocess
+
+    shutil.copy(os.path.join(os.path.dirname(oracle._SRC), "la_oracle.h"), tmp_path / "la_oracle.h")
+    so = str(tmp_path / "mut.so")
+    subprocess.check_call(["gcc", "-O2", "-fPIC", "-shared", "-pthread", str(msrc), "-o", so])
+    lib = oracle.load(so)
+    failed = []
+    for pin in PINS:
+        try:
+            ok = pin(lib)
+        except Exception:
+            ok = False
+        if not ok:
+            failed.append(pin.__name__)
+    assert failed, f"no pin caught the planted mistake: {desc}"
