@@ -1,0 +1,203 @@
+"""Causal linear attention (Lightning-style prefill and decode) for AMD MI355X.
+
+Thin binding over the C ABI in ``include/la.h`` (``liblightning_la.so``, HIP
+for gfx950).  The functions named like the C entry points take raw device
+pointers and sizes and only marshal arguments; :func:`prefill` and
+:func:`decode` take torch tensors (torch provides device memory and the
+current stream, nothing else).  Every step of the computation runs in the HIP
+kernels: there is no fallback path.  If the library has not been built the
+import of this module still succeeds, but every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liblightning_la.so")
+
+LA_OK, LA_ERR_INVALID_ARG, LA_ERR_UNSUPPORTED, LA_ERR_WORKSPACE, LA_ERR_HIP = range(5)
+LA_BF16, LA_FP32 = 0, 1
+
+EXPORTED = ("la_prefill", "la_decode", "la_prefill_workspace_size", "la_status_string", "la_prefill_plan",
+            "la_prefill_workspace_size_ex", "la_prefill_ex")
+
+
+class LAError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)} ({status})")
+
+
+class la_prefill_opts(ctypes.Structure):
+    _fields_ = [("seg_len", ctypes.c_int32), ("value_slices", ctypes.c_int32), ("force_scan", ctypes.c_int32),
+                ("reserved", ctypes.c_int32), ("main_begin_event", ctypes.c_void_p),
+                ("main_end_event", ctypes.c_void_p)]
+
+
+class la_prefill_plan_info(ctypes.Structure):
+    _fields_ = [("seg_len", ctypes.c_int32), ("value_slices", ctypes.c_int32), ("num_segments", ctypes.c_int32),
+                ("scan", ctypes.c_int32), ("units", ctypes.c_int64), ("workspace_bytes", ctypes.c_size_t)]
+
+
+_lib = None
+
+
+def library_path() -> str:
+    return LIB_PATH
+
+
+def load():
+    """The HIP library (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m causal_linear_attention_la_amd._build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    lib.la_prefill.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, vp, i32, i64, ctypes.c_int, vp, sz, vp]
+    lib.la_prefill.restype = ctypes.c_int
+    lib.la_prefill_ex.argtypes = lib.la_prefill.argtypes + [ctypes.POINTER(la_prefill_opts)]
+    lib.la_prefill_ex.restype = ctypes.c_int
+    lib.la_decode.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, ctypes.c_int, vp]
+    lib.la_decode.restype = ctypes.c_int
+    lib.la_prefill_workspace_size.argtypes = [i64, i32, i32, i32, i32, ctypes.c_int]
+    lib.la_prefill_workspace_size.restype = sz
+    lib.la_prefill_workspace_size_ex.argtypes = [i64, i32, i32, i32, i32, ctypes.c_int,
+                                                 ctypes.POINTER(la_prefill_opts)]
+    lib.la_prefill_workspace_size_ex.restype = sz
+    lib.la_prefill_plan.argtypes = [i64, i32, i32, i32, i32, ctypes.c_int, ctypes.POINTER(la_prefill_opts),
+                                    ctypes.POINTER(la_prefill_plan_info)]
+    lib.la_prefill_plan.restype = ctypes.c_int
+    lib.la_status_string.argtypes = [ctypes.c_int]
+    lib.la_status_string.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+# ---------------------------------------------------------- C-ABI mirrors
+
+def status_string(status: int) -> str:
+    return load().la_status_string(int(status)).decode()
+
+
+def la_prefill(q, k, v, o, cu_seqlens, H, d, block, kv_state_out, num_seqs, total_tokens, dtype, workspace,
+               workspace_bytes, stream) -> int:
+    return load().la_prefill(q, k, v, o, cu_seqlens, H, d, block, kv_state_out, num_seqs, total_tokens, dtype,
+                             workspace, workspace_bytes, stream)
+
+
+def la_prefill_ex(q, k, v, o, cu_seqlens, H, d, block, kv_state_out, num_seqs, total_tokens, dtype, workspace,
+                  workspace_bytes, stream, opts: la_prefill_opts | None) -> int:
+    return load().la_prefill_ex(q, k, v, o, cu_seqlens, H, d, block, kv_state_out, num_seqs, total_tokens, dtype,
+                                workspace, workspace_bytes, stream, ctypes.byref(opts) if opts is not None else None)
+
+
+def la_decode(q, k, v, kv_state_inout, o, num_seqs, H, d, dtype, stream) -> int:
+    return load().la_decode(q, k, v, kv_state_inout, o, num_seqs, H, d, dtype, stream)
+
+
+def la_prefill_workspace_size(total_tokens, num_seqs, H, d, block, dtype) -> int:
+    return int(load().la_prefill_workspace_size(total_tokens, num_seqs, H, d, block, dtype))
+
+
+def make_opts(seg_len: int = 0, value_slices: int = 0, force_scan: bool = False, begin_event=None,
+              end_event=None) -> la_prefill_opts:
+    return la_prefill_opts(int(seg_len), int(value_slices), 1 if force_scan else 0, 0,
+                           _event_ptr(begin_event), _event_ptr(end_event))
+
+
+def la_prefill_workspace_size_ex(total_tokens, num_seqs, H, d, block, dtype, opts=None) -> int:
+    return int(load().la_prefill_workspace_size_ex(total_tokens, num_seqs, H, d, block, dtype,
+                                                   ctypes.byref(opts) if opts is not None else None))
+
+
+def la_prefill_plan(total_tokens, num_seqs, H, d, block, dtype, opts=None) -> dict:
+    info = la_prefill_plan_info()
+    st = load().la_prefill_plan(total_tokens, num_seqs, H, d, block, dtype,
+                                ctypes.byref(opts) if opts is not None else None, ctypes.byref(info))
+    if st != LA_OK:
+        raise LAError(st, "la_prefill_plan")
+    return dict(seg_len=info.seg_len, value_slices=info.value_slices, num_segments=info.num_segments,
+                scan=info.scan, units=info.units, workspace_bytes=info.workspace_bytes)
+
+
+# ------------------------------------------------------------ torch layer
+
+def _event_ptr(ev):
+    if ev is None:
+        return None
+    return ctypes.c_void_p(int(ev.cuda_event) if hasattr(ev, "cuda_event") else int(ev))
+
+
+def _dtype_code(t) -> int:
+    import torch
+
+    if t.dtype == torch.bfloat16:
+        return LA_BF16
+    if t.dtype == torch.float32:
+        return LA_FP32
+    raise TypeError(f"unsupported dtype {t.dtype} (bfloat16 or float32)")
+
+
+def _stream_ptr(stream):
+    import torch
+
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def prefill(q, k, v, cu_seqlens, block: int = 64, want_state: bool = True, out=None, kv_state_out=None,
+            workspace=None, seg_len: int = 0, value_slices: int = 0, force_scan: bool = False, stream=None,
+            begin_event=None, end_event=None):
+    """Lightning-style causal linear attention over packed documents.
+
+    q, k, v: [T, H, d] bf16/fp32 CUDA tensors; cu_seqlens: int32 [num_seqs + 1]
+    CUDA tensor.  Returns (o, kv_state) with kv_state fp32 [num_seqs, H, d, d]
+    (None when want_state is False).  Asynchronous on the current stream.
+    """
+    import torch
+
+    T, H, d = q.shape
+    dt = _dtype_code(q)
+    num_seqs = cu_seqlens.numel() - 1
+    o = out if out is not None else torch.empty_like(q)
+    kv = kv_state_out
+    if kv is None and want_state:
+        kv = torch.empty((num_seqs, H, d, d), dtype=torch.float32, device=q.device)
+    opts = make_opts(seg_len, value_slices, force_scan, begin_event, end_event)
+    need = la_prefill_workspace_size_ex(T, num_seqs, H, d, block, dt, opts)
+    ws = workspace
+    if need and (ws is None or ws.numel() * ws.element_size() < need):
+        ws = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = ws.numel() * ws.element_size() if ws is not None else 0
+    st = la_prefill_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(cu_seqlens), H, d, block, _ptr(kv), num_seqs, T, dt,
+                       _ptr(ws) if need else None, ws_bytes if need else 0, _stream_ptr(stream), opts)
+    if st != LA_OK:
+        raise LAError(st, "la_prefill")
+    return o, kv
+
+
+def decode(q, k, v, kv_state, out=None, stream=None):
+    """One decode step; kv_state (fp32 [num_seqs, H, d, d]) is updated in place.
+    q, k, v: [num_seqs, H, d].  Returns o."""
+    import torch
+
+    num_seqs, H, d = q.shape
+    o = out if out is not None else torch.empty_like(q)
+    st = la_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(kv_state), _ptr(o), num_seqs, H, d, _dtype_code(q),
+                   _stream_ptr(stream))
+    if st != LA_OK:
+        raise LAError(st, "la_decode")
+    return o
+
+
+def build():
+    from . import _build
+
+    return _build.build()

@@ -1,0 +1,108 @@
+// C ABI (include/la.h): validate on the host, plan, enqueue.
+#include <hip/hip_runtime.h>
+
+#include "../../include/la.h"
+#include "la_host.h"
+#include "la_launch.h"
+
+using la::Plan;
+
+extern "C" {
+
+const char* la_status_string(la_status s) {
+    switch (s) {
+        case LA_OK: return "LA_OK";
+        case LA_ERR_INVALID_ARG: return "LA_ERR_INVALID_ARG";
+        case LA_ERR_UNSUPPORTED: return "LA_ERR_UNSUPPORTED";
+        case LA_ERR_WORKSPACE: return "LA_ERR_WORKSPACE";
+        case LA_ERR_HIP: return "LA_ERR_HIP";
+        default: return "LA_ERR_UNKNOWN";
+    }
+}
+
+la_status la_prefill_plan(int64_t total_tokens, int32_t num_seqs, int32_t H, int32_t d, int32_t block,
+                          la_dtype dtype, const la_prefill_opts* opts, la_prefill_plan_info* out) {
+    Plan p;
+    la_status st = la::make_plan(total_tokens, num_seqs, H, d, block, (int)dtype, opts, &p);
+    if (st != LA_OK) return st;
+    if (out) {
+        out->seg_len = p.L;
+        out->value_slices = p.S;
+        out->num_segments = p.nseg;
+        out->scan = p.scan;
+        out->units = p.units;
+        out->workspace_bytes = p.ws_bytes;
+    }
+    return LA_OK;
+}
+
+size_t la_prefill_workspace_size_ex(int64_t total_tokens, int32_t num_seqs, int32_t H, int32_t d, int32_t block,
+                                    la_dtype dtype, const la_prefill_opts* opts) {
+    Plan p;
+    if (la::make_plan(total_tokens, num_seqs, H, d, block, (int)dtype, opts, &p) != LA_OK) return 0;
+    return p.ws_bytes;
+}
+
+size_t la_prefill_workspace_size(int64_t total_tokens, int32_t num_seqs, int32_t H, int32_t d, int32_t block,
+                                 la_dtype dtype) {
+    return la_prefill_workspace_size_ex(total_tokens, num_seqs, H, d, block, dtype, nullptr);
+}
+
+la_status la_prefill_ex(const void* q, const void* k, const void* v, void* o, const int32_t* cu_seqlens, int32_t H,
+                        int32_t d, int32_t block, float* kv_state_out, int32_t num_seqs, int64_t total_tokens,
+                        la_dtype dtype, void* workspace, size_t workspace_bytes, void* stream,
+                        const la_prefill_opts* opts) {
+    Plan plan;
+    la_status st = la::validate_prefill(q, k, v, o, cu_seqlens, H, d, block, kv_state_out, num_seqs, total_tokens,
+                                        (int)dtype, workspace, workspace_bytes, opts, &plan);
+    if (st != LA_OK) return st;
+    la::PrefillParams p{};
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.o = o;
+    p.cu = cu_seqlens;
+    p.kv_out = kv_state_out;
+    p.ws = plan.ws_bytes ? reinterpret_cast<float*>(static_cast<char*>(workspace) + plan.ws_states_off) : nullptr;
+    p.flags = plan.ws_bytes ? reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + plan.ws_flags_off) : nullptr;
+    p.T = (int32_t)total_tokens;
+    p.num_seqs = num_seqs;
+    p.H = H;
+    p.L = plan.L;
+    p.nseg = plan.nseg;
+    p.S = plan.S;
+    p.scan = plan.scan;
+    p.units = plan.units;
+    p.per_xcd = (plan.units + 7) / 8;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipEvent_t e0 = opts ? static_cast<hipEvent_t>(opts->main_begin_event) : nullptr;
+    hipEvent_t e1 = opts ? static_cast<hipEvent_t>(opts->main_end_event) : nullptr;
+    hipError_t e = dtype == LA_BF16 ? la::launch_prefill_bf16(p, d, block, plan.W, s, e0, e1)
+                                    : la::launch_prefill_fp32(p, d, block, plan.W, s, e0, e1);
+    return e == hipSuccess ? LA_OK : LA_ERR_HIP;
+}
+
+la_status la_prefill(const void* q, const void* k, const void* v, void* o, const int32_t* cu_seqlens, int32_t H,
+                     int32_t d, int32_t block, float* kv_state_out, int32_t num_seqs, int64_t total_tokens,
+                     la_dtype dtype, void* workspace, size_t workspace_bytes, void* stream) {
+    return la_prefill_ex(q, k, v, o, cu_seqlens, H, d, block, kv_state_out, num_seqs, total_tokens, dtype, workspace,
+                         workspace_bytes, stream, nullptr);
+}
+
+la_status la_decode(const void* q, const void* k, const void* v, float* kv_state_inout, void* o, int32_t num_seqs,
+                    int32_t H, int32_t d, la_dtype dtype, void* stream) {
+    la_status st = la::validate_decode(q, k, v, kv_state_inout, o, num_seqs, H, d, (int)dtype);
+    if (st != LA_OK) return st;
+    la::DecodeParams p{};
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.S = kv_state_inout;
+    p.o = o;
+    p.pairs = (int64_t)num_seqs * H;
+    if (p.pairs > INT32_MAX) return LA_ERR_UNSUPPORTED;
+    hipError_t e = la::launch_decode(p, d, (int)dtype, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? LA_OK : LA_ERR_HIP;
+}
+
+}  // extern "C"

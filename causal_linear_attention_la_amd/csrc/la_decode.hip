@@ -1,0 +1,24 @@
+// Decode kernel instantiations.
+#include "la_launch.h"
+
+namespace la {
+namespace {
+template <typename T>
+hipError_t run_decode(const DecodeParams& p, int D, hipStream_t st) {
+    const dim3 grid((unsigned)p.pairs), block(kThreads);
+    switch (D) {
+        case 16: la_decode_kernel<T, 16><<<grid, block, 0, st>>>(p); break;
+        case 32: la_decode_kernel<T, 32><<<grid, block, 0, st>>>(p); break;
+        case 64: la_decode_kernel<T, 64><<<grid, block, 0, st>>>(p); break;
+        case 128: la_decode_kernel<T, 128><<<grid, block, 0, st>>>(p); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_decode(const DecodeParams& p, int D, int dtype, hipStream_t st) {
+    if (p.pairs == 0) return hipSuccess;
+    return dtype == 0 ? run_decode<bf16_t>(p, D, st) : run_decode<float>(p, D, st);
+}
+}  // namespace la

@@ -1,0 +1,155 @@
+// Host-only validation and planning (see la_host.h).
+#include "la_host.h"
+
+#include <climits>
+
+#include "la_tiles.h"
+
+namespace la {
+
+namespace {
+
+constexpr int kNumCUs = 256;      // MI355X compute units
+constexpr int kUnitsTarget = 256; // block-loop workgroups to aim for (one per CU)
+constexpr int kMinSegment = 1024; // shorter segments spend too much on state traffic
+constexpr int kMaxLookback = 8;   // a unit sums at most this many segment states
+
+bool is_pow2_in(int32_t x, int32_t lo, int32_t hi) {
+    if (x < lo || x > hi) return false;
+    return (x & (x - 1)) == 0;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// [a, a+na) and [b, b+nb) overlap (empty ranges never overlap)
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+    if (!a || !b || na == 0 || nb == 0) return false;
+    uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+    return x < y + nb && y < x + na;
+}
+
+bool mul_ok(int64_t a, int64_t b, int64_t& out) {
+    if (a < 0 || b < 0) return false;
+    if (a != 0 && b > INT64_MAX / a) return false;
+    out = a * b;
+    return true;
+}
+
+}  // namespace
+
+size_t elem_size(int dtype) { return dtype == LA_BF16 ? 2 : dtype == LA_FP32 ? 4 : 0; }
+
+la_status make_plan(int64_t T, int32_t num_seqs, int32_t H, int32_t d, int32_t block, int dtype,
+                    const la_prefill_opts* opts, Plan* out) {
+    if (H < 1 || num_seqs < 1 || T < 0 || T > INT32_MAX) return LA_ERR_INVALID_ARG;
+    const size_t es = elem_size(dtype);
+    if (es == 0) return LA_ERR_UNSUPPORTED;
+    if (!(d == 16 || d == 32 || d == 64 || d == 128)) return LA_ERR_UNSUPPORTED;
+    if (!(block == 32 || block == 64 || block == 128)) return LA_ERR_UNSUPPORTED;
+
+    auto slice_ok = [&](int32_t S) {
+        if (S < 1 || d % S != 0) return false;
+        return main_fits((int)es, d, block, d / S);
+    };
+
+    Plan p;
+    const int64_t work = T * (int64_t)H;
+    if (opts && opts->value_slices != 0) {
+        if (!is_pow2_in(opts->value_slices, 1, 4) || !slice_ok(opts->value_slices)) return LA_ERR_UNSUPPORTED;
+        p.S = opts->value_slices;
+    } else {
+        int32_t chosen = 0;
+        for (int32_t S = 1; S <= 4; S *= 2) {
+            if (!slice_ok(S)) continue;
+            chosen = S;
+            if (work * S / kUnitsTarget >= kMinSegment) break;
+        }
+        if (chosen == 0) return LA_ERR_UNSUPPORTED;
+        p.S = chosen;
+    }
+    p.W = d / p.S;
+
+    if (opts && opts->seg_len != 0) {
+        if (opts->seg_len < block || opts->seg_len % block != 0) return LA_ERR_UNSUPPORTED;
+        p.L = opts->seg_len;
+    } else {
+        int64_t L = work * p.S / kUnitsTarget;
+        L = (L / block) * block;
+        int64_t floor_len = T < kMinSegment ? T : kMinSegment;
+        floor_len = ((floor_len + block - 1) / block) * block;
+        if (L < floor_len) L = floor_len;
+        if (L < block) L = block;
+        if (L > INT32_MAX / 2) L = (INT32_MAX / 2 / block) * block;
+        p.L = (int32_t)L;
+    }
+    const int64_t nseg = T == 0 ? 1 : (T + p.L - 1) / p.L;
+    if (nseg > INT32_MAX) return LA_ERR_UNSUPPORTED;
+    p.nseg = (int32_t)nseg;
+    p.units = nseg * (int64_t)H * p.S;
+    if (p.units > (int64_t)INT32_MAX * 8) return LA_ERR_UNSUPPORTED;
+    p.scan = (p.nseg - 1 > kMaxLookback || (opts && opts->force_scan)) && p.nseg > 1 ? 1 : 0;
+
+    if (p.nseg > 1) {
+        int64_t states;
+        if (!mul_ok(nseg, (int64_t)H * d * d, states) || !mul_ok(states, 4, states)) return LA_ERR_UNSUPPORTED;
+        p.ws_states_off = 0;
+        p.ws_flags_off = ((size_t)states + 255) & ~(size_t)255;
+        p.ws_bytes = p.ws_flags_off + (((size_t)nseg * 4 + 255) & ~(size_t)255);
+    }
+    (void)kNumCUs;
+    *out = p;
+    return LA_OK;
+}
+
+la_status validate_prefill(const void* q, const void* k, const void* v, const void* o, const int32_t* cu, int32_t H,
+                           int32_t d, int32_t block, const float* kv_out, int32_t num_seqs, int64_t T, int dtype,
+                           const void* ws, size_t ws_bytes, const la_prefill_opts* opts, Plan* plan) {
+    if (!q || !k || !v || !o || !cu) return LA_ERR_INVALID_ARG;
+    la_status st = make_plan(T, num_seqs, H, d, block, dtype, opts, plan);
+    if (st != LA_OK) return st;
+    const size_t es = elem_size(dtype);
+    int64_t n;
+    if (!mul_ok(T, (int64_t)H * d, n) || !mul_ok(n, (int64_t)es, n)) return LA_ERR_INVALID_ARG;
+    const size_t tensor = (size_t)n;
+    int64_t ns;
+    if (!mul_ok(num_seqs, (int64_t)H * d * d, ns) || !mul_ok(ns, 4, ns)) return LA_ERR_INVALID_ARG;
+    const size_t state = (size_t)ns;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(cu, 4))
+        return LA_ERR_INVALID_ARG;
+    if (kv_out && !aligned(kv_out, 16)) return LA_ERR_INVALID_ARG;
+    if (overlap(o, tensor, q, tensor) || overlap(o, tensor, k, tensor) || overlap(o, tensor, v, tensor))
+        return LA_ERR_INVALID_ARG;
+    if (kv_out && (overlap(kv_out, state, q, tensor) || overlap(kv_out, state, k, tensor) ||
+                   overlap(kv_out, state, v, tensor) || overlap(kv_out, state, o, tensor)))
+        return LA_ERR_INVALID_ARG;
+    if (plan->ws_bytes > 0) {
+        if (!ws || ws_bytes < plan->ws_bytes) return LA_ERR_WORKSPACE;
+        if (!aligned(ws, 256)) return LA_ERR_INVALID_ARG;
+        const size_t wn = plan->ws_bytes;
+        if (overlap(ws, wn, q, tensor) || overlap(ws, wn, k, tensor) || overlap(ws, wn, v, tensor) ||
+            overlap(ws, wn, o, tensor) || (kv_out && overlap(ws, wn, kv_out, state)))
+            return LA_ERR_INVALID_ARG;
+    }
+    return LA_OK;
+}
+
+la_status validate_decode(const void* q, const void* k, const void* v, const float* S, const void* o,
+                          int32_t num_seqs, int32_t H, int32_t d, int dtype) {
+    if (!q || !k || !v || !S || !o) return LA_ERR_INVALID_ARG;
+    if (num_seqs < 1 || H < 1) return LA_ERR_INVALID_ARG;
+    const size_t es = elem_size(dtype);
+    if (es == 0) return LA_ERR_UNSUPPORTED;
+    if (!(d == 16 || d == 32 || d == 64 || d == 128)) return LA_ERR_UNSUPPORTED;
+    int64_t pairs, n, ns;
+    if (!mul_ok(num_seqs, H, pairs) || !mul_ok(pairs, (int64_t)d * es, n) || !mul_ok(pairs, (int64_t)d * d * 4, ns))
+        return LA_ERR_INVALID_ARG;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(S, 16) || !aligned(o, 16))
+        return LA_ERR_INVALID_ARG;
+    const size_t tn = (size_t)n, sn = (size_t)ns;
+    if (overlap(o, tn, q, tn) || overlap(o, tn, k, tn) || overlap(o, tn, v, tn) || overlap(o, tn, S, sn) ||
+        overlap(S, sn, q, tn) || overlap(S, sn, k, tn) || overlap(S, sn, v, tn))
+        return LA_ERR_INVALID_ARG;
+    return LA_OK;
+}
+
+}  // namespace la

@@ -1,0 +1,499 @@
+// Prefill kernels (templates; instantiated per dtype in la_prefill_*.hip).
+//
+// The method ("MiniMax-01技术报告解读（一）模型架构" and "MiniMax-01技术报告解读",
+// §2.2 线性注意力): Q, K, V are cut along the sequence into blocks; inside a
+// block the masked left product (Q K^T ⊙ M) V, across blocks the right
+// product Q . KV against the running state, then KV += K^T V.
+//
+// Work decomposition.  The packed token range [0, T) is cut into segments of
+// L tokens (a multiple of the block).  One workgroup ("unit") handles one
+// (segment u, head h, value-column slice s of width W).  A segment can hold
+// pieces of several documents; blocks never straddle a document boundary and
+// the state restarts at zero at each document start.  When a document starts
+// before the segment, the unit starts from the document's state at the
+// segment start, obtained the LASP+ way ("MiniMax-01技术报告解读", §3.2 item 3:
+// each part computes its local prefix state, then a global prefix is formed
+// from them):
+//   la_segment_state_kernel  K^T V of each segment's last document piece
+//   la_segment_scan_kernel   (long documents) per-document inclusive scan of
+//                            those states, in place
+//   la_prefill_main_kernel   the block loop from the prefix; writes o and
+//                            the final state of every document ending here.
+#pragma once
+#include "la_device.h"
+#include "la_tiles.h"
+
+namespace la {
+
+struct PrefillParams {
+    const void* q;
+    const void* k;
+    const void* v;
+    void* o;
+    const int32_t* cu;
+    float* kv_out;   // [num_seqs][H][D][D] or null
+    float* ws;       // segment states [nseg][H][D][D] (null when nseg == 1)
+    int32_t* flags;  // [nseg]: bit 0 = the segment's last document continues past it,
+                     //         bit 1 = that piece also continues from the previous segment
+    int32_t T;
+    int32_t num_seqs;
+    int32_t H;
+    int32_t L;       // segment length (tokens)
+    int32_t nseg;
+    int32_t S;       // value slices per head
+    int32_t scan;    // 1: ws holds inclusive per-document states (after the scan kernel)
+    int32_t pad_;
+    int64_t units;   // nseg * H * S
+    int64_t per_xcd; // ceil(units / 8)
+};
+
+// Largest doc in [0, n-1] with cu[doc] <= t.
+__device__ __forceinline__ int doc_at(const int32_t* cu, int n, int t) {
+    int lo = 0, hi = n - 1;
+    while (lo < hi) {
+        int mid = (lo + hi + 1) >> 1;
+        if (cu[mid] <= t) lo = mid; else hi = mid - 1;
+    }
+    return lo;
+}
+// First doc in [0, n] with cu[doc] >= t.
+__device__ __forceinline__ int doc_lower(const int32_t* cu, int n, int t) {
+    int lo = 0, hi = n;
+    while (lo < hi) {
+        int mid = (lo + hi) >> 1;
+        if (cu[mid] < t) lo = mid + 1; else hi = mid;
+    }
+    return lo;
+}
+
+// Workgroup -> unit.  Consecutive unit indices x = (u*H + h)*S + s go to the
+// same XCD (workgroup ids are dealt round-robin over the 8 XCDs), so the S
+// slices of one (segment, head) -- which read the same Q and K rows -- share
+// that XCD's L2.
+__device__ __forceinline__ bool unit_of(const PrefillParams& p, int& u, int& h, int& s) {
+    const int64_t g = blockIdx.x;
+    const int64_t x = (g & 7) * p.per_xcd + (g >> 3);
+    if (x >= p.units) return false;
+    s = (int)(x % p.S);
+    h = (int)((x / p.S) % p.H);
+    u = (int)(x / ((int64_t)p.S * p.H));
+    return true;
+}
+
+// Walks the blocks of one segment [t0, t1): blocks start at the segment start
+// or at a document start, hold at most B tokens and never cross a document end.
+struct Cursor {
+    int b0;       // first token of the block
+    int nb;       // tokens in it (0: no more blocks)
+    int doc;
+    int doc_end;  // cu[doc + 1]
+    bool first_of_doc;
+};
+
+__device__ __forceinline__ void cursor_first(Cursor& c, const int32_t* cu, int n, int t0, int t1, int B) {
+    if (t0 >= t1) { c.nb = 0; return; }
+    c.doc = doc_at(cu, n, t0);
+    c.doc_end = cu[c.doc + 1];
+    c.b0 = t0;
+    c.nb = min(B, min(t1, c.doc_end) - t0);
+    c.first_of_doc = (cu[c.doc] == t0);
+}
+
+__device__ __forceinline__ void cursor_next(Cursor& c, const int32_t* cu, int n, int t1, int B) {
+    int nb0 = c.b0 + c.nb;
+    int piece_end = min(t1, c.doc_end);
+    if (nb0 < piece_end) {
+        c.b0 = nb0;
+        c.nb = min(B, piece_end - nb0);
+        c.first_of_doc = false;
+        return;
+    }
+    int d = c.doc + 1;
+    while (d < n && cu[d + 1] == cu[d]) ++d;  // skip empty documents
+    if (d >= n || cu[d] >= t1) { c.nb = 0; return; }
+    c.doc = d;
+    c.b0 = cu[d];
+    c.doc_end = cu[d + 1];
+    c.nb = min(B, min(t1, c.doc_end) - c.b0);
+    c.first_of_doc = true;
+}
+
+// Register staging of a ROWS x COLS tile of one head (row stride ld elements):
+// each item is 4 consecutive rows x one 16-byte column chunk, so the tile can
+// be written to LDS both row-major and transposed (4-token runs).
+template <typename T, int ROWS, int COLS>
+struct TileRegs {
+    static constexpr int CE = 16 / (int)sizeof(T);
+    static constexpr int CPR = COLS / CE;
+    static constexpr int ITEMS = (ROWS / 4) * CPR;
+    static constexpr int PER = (ITEMS + kThreads - 1) / kThreads;
+    uint4 r[PER][4];
+
+    __device__ __forceinline__ void load(const T* base, int64_t ld, int nb, int tid) {
+#pragma unroll
+        for (int p = 0; p < PER; ++p) {
+            const int item = tid + p * kThreads;
+            const int rq = item / CPR, c = item % CPR;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int row = 4 * rq + i;
+                if (item < ITEMS && row < nb)
+                    r[p][i] = *reinterpret_cast<const uint4*>(base + (int64_t)row * ld + c * CE);
+                else
+                    r[p][i] = make_uint4(0u, 0u, 0u, 0u);
+            }
+        }
+    }
+    // row-major: lds[row][col], pitch in elements
+    __device__ __forceinline__ void store_rows(T* lds, int pitch, int tid) const {
+#pragma unroll
+        for (int p = 0; p < PER; ++p) {
+            const int item = tid + p * kThreads;
+            if (item < ITEMS) {
+                const int rq = item / CPR, c = item % CPR;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4*>(lds + (4 * rq + i) * pitch + c * CE) = r[p][i];
+            }
+        }
+    }
+    // transposed: lds[col][row], 4 rows per write
+    __device__ __forceinline__ void store_cols(T* lds, int pitch, int tid) const {
+#pragma unroll
+        for (int p = 0; p < PER; ++p) {
+            const int item = tid + p * kThreads;
+            if (item < ITEMS) {
+                const int rq = item / CPR, c = item % CPR;
+#pragma unroll
+                for (int e = 0; e < CE; ++e) store_col4(lds + (c * CE + e) * pitch + 4 * rq, r[p], e);
+            }
+        }
+    }
+};
+
+// Round LDS sub-array sizes to 8 elements so every tile starts 16-byte aligned.
+constexpr size_t al8(size_t n) { return (n + 7) & ~(size_t)7; }
+
+// KV += K^T V for one block: the state tiles owned by this wave.  kv[j] is the
+// 16x16 tile t = wave + 4j of the D x W state, rows = key dim, cols = value dim;
+// lane (col li, group g) holds rows 4g..4g+3.
+template <typename TIn, int D, int B, int W, int KVPW>
+__device__ __forceinline__ void state_update(f32x4_t (&kv)[KVPW], const TIn* Kt, const TIn* Vt, int wave, int li,
+                                             int g) {
+    constexpr int NCT = W / 16, NKV = (D / 16) * NCT, TP = t_pitch(B);
+#pragma unroll
+    for (int j = 0; j < KVPW; ++j) {
+        const int t = wave + kWaves * j;
+        if (t < NKV) {
+            const int a = t / NCT, c = t % NCT;
+#pragma unroll
+            for (int kc = 0; kc < B / 32; ++kc) {
+                Frag<TIn> fa, fb;
+                load_frag(fa, Kt + (16 * a + li) * TP + 32 * kc, g);  // K^T[d][keys]
+                load_frag(fb, Vt + (16 * c + li) * TP + 32 * kc, g);  // V[keys][col]
+                mma(kv[j], fa, fb);
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Segment states: for every segment whose last document continues into the
+// next segment, K^T V over that document's piece of the segment.
+template <typename TIn, int D, int B, int W>
+__global__ __launch_bounds__(kThreads, 2) void la_segment_state_kernel(PrefillParams p) {
+    constexpr int TP = t_pitch(B);
+    constexpr int NKV = (D / 16) * (W / 16);
+    constexpr int KVPW = (NKV + kWaves - 1) / kWaves;
+    __shared__ __align__(16) TIn smem[al8(kt_elems(D, B)) + al8(vt_elems(W, B))];
+    TIn* Kt = smem;
+    TIn* Vt = smem + al8(kt_elems(D, B));
+
+    int u, h, s;
+    if (!unit_of(p, u, h, s)) return;
+    if (u >= p.nseg - 1) return;  // nothing after the last segment
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, li = lane & 15, g = lane >> 4;
+    const int t_beg = u * p.L, t_end = (u + 1) * p.L;  // t_end < T here
+    const int de = doc_at(p.cu, p.num_seqs, t_end - 1);
+    const int dstart = p.cu[de];
+    const bool needs = p.cu[de + 1] > t_end;
+    const bool chain = dstart < t_beg;
+    if (h == 0 && s == 0 && tid == 0) p.flags[u] = (needs ? 1 : 0) | (chain ? 2 : 0);
+    if (!needs) return;
+
+    const TIn* kg = static_cast<const TIn*>(p.k);
+    const TIn* vg = static_cast<const TIn*>(p.v);
+    const int64_t ld = (int64_t)p.H * D;
+    f32x4_t kv[KVPW];
+#pragma unroll
+    for (int j = 0; j < KVPW; ++j) kv[j] = zero4();
+
+    TileRegs<TIn, B, D> lk;
+    TileRegs<TIn, B, W> lv;
+    int b0 = max(t_beg, dstart);
+    int nb = min(B, t_end - b0);
+    lk.load(kg + ((int64_t)b0 * p.H + h) * D, ld, nb, tid);
+    lv.load(vg + ((int64_t)b0 * p.H + h) * D + s * W, ld, nb, tid);
+    while (nb > 0) {
+        __syncthreads();
+        lk.store_cols(Kt, TP, tid);
+        lv.store_cols(Vt, TP, tid);
+        const int nb0 = b0 + nb;
+        const int nnb = min(B, t_end - nb0);
+        if (nnb > 0) {
+            lk.load(kg + ((int64_t)nb0 * p.H + h) * D, ld, nnb, tid);
+            lv.load(vg + ((int64_t)nb0 * p.H + h) * D + s * W, ld, nnb, tid);
+        }
+        __syncthreads();
+        state_update<TIn, D, B, W, KVPW>(kv, Kt, Vt, wave, li, g);
+        b0 = nb0;
+        nb = nnb;
+    }
+    float* dst = p.ws + (((int64_t)u * p.H + h) * D) * D + s * W;
+#pragma unroll
+    for (int j = 0; j < KVPW; ++j) {
+        const int t = wave + kWaves * j;
+        if (t < NKV) {
+            const int a = t / (W / 16), c = t % (W / 16);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) dst[(int64_t)(16 * a + 4 * g + r) * D + 16 * c + li] = kv[j][r];
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Per-document inclusive scan of the segment states, in place: afterwards
+// ws[u] is the state of segment u's last document at the end of segment u.
+// One thread per state entry (h, i, j); the loop over segments is sequential.
+template <int UNROLL>
+__global__ __launch_bounds__(kThreads) void la_segment_scan_kernel(float* ws, const int32_t* flags, int nseg,
+                                                                   int64_t entries) {
+    const int64_t idx = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (idx >= entries) return;
+    float carry = 0.f;
+#pragma unroll UNROLL
+    for (int u = 0; u < nseg - 1; ++u) {
+        const int f = flags[u];
+        if (f & 1) {
+            const float a = ws[(int64_t)u * entries + idx];
+            carry = (f & 2) ? carry + a : a;
+            ws[(int64_t)u * entries + idx] = carry;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// The block loop.
+template <typename TIn, int D, int B, int W>
+__global__ __launch_bounds__(kThreads, 1) void la_prefill_main_kernel(PrefillParams p) {
+    constexpr int ES = (int)sizeof(TIn);
+    constexpr int CE = 16 / ES;
+    constexpr int DK = dk_of(D);
+    constexpr int QP = row_pitch(ES, D), TP = t_pitch(B), OP = o_pitch(ES, W), KP = kvt_pitch(D);
+    constexpr int NQT = B / 16, NCT = W / 16, NKV = (D / 16) * NCT;
+    constexpr int KVPW = (NKV + kWaves - 1) / kWaves;
+    constexpr int NTRI = NQT * (NQT + 1) / 2, NZT = NQT / 2;
+    constexpr size_t OQ = 0;
+    constexpr size_t OK = OQ + al8(qs_elems(ES, D, B));
+    constexpr size_t OKT = OK + al8(ks_elems(ES, D, B, W));
+    constexpr size_t OVT = OKT + al8(kt_elems(D, B));
+    constexpr size_t OPS = OVT + al8(vt_elems(W, B));
+    constexpr size_t OKV = OPS + al8(ps_elems(B));
+    constexpr size_t NTOT = OKV + al8(kvt_elems(D, W));
+    static_assert(NTOT * ES <= kMaxLdsBytes, "LDS budget exceeded");
+    __shared__ __align__(16) TIn smem[NTOT];
+    TIn* Qs = smem + OQ;
+    TIn* Ks = smem + OK;
+    TIn* Os = smem + OK;  // O staging reuses the key rows (dead after the score phase)
+    TIn* Kt = smem + OKT;
+    TIn* Vt = smem + OVT;
+    TIn* Ps = smem + OPS;
+    TIn* KVt = smem + OKV;
+
+    int u, h, s;
+    if (!unit_of(p, u, h, s)) return;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, li = lane & 15, g = lane >> 4;
+    const int t0 = u * p.L, t1 = min(p.T, t0 + p.L);
+    const TIn* qg = static_cast<const TIn*>(p.q);
+    const TIn* kg = static_cast<const TIn*>(p.k);
+    const TIn* vg = static_cast<const TIn*>(p.v);
+    TIn* og = static_cast<TIn*>(p.o);
+    const int64_t ld = (int64_t)p.H * D;
+
+    // Zero LDS once: pad columns (d >= D) of Qs and KVt must stay finite zeros.
+    {
+        uint4* z = reinterpret_cast<uint4*>(smem);
+        constexpr int NV = (int)(NTOT * ES / 16);
+        for (int i = tid; i < NV; i += kThreads) z[i] = make_uint4(0u, 0u, 0u, 0u);
+    }
+
+    Cursor cur;
+    cursor_first(cur, p.cu, p.num_seqs, t0, t1, B);
+
+    // Initial state: zero, or the document's state at the segment start.
+    f32x4_t kv[KVPW];
+#pragma unroll
+    for (int j = 0; j < KVPW; ++j) kv[j] = zero4();
+    if (cur.nb > 0 && !cur.first_of_doc) {
+        const int u_first = p.scan ? u - 1 : p.cu[cur.doc] / p.L;
+        for (int uu = u_first; uu < u; ++uu) {
+            const float* src = p.ws + (((int64_t)uu * p.H + h) * D) * D + s * W;
+#pragma unroll
+            for (int j = 0; j < KVPW; ++j) {
+                const int t = wave + kWaves * j;
+                if (t < NKV) {
+                    const int a = t / NCT, c = t % NCT;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) kv[j][r] += src[(int64_t)(16 * a + 4 * g + r) * D + 16 * c + li];
+                }
+            }
+        }
+    }
+    __syncthreads();  // LDS zeroed before the state copy below
+#pragma unroll
+    for (int j = 0; j < KVPW; ++j) {
+        const int t = wave + kWaves * j;
+        if (t < NKV) {
+            const int a = t / NCT, c = t % NCT;
+            store4(KVt + (16 * c + li) * KP + 16 * a + 4 * g, kv[j][0], kv[j][1], kv[j][2], kv[j][3]);
+        }
+    }
+
+    TileRegs<TIn, B, D> lq, lk;
+    TileRegs<TIn, B, W> lv;
+    if (cur.nb > 0) {
+        const int64_t row0 = (int64_t)cur.b0 * p.H + h;
+        lq.load(qg + row0 * D, ld, cur.nb, tid);
+        lk.load(kg + row0 * D, ld, cur.nb, tid);
+        lv.load(vg + row0 * D + s * W, ld, cur.nb, tid);
+    }
+
+    while (cur.nb > 0) {
+        __syncthreads();  // (A) previous block fully consumed
+        lq.store_rows(Qs, QP, tid);
+        lk.store_rows(Ks, QP, tid);
+        if constexpr (DK != D) {  // Ks pad columns were overwritten by the O staging
+            for (int i = tid; i < B * (DK - D) / CE; i += kThreads) {
+                const int row = i / ((DK - D) / CE), c = i % ((DK - D) / CE);
+                *reinterpret_cast<uint4*>(Ks + row * QP + D + c * CE) = make_uint4(0u, 0u, 0u, 0u);
+            }
+        }
+        lk.store_cols(Kt, TP, tid);
+        lv.store_cols(Vt, TP, tid);
+        Cursor nxt = cur;
+        cursor_next(nxt, p.cu, p.num_seqs, t1, B);
+        if (nxt.nb > 0) {
+            const int64_t row0 = (int64_t)nxt.b0 * p.H + h;
+            lq.load(qg + row0 * D, ld, nxt.nb, tid);
+            lk.load(kg + row0 * D, ld, nxt.nb, tid);
+            lv.load(vg + row0 * D + s * W, ld, nxt.nb, tid);
+        }
+        __syncthreads();  // (B) tiles in LDS
+
+        // Scores, transposed: S^T = K Q^T on the lower-triangular tiles, causal
+        // mask on the diagonal tiles (key <= query kept), stored as P[query][key].
+        for (int t = wave; t < NTRI + NZT; t += kWaves) {
+            int a, b;
+            if (t < NTRI) {
+                b = 0;
+                while ((b + 1) * (b + 2) / 2 <= t) ++b;
+                a = t - b * (b + 1) / 2;
+            } else {
+                b = 2 * (t - NTRI);
+                a = b + 1;
+            }
+            TIn* prow = Ps + (16 * b + li) * TP + 16 * a + 4 * g;
+            if (t >= NTRI) {  // above-diagonal tile read by the P.V chunk loop: zeros
+                store4_zero(prow);
+                continue;
+            }
+            f32x4_t acc = zero4();
+#pragma unroll
+            for (int m = 0; m < DK / 32; ++m) {
+                Frag<TIn> fa, fb;
+                load_frag(fa, Ks + (16 * a + li) * QP + 32 * m, g);
+                load_frag(fb, Qs + (16 * b + li) * QP + 32 * m, g);
+                mma(acc, fa, fb);
+            }
+            if (a == b) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    if (4 * g + r > li) acc[r] = 0.f;
+            }
+            store4(prow, acc[0], acc[1], acc[2], acc[3]);
+        }
+        __syncthreads();  // (C) P complete
+
+        // Output, transposed: O^T = V^T P^T (intra) + KV^T Q^T (inter, state
+        // before this block).
+        for (int t = wave; t < NQT * NCT; t += kWaves) {
+            const int b = t % NQT, c = t / NQT;
+            f32x4_t acc = zero4();
+            for (int kc = 0; kc <= b / 2; ++kc) {
+                Frag<TIn> fa, fb;
+                load_frag(fa, Vt + (16 * c + li) * TP + 32 * kc, g);
+                load_frag(fb, Ps + (16 * b + li) * TP + 32 * kc, g);
+                mma(acc, fa, fb);
+            }
+#pragma unroll
+            for (int m = 0; m < DK / 32; ++m) {
+                Frag<TIn> fa, fb;
+                load_frag(fa, KVt + (16 * c + li) * KP + 32 * m, g);
+                load_frag(fb, Qs + (16 * b + li) * QP + 32 * m, g);
+                mma(acc, fa, fb);
+            }
+            store4(Os + (16 * b + li) * OP + 16 * c + 4 * g, acc[0], acc[1], acc[2], acc[3]);
+        }
+        // State update after the inter product used the old state.
+        state_update<TIn, D, B, W, KVPW>(kv, Kt, Vt, wave, li, g);
+        __syncthreads();  // (D) O staged, old KVt no longer read
+
+        // Coalesced store of the block's output rows.
+        {
+            constexpr int OCPR = W / CE;
+            TIn* obase = og + ((int64_t)cur.b0 * p.H + h) * D + s * W;
+            for (int i = tid; i < cur.nb * OCPR; i += kThreads) {
+                const int row = i / OCPR, c = i % OCPR;
+                *reinterpret_cast<uint4*>(obase + (int64_t)row * ld + c * CE) =
+                    *reinterpret_cast<const uint4*>(Os + row * OP + c * CE);
+            }
+        }
+        if (cur.b0 + cur.nb == cur.doc_end && p.kv_out) {
+            float* dst = p.kv_out + (((int64_t)cur.doc * p.H + h) * D) * D + s * W;
+#pragma unroll
+            for (int j = 0; j < KVPW; ++j) {
+                const int t = wave + kWaves * j;
+                if (t < NKV) {
+                    const int a = t / NCT, c = t % NCT;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) dst[(int64_t)(16 * a + 4 * g + r) * D + 16 * c + li] = kv[j][r];
+                }
+            }
+        }
+        if (nxt.nb > 0 && nxt.first_of_doc) {
+#pragma unroll
+            for (int j = 0; j < KVPW; ++j) kv[j] = zero4();
+        }
+#pragma unroll
+        for (int j = 0; j < KVPW; ++j) {
+            const int t = wave + kWaves * j;
+            if (t < NKV) {
+                const int a = t / NCT, c = t % NCT;
+                store4(KVt + (16 * c + li) * KP + 16 * a + 4 * g, kv[j][0], kv[j][1], kv[j][2], kv[j][3]);
+            }
+        }
+        cur = nxt;
+    }
+
+    // Empty documents placed in this segment get a zero final state.
+    if (p.kv_out) {
+        const int lo = doc_lower(p.cu, p.num_seqs, t0);
+        const int hi = (u == p.nseg - 1) ? p.num_seqs : doc_lower(p.cu, p.num_seqs, t1);
+        for (int d = lo; d < hi; ++d) {
+            if (p.cu[d + 1] != p.cu[d]) continue;
+            float* dst = p.kv_out + (((int64_t)d * p.H + h) * D) * D + s * W;
+            for (int i = tid; i < D * W; i += kThreads) dst[(int64_t)(i / W) * D + (i % W)] = 0.f;
+        }
+    }
+}
+
+}  // namespace la

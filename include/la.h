@@ -1,0 +1,157 @@
+/*
+ * la.h -- C ABI of the causal linear attention library for AMD MI355X (gfx950).
+ *
+ * The operation, per document and head (tokens of that document only):
+ *     KV_t = sum_{s <= t} k_s^T v_s        (d x d, row i = key dim, column j = value dim)
+ *     o_t  = q_t . KV_t = sum_{s <= t} (q_t . k_s) v_s
+ * i.e. linear attention without softmax, computed as on the MiniMax-01 pages:
+ * "MiniMax-01技术报告解读（一）模型架构" (CSDN) and "MiniMax-01技术报告解读"
+ * (qingkelab), §2.2 线性注意力 -- the right-product trick with a recursively
+ * updated key-value product; Q, K, V are tiled along the sequence into blocks,
+ * with a left product inside each block and a right product across blocks.
+ * There is no scale, feature map, normaliser or decay (the pages define none);
+ * the causal mask includes the current token.
+ *
+ * Layouts
+ *   q, k, v, o : token-major packed [T, H, d]; element (t, h, i) at (t*H + h)*d + i.
+ *   states     : fp32 [num_seqs, H, d, d]; element (i = key, j = value) at i*d + j,
+ *                so that o = q . KV.
+ *   cu_seqlens : int32 [num_seqs + 1] in DEVICE memory, 0 = c_0 <= c_1 <= ... <= c_D = T.
+ *                Documents may be empty.  Monotonicity and c_D = T are preconditions
+ *                (the values live on the device and are not checked).
+ *
+ * Ownership and execution
+ *   Every pointer is caller-owned device memory.  The library allocates, frees
+ *   and synchronises nothing and keeps no mutable global state, so calls are
+ *   reentrant and thread-safe.  Work is enqueued on `stream` (a hipStream_t;
+ *   NULL = the null stream) and the call returns after enqueueing.
+ *
+ * Errors
+ *   Arguments are validated on the host before anything is enqueued; a rejected
+ *   call returns a status and enqueues nothing.  A failed kernel launch returns
+ *   LA_ERR_HIP.  Asynchronous device faults surface on the stream as usual.
+ */
+#ifndef LA_H
+#define LA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    LA_OK = 0,
+    LA_ERR_INVALID_ARG = 1, /* null / misaligned / overlapping pointer, H < 1, num_seqs < 1, T < 0 */
+    LA_ERR_UNSUPPORTED = 2, /* d, block, dtype or tuning value outside the supported set */
+    LA_ERR_WORKSPACE = 3,   /* workspace_bytes below la_prefill_workspace_size() or NULL workspace */
+    LA_ERR_HIP = 4          /* a HIP launch failed */
+} la_status;
+
+typedef enum { LA_BF16 = 0, LA_FP32 = 1 } la_dtype;
+
+/* Bytes of device workspace la_prefill needs for this shape (0 if none).
+ * Depends only on the arguments.  Returns 0 for arguments la_prefill rejects. */
+size_t la_prefill_workspace_size(int64_t total_tokens, int32_t num_seqs, int32_t H, int32_t d, int32_t block,
+                                 la_dtype dtype);
+
+/* Prefill: causal linear attention over packed variable-length documents,
+ * Lightning-style (blocks of `block` tokens: masked left product inside a
+ * block, right product against the running d x d state across blocks, state
+ * update KV += K^T V after each block).  The state restarts at zero at every
+ * document start: packed samples are independent ("MiniMax-01技术报告解读",
+ * §3.2 item 1 数据打包, item 4 变长特征支持).  Block sizes 32/64/128 follow the
+ * segment options of §3.3 item 3 (多级填充); document tails are predicated,
+ * not padded in memory.
+ *
+ *   q, k, v      [T, H, d] dtype, device, 16-byte aligned, read only.
+ *   o            [T, H, d] dtype, device, 16-byte aligned, fully overwritten;
+ *                must not overlap q, k, v.
+ *   cu_seqlens   [num_seqs + 1] int32, device.
+ *   H            heads, >= 1.
+ *   d            head dim: 16, 32, 64 or 128.
+ *   block        32, 64 or 128 (fp32 with d >= 64: 32 or 64).
+ *   kv_state_out [num_seqs, H, d, d] fp32, device, 16-byte aligned, or NULL.
+ *                Row (doc, h) receives KV after the document's last token (zero
+ *                for an empty document).  Must not overlap q, k, v, o.
+ *   num_seqs     documents, >= 1.
+ *   total_tokens T = cu_seqlens[num_seqs], >= 0.
+ *   dtype        LA_BF16 (bf16 MFMA, fp32 accumulation, fp32 state, bf16 output
+ *                rounded to nearest even) or LA_FP32 (fp32 throughout).
+ *   workspace    device scratch of at least la_prefill_workspace_size() bytes,
+ *                256-byte aligned (NULL allowed when that size is 0).  Its
+ *                contents on entry are ignored; it must not be shared by calls
+ *                in flight at the same time.
+ *   stream       hipStream_t or NULL.
+ */
+la_status la_prefill(const void* q, const void* k, const void* v, void* o, const int32_t* cu_seqlens, int32_t H,
+                     int32_t d, int32_t block, float* kv_state_out, int32_t num_seqs, int64_t total_tokens,
+                     la_dtype dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Decode: one length-1 step for num_seqs independent sequences, each with H
+ * heads ("MiniMax-01技术报告解读", §3.3 item 2 分离预填充和解码执行: length-1
+ * tokens get their own kernel; item 1: the step fuses the KV computation with
+ * the prefix KV-cache update).  Per (seq, head):
+ *     KV <- KV + k^T v ;   o = q . KV        (update first: s <= t includes t)
+ *
+ *   q, k, v        [num_seqs, H, d] dtype, device, 16-byte aligned.
+ *   kv_state_inout [num_seqs, H, d, d] fp32, device, 16-byte aligned, updated in place.
+ *   o              [num_seqs, H, d] dtype, device, 16-byte aligned; no overlap with
+ *                  the other arguments.
+ *   d              16, 32, 64 or 128.
+ */
+la_status la_decode(const void* q, const void* k, const void* v, float* kv_state_inout, void* o, int32_t num_seqs,
+                    int32_t H, int32_t d, la_dtype dtype, void* stream);
+
+/* Human-readable status name (static string). */
+const char* la_status_string(la_status s);
+
+/* ------------------------------------------------------------------------
+ * Tuned prefill: the same operation as la_prefill (identical results up to
+ * floating-point summation order) with explicit work decomposition and
+ * optional timing events.
+ *
+ * The packed token range is cut into segments of seg_len tokens; a workgroup
+ * handles one (segment, head, value-column slice).  When a document spans
+ * several segments, each segment first reduces its K^T V (a segment state),
+ * the states are prefix-summed per document, and each segment then runs the
+ * block loop from its prefix -- the single-GPU form of the LASP+ scheme of
+ * "MiniMax-01技术报告解读", §3.2 item 3 (local prefix states, one exchange,
+ * global prefix).
+ */
+typedef struct {
+    int32_t seg_len;        /* tokens per segment, a multiple of block; 0 = automatic */
+    int32_t value_slices;   /* 1, 2 or 4 value-column slices per head; 0 = automatic */
+    int32_t force_scan;     /* 1 = always run the separate prefix-scan kernel */
+    int32_t reserved;
+    void* main_begin_event; /* hipEvent_t recorded on the stream right before the
+                               block-loop kernel is launched, or NULL */
+    void* main_end_event;   /* hipEvent_t recorded right after it, or NULL */
+} la_prefill_opts;
+
+/* The decomposition a prefill call will use (for reports and tests). */
+typedef struct {
+    int32_t seg_len;
+    int32_t value_slices;
+    int32_t num_segments;
+    int32_t scan;          /* 1 if the prefix-scan kernel runs */
+    int64_t units;         /* workgroups of the block-loop kernel */
+    size_t workspace_bytes;
+} la_prefill_plan_info;
+
+la_status la_prefill_plan(int64_t total_tokens, int32_t num_seqs, int32_t H, int32_t d, int32_t block,
+                          la_dtype dtype, const la_prefill_opts* opts, la_prefill_plan_info* out);
+
+size_t la_prefill_workspace_size_ex(int64_t total_tokens, int32_t num_seqs, int32_t H, int32_t d, int32_t block,
+                                    la_dtype dtype, const la_prefill_opts* opts);
+
+la_status la_prefill_ex(const void* q, const void* k, const void* v, void* o, const int32_t* cu_seqlens, int32_t H,
+                        int32_t d, int32_t block, float* kv_state_out, int32_t num_seqs, int64_t total_tokens,
+                        la_dtype dtype, void* workspace, size_t workspace_bytes, void* stream,
+                        const la_prefill_opts* opts);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* LA_H */

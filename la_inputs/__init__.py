@@ -138,6 +138,8 @@ def decode_states(seed: int, num_seqs: int, H: int, d: int, lo: int, hi: int, fi
         assert fn.size == num_seqs * H
     rc = _load().lagen_decode_states(seed, TID_STATE, TID_PREFIX, num_seqs, H, d, lo, hi,
                                      _ptr(fn) if fn is not None else None, _ptr(out), nthreads)
+    if rc == -2:
+        raise ValueError("prefix lengths must be >= d")
     if rc != 0:
         raise ValueError("unsupported d")
     return out

@@ -191,8 +191,13 @@ static inline double st_normal(stream_t* s) {
     return sqrt(-2.0 * log(u1)) * cos(TWO_PI * u2);
 }
 
-/* Gamma(alpha, 1) for alpha >= 1, Marsaglia & Tsang (2000). */
+/* Gamma(alpha, 1), Marsaglia & Tsang (2000); for alpha < 1 their boost
+ * Gamma(alpha) = Gamma(alpha + 1) * U^(1/alpha). */
 static double st_gamma(stream_t* s, double alpha) {
+    if (alpha < 1.0) {
+        double g = st_gamma(s, alpha + 1.0);
+        return g * pow(st_u01_open0(s), 1.0 / alpha);
+    }
     double dd = alpha - 1.0 / 3.0, cc = 1.0 / sqrt(9.0 * dd);
     for (;;) {
         double x = st_normal(s), v = 1.0 + cc * x;
@@ -256,10 +261,18 @@ static void kv_range(void* cv, int64_t lo, int64_t hi) {
 
 /* Incoming decode states for npairs = num_seqs * H pairs, fp32 [npairs, d, d],
  * state[i][j] indexed (key i, value j).  n per sequence is drawn from stream
- * (seed, tid_len) unless fixed_n (per pair) is given.  d <= 512. */
+ * (seed, tid_len) unless fixed_n (per pair) is given.  d <= 512; every n must
+ * be >= d (the Bartlett factor needs n - i >= 1 degrees of freedom): returns
+ * -2 otherwise. */
 int lagen_decode_states(uint64_t seed, uint64_t tid_state, uint64_t tid_len, int64_t num_seqs, int64_t H,
                         int64_t d, int64_t lo, int64_t hi, const int64_t* fixed_n, float* out, int nthreads) {
     if (d < 1 || d > 512) return -1;
+    if (fixed_n) {
+        for (int64_t p = 0; p < num_seqs * H; ++p)
+            if (fixed_n[p] < d) return -2;
+    } else if (lo < d) {
+        return -2;
+    }
     kv_ctx c = {seed, tid_state, tid_len, H, d, lo, hi, fixed_n, out};
     int64_t np = num_seqs * H;
     nthreads = resolve_threads(nthreads);

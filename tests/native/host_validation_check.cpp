@@ -1,0 +1,100 @@
+// Host-only checks of argument validation and planning, built with
+// -fsanitize=address,undefined by tests/test_abi.py (no GPU, no HIP).
+#include <cstdint>
+#include <cstdio>
+#include <cstdlib>
+#include <initializer_list>
+
+#include "../../causal_linear_attention_la_amd/csrc/la_host.h"
+
+static int failures = 0;
+#define EXPECT(cond)                                                   \
+    do {                                                               \
+        if (!(cond)) {                                                 \
+            std::fprintf(stderr, "FAILED %s:%d: %s\n", __FILE__, __LINE__, #cond); \
+            ++failures;                                                \
+        }                                                              \
+    } while (0)
+
+static void* P(uintptr_t x) { return reinterpret_cast<void*>(x); }
+
+int main() {
+    using namespace la;
+    Plan p;
+    const uintptr_t G = 1ull << 40;  // fake, never dereferenced
+    void *q = P(G), *k = P(2 * G), *v = P(3 * G), *o = P(4 * G);
+    const int32_t* cu = static_cast<const int32_t*>(P(5 * G));
+    float* kv = static_cast<float*>(P(6 * G));
+    void* ws = P(7 * G);
+
+    // plans for the standard shapes
+    EXPECT(make_plan(8192, 1, 8, 128, 64, LA_BF16, nullptr, &p) == LA_OK);
+    EXPECT(p.L % 64 == 0 && p.units == (int64_t)p.nseg * 8 * p.S && p.W * p.S == 128);
+    EXPECT(make_plan(256, 1, 2, 16, 32, LA_FP32, nullptr, &p) == LA_OK && p.nseg == 1 && p.ws_bytes == 0);
+    EXPECT(make_plan(1048576, 1, 8, 128, 128, LA_BF16, nullptr, &p) == LA_OK && p.W == 32);
+    EXPECT(make_plan(0, 3, 4, 64, 64, LA_BF16, nullptr, &p) == LA_OK && p.nseg == 1 && p.units == 4 * p.S);
+    // every (d, block, dtype) combination has some plan
+    for (int d : {16, 32, 64, 128})
+        for (int b : {32, 64, 128})
+            for (int dt : {0, 1}) {
+                la_status st = make_plan(5000, 3, 4, d, b, dt, nullptr, &p);
+                bool fp32_big = (dt == 1 && d >= 64 && b == 128);
+                EXPECT(fp32_big ? st == LA_ERR_UNSUPPORTED : st == LA_OK);
+            }
+    // explicit knobs
+    la_prefill_opts o1{};
+    o1.seg_len = 64;
+    o1.value_slices = 4;
+    EXPECT(make_plan(8192, 1, 8, 128, 64, LA_BF16, &o1, &p) == LA_OK && p.L == 64 && p.S == 4 && p.nseg == 128 && p.scan == 1);
+    o1.seg_len = 96;
+    EXPECT(make_plan(8192, 1, 8, 128, 64, LA_BF16, &o1, &p) == LA_ERR_UNSUPPORTED);
+    o1.seg_len = 0;
+    o1.value_slices = 3;
+    EXPECT(make_plan(8192, 1, 8, 128, 64, LA_BF16, &o1, &p) == LA_ERR_UNSUPPORTED);
+    o1.value_slices = 8;
+    EXPECT(make_plan(8192, 1, 8, 128, 64, LA_BF16, &o1, &p) == LA_ERR_UNSUPPORTED);
+
+    // shape errors
+    EXPECT(make_plan(-1, 1, 8, 128, 64, LA_BF16, nullptr, &p) == LA_ERR_INVALID_ARG);
+    EXPECT(make_plan(10, 0, 8, 128, 64, LA_BF16, nullptr, &p) == LA_ERR_INVALID_ARG);
+    EXPECT(make_plan(10, 1, 0, 128, 64, LA_BF16, nullptr, &p) == LA_ERR_INVALID_ARG);
+    EXPECT(make_plan(10, 1, 8, 96, 64, LA_BF16, nullptr, &p) == LA_ERR_UNSUPPORTED);
+    EXPECT(make_plan(10, 1, 8, 128, 48, LA_BF16, nullptr, &p) == LA_ERR_UNSUPPORTED);
+    EXPECT(make_plan(10, 1, 8, 128, 64, 7, nullptr, &p) == LA_ERR_UNSUPPORTED);
+    EXPECT(make_plan((int64_t)1 << 33, 1, 8, 128, 64, LA_BF16, nullptr, &p) == LA_ERR_INVALID_ARG);
+
+    // pointer errors
+    const int64_t T = 8192;
+    EXPECT(make_plan(T, 1, 8, 128, 64, LA_BF16, nullptr, &p) == LA_OK);
+    const size_t need = p.ws_bytes;
+    EXPECT(validate_prefill(q, k, v, o, cu, 8, 128, 64, kv, 1, T, LA_BF16, ws, need, nullptr, &p) == LA_OK);
+    EXPECT(validate_prefill(nullptr, k, v, o, cu, 8, 128, 64, kv, 1, T, LA_BF16, ws, need, nullptr, &p) == LA_ERR_INVALID_ARG);
+    EXPECT(validate_prefill(q, k, v, nullptr, cu, 8, 128, 64, kv, 1, T, LA_BF16, ws, need, nullptr, &p) == LA_ERR_INVALID_ARG);
+    EXPECT(validate_prefill(q, k, v, o, nullptr, 8, 128, 64, kv, 1, T, LA_BF16, ws, need, nullptr, &p) == LA_ERR_INVALID_ARG);
+    EXPECT(validate_prefill(P(G + 8), k, v, o, cu, 8, 128, 64, kv, 1, T, LA_BF16, ws, need, nullptr, &p) == LA_ERR_INVALID_ARG);
+    EXPECT(validate_prefill(q, k, v, P(G + 4096), cu, 8, 128, 64, kv, 1, T, LA_BF16, ws, need, nullptr, &p) == LA_ERR_INVALID_ARG);
+    EXPECT(validate_prefill(q, k, v, o, cu, 8, 128, 64, static_cast<float*>(P(4 * G + 64)), 1, T, LA_BF16, ws, need, nullptr, &p) == LA_ERR_INVALID_ARG);
+    EXPECT(validate_prefill(q, k, v, o, cu, 8, 128, 64, kv, 1, T, LA_BF16, nullptr, need, nullptr, &p) == (need ? LA_ERR_WORKSPACE : LA_OK));
+    if (need) {
+        EXPECT(validate_prefill(q, k, v, o, cu, 8, 128, 64, kv, 1, T, LA_BF16, ws, need - 1, nullptr, &p) == LA_ERR_WORKSPACE);
+        EXPECT(validate_prefill(q, k, v, o, cu, 8, 128, 64, kv, 1, T, LA_BF16, P(7 * G + 16), need, nullptr, &p) == LA_ERR_INVALID_ARG);
+        EXPECT(validate_prefill(q, k, v, o, cu, 8, 128, 64, kv, 1, T, LA_BF16, P(G), need, nullptr, &p) == LA_ERR_INVALID_ARG);
+    }
+    EXPECT(validate_prefill(q, k, v, o, cu, 8, 128, 64, nullptr, 1, T, LA_BF16, ws, need, nullptr, &p) == LA_OK);
+
+    // decode
+    EXPECT(validate_decode(q, k, v, kv, o, 256, 64, 128, LA_BF16) == LA_OK);
+    EXPECT(validate_decode(q, k, v, kv, o, 0, 64, 128, LA_BF16) == LA_ERR_INVALID_ARG);
+    EXPECT(validate_decode(q, k, v, kv, o, 256, 64, 100, LA_BF16) == LA_ERR_UNSUPPORTED);
+    EXPECT(validate_decode(q, k, v, kv, q, 256, 64, 128, LA_BF16) == LA_ERR_INVALID_ARG);
+    EXPECT(validate_decode(q, k, v, static_cast<float*>(P(G + 16)), o, 256, 64, 128, LA_BF16) == LA_ERR_INVALID_ARG);
+    EXPECT(validate_decode(q, k, v, static_cast<float*>(P(6 * G + 4)), o, 256, 64, 128, LA_BF16) == LA_ERR_INVALID_ARG);
+    EXPECT(validate_decode(q, k, v, kv, o, 256, 64, 128, 5) == LA_ERR_UNSUPPORTED);
+
+    if (failures) {
+        std::fprintf(stderr, "%d check(s) failed\n", failures);
+        return 1;
+    }
+    std::printf("host validation checks passed\n");
+    return 0;
+}

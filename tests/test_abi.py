@@ -1,0 +1,125 @@
+"""C-ABI checks that need no GPU: the library loads, exports every entry point
+include/la.h declares, and rejects bad arguments on the host before anything
+is enqueued (only invalid calls are made here)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import causal_linear_attention_la_amd as la
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "la.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(la.LIB_PATH):
+        la.build()
+    return la.load()
+
+
+def declared_functions():
+    text = open(HEADER, encoding="utf-8").read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"\b(?:la_status|size_t|const char\s*\*)\s+(la_\w+)\s*\(", text)
+    return sorted(set(names))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert set(la.EXPORTED) <= set(names)
+    out = subprocess.run(["nm", "-D", "--defined-only", la.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (la_\w+)", out))
+    missing = [n for n in names if n not in exported]
+    assert not missing, missing
+    for n in names:
+        assert hasattr(lib, n)
+
+
+def test_status_strings(lib):
+    assert la.status_string(0) == "LA_OK"
+    assert la.status_string(3) == "LA_ERR_WORKSPACE"
+    assert la.status_string(99) == "LA_ERR_UNKNOWN"
+
+
+G = 1 << 40  # fake device addresses: validation rejects before any use
+
+
+def _prefill(**kw):
+    a = dict(q=G, k=2 * G, v=3 * G, o=4 * G, cu=5 * G, H=8, d=128, block=64, kv=6 * G, num_seqs=1, T=8192,
+             dtype=la.LA_BF16, ws=7 * G, ws_bytes=1 << 30)
+    a.update(kw)
+    vp = lambda x: ctypes.c_void_p(x) if x else None
+    return la.la_prefill(vp(a["q"]), vp(a["k"]), vp(a["v"]), vp(a["o"]), vp(a["cu"]), a["H"], a["d"], a["block"],
+                         vp(a["kv"]), a["num_seqs"], a["T"], a["dtype"], vp(a["ws"]), a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=0), la.LA_ERR_INVALID_ARG),
+    (dict(o=0), la.LA_ERR_INVALID_ARG),
+    (dict(cu=0), la.LA_ERR_INVALID_ARG),
+    (dict(H=0), la.LA_ERR_INVALID_ARG),
+    (dict(num_seqs=0), la.LA_ERR_INVALID_ARG),
+    (dict(T=-5), la.LA_ERR_INVALID_ARG),
+    (dict(d=48), la.LA_ERR_UNSUPPORTED),
+    (dict(block=16), la.LA_ERR_UNSUPPORTED),
+    (dict(dtype=9), la.LA_ERR_UNSUPPORTED),
+    (dict(dtype=la.LA_FP32, block=128), la.LA_ERR_UNSUPPORTED),
+    (dict(q=G + 8), la.LA_ERR_INVALID_ARG),
+    (dict(o=G + 4096), la.LA_ERR_INVALID_ARG),       # o overlaps q
+    (dict(kv=3 * G + 16), la.LA_ERR_INVALID_ARG),    # state overlaps v
+    (dict(kv=6 * G + 4), la.LA_ERR_INVALID_ARG),     # misaligned state
+    (dict(ws=0), la.LA_ERR_WORKSPACE),
+    (dict(ws_bytes=16), la.LA_ERR_WORKSPACE),
+    (dict(ws=7 * G + 64), la.LA_ERR_INVALID_ARG),    # workspace not 256-aligned
+])
+def test_prefill_rejects(lib, kw, status):
+    assert _prefill(**kw) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=0), la.LA_ERR_INVALID_ARG),
+    (dict(S=0), la.LA_ERR_INVALID_ARG),
+    (dict(num_seqs=0), la.LA_ERR_INVALID_ARG),
+    (dict(H=-1), la.LA_ERR_INVALID_ARG),
+    (dict(d=100), la.LA_ERR_UNSUPPORTED),
+    (dict(dtype=3), la.LA_ERR_UNSUPPORTED),
+    (dict(o=G), la.LA_ERR_INVALID_ARG),
+    (dict(S=G + 16), la.LA_ERR_INVALID_ARG),
+    (dict(S=6 * G + 8), la.LA_ERR_INVALID_ARG),
+])
+def test_decode_rejects(lib, kw, status):
+    a = dict(q=G, k=2 * G, v=3 * G, S=6 * G, o=4 * G, num_seqs=256, H=64, d=128, dtype=la.LA_BF16)
+    a.update(kw)
+    vp = lambda x: ctypes.c_void_p(x) if x else None
+    assert la.la_decode(vp(a["q"]), vp(a["k"]), vp(a["v"]), vp(a["S"]), vp(a["o"]), a["num_seqs"], a["H"], a["d"],
+                        a["dtype"], None) == status
+
+
+def test_plans(lib):
+    p = la.la_prefill_plan(8192, 1, 8, 128, 64, la.LA_BF16)
+    assert p["units"] == p["num_segments"] * 8 * p["value_slices"] and p["seg_len"] % 64 == 0
+    assert p["workspace_bytes"] == la.la_prefill_workspace_size(8192, 1, 8, 128, 64, la.LA_BF16)
+    p = la.la_prefill_plan(256, 1, 2, 16, 32, la.LA_FP32)
+    assert p["num_segments"] == 1 and p["workspace_bytes"] == 0
+    p = la.la_prefill_plan(1048576, 1, 8, 128, 64, la.LA_BF16)
+    assert p["units"] >= 256
+    o = la.make_opts(seg_len=64, value_slices=2)
+    p = la.la_prefill_plan(8192, 1, 8, 128, 64, la.LA_BF16, o)
+    assert (p["seg_len"], p["value_slices"], p["num_segments"], p["scan"]) == (64, 2, 128, 1)
+    assert p["workspace_bytes"] >= 128 * 8 * 128 * 128 * 4
+    with pytest.raises(la.LAError):
+        la.la_prefill_plan(8192, 1, 8, 128, 64, la.LA_BF16, la.make_opts(seg_len=100))
+
+
+def test_host_validation_under_sanitizers(tmp_path):
+    exe = str(tmp_path / "hvc")
+    src = [os.path.join(ROOT, "tests", "native", "host_validation_check.cpp"),
+           os.path.join(ROOT, "causal_linear_attention_la_amd", "csrc", "la_host.cpp")]
+    subprocess.check_call(["g++", "-std=c++17", "-O1", "-g", "-fsanitize=address,undefined",
+                           "-fno-sanitize-recover=undefined", *src, "-o", exe])
+    r = subprocess.run([exe], capture_output=True, text=True)
+    assert r.returncode == 0, r.stdout + r.stderr

@@ -103,3 +103,14 @@ def test_decode_state_prefix_lengths(inputs_lib):
     assert S.shape == (6, 8, 8) and np.all(np.isfinite(S))
     S2 = la_inputs.decode_states(105, 2, 3, 8, 1024, 1 << 20, nthreads=1)
     assert np.array_equal(S, S2)
+
+
+def test_decode_state_sampler_small_prefix(inputs_lib):
+    """n just above d exercises chi-square shapes below 1 (boosted gamma draws);
+    entries keep variance n/d^2.  n < d is rejected."""
+    d, n, pairs = 8, 9, 4000
+    S = la_inputs.decode_states(4, 1, pairs, d, 1, 2, fixed_n=np.full(pairs, n)).astype(np.float64)
+    assert np.all(np.isfinite(S))
+    assert abs(S.var() / (n / d ** 2) - 1.0) < 0.05
+    with pytest.raises(ValueError):
+        la_inputs.decode_states(4, 1, 2, 8, 1, 2, fixed_n=np.array([7, 9]))
