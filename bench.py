@@ -1,0 +1,335 @@
+#!/usr/bin/env python3
+"""Benchmark: causal linear attention (Lightning-style) on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload prefill_8k]
+
+A step is one pass of the hot path over one batch of synthetic input: one
+la_prefill call over the workload (segment states, prefix scan when needed,
+block loop).  The default workload is the 8-head x 8192-token bf16 prefill
+(d = 128, block 64).  Inputs are generated on the host from fixed seeds,
+copied to HBM before timing, and rotated over several input sets so that the
+timed steps read HBM rather than the 256 MB last-level cache.  The decode
+workload (256 sequences x 64 heads, fp32 state, 1000 steps) is timed in the
+same run and reported under "decode".
+
+Prints one JSON line.  `roofline` is for the block-loop kernel: algorithmic
+bytes (q, k, v read + o written, 8 d bytes per token-head) per launch over its
+average duration, measured with HIP events recorded on the launch stream
+around every launch inside the timed region.  `cpu_baseline` times the fp64
+oracle (the recurrent form) on the host cores for the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+KERNEL_SOURCES = ["la_prefill_kernels.h", "la_device.h", "la_tiles.h", "la_prefill_launch.inl", "la_host.cpp"]
+DECODE_SOURCES = ["la_decode_kernels.h", "la_device.h"]
+
+
+def sources_sha(names) -> str:
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "causal_linear_attention_la_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+class Hip:
+    """hipEvent helpers through the HIP runtime (events on the launch stream)."""
+
+    def __init__(self):
+        self.lib = ctypes.CDLL("libamdhip64.so")
+        self.lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+
+    def event(self):
+        e = ctypes.c_void_p()
+        rc = self.lib.hipEventCreate(ctypes.byref(e))
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreate failed ({rc})")
+        return e
+
+    def record(self, e, stream_ptr):
+        rc = self.lib.hipEventRecord(e, ctypes.c_void_p(stream_ptr))
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord failed ({rc})")
+
+    def elapsed_ms(self, a, b) -> float:
+        ms = ctypes.c_float()
+        rc = self.lib.hipEventElapsedTime(ctypes.byref(ms), a, b)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return float(ms.value)
+
+    def destroy(self, e):
+        self.lib.hipEventDestroy(e)
+
+
+def load_traffic(kernel: str, workload: str, sha: str):
+    """HBM bytes per launch from a committed rocprofv3 counter summary, if it
+    was taken on the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_sources_sha") != sha:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, target_cpu_s: float = 10.0) -> dict:
+    """The fp64 oracle as it stands, over the whole workload, repeated until
+    about target_cpu_s seconds of CPU time have been spent."""
+    import oracle
+
+    oracle.build()
+    reps, wall = 0, 0.0
+    while True:
+        t0 = time.perf_counter()
+        oracle.recurrent(w["q"], w["k"], w["v"], w["cu"], want_o=True, want_state=True)
+        wall += time.perf_counter() - t0
+        reps += 1
+        threads = oracle.last_threads()
+        if wall * threads >= target_cpu_s or reps >= 50:
+            break
+    th = w["T"] * w["H"] * reps / wall
+    return {"value": th, "unit": "token·heads/s", "cores": threads, "kind": "oracle",
+            "sample": f"whole {w['name']} workload ({w['T']} tokens x {w['H']} heads, d={w['d']}), "
+                      f"fp64 recurrent form, {reps} repetitions, {wall:.2f} s wall"}
+
+
+def bench_prefill(args, la, torch, hip):
+    import la_inputs
+
+    name = args.workload
+    cfg = la_inputs.WORKLOADS[name]
+    w = la_inputs.prefill_inputs(name)
+    w["name"] = name
+    T, H, d, block = w["T"], w["H"], w["d"], args.block or w["block"]
+    dt = la.LA_BF16 if w["dtype"] == "bf16" else la.LA_FP32
+    num_seqs = len(w["cu"]) - 1
+    opts = dict(seg_len=args.seg_len, value_slices=args.slices, force_scan=args.force_scan)
+    plan = la.la_prefill_plan(T, num_seqs, H, d, block, dt, la.make_opts(**opts))
+
+    def dev(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(a).cuda()
+
+    # input sets: set 0 is the seeded workload, the others are copies shifted
+    # by one token per set (same statistics, different bytes in HBM)
+    per_set = 4 * T * H * d * (2 if w["dtype"] == "bf16" else 4)
+    nsets = max(1, min(args.rotate, int((8 << 30) // max(per_set, 1))))
+    q0, k0, v0 = dev(w["q"]), dev(w["k"]), dev(w["v"])
+    sets = []
+    for i in range(nsets):
+        sh = i % max(T, 1)
+        q, k, v = (torch.roll(x, sh, 0).contiguous() if sh else x for x in (q0, k0, v0))
+        sets.append((q, k, v, torch.empty_like(q)))
+    cu = torch.from_numpy(w["cu"]).cuda()
+    kv = torch.empty((num_seqs, H, d, d), dtype=torch.float32, device="cuda")
+    ws_bytes = plan["workspace_bytes"]
+    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+
+    def step(i, ev0=None, ev1=None):
+        q, k, v, o = sets[i % nsets]
+        la.prefill(q, k, v, cu, block=block, out=o, kv_state_out=kv, workspace=ws, begin_event=ev0, end_event=ev1,
+                   **opts)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    K = args.steps
+    evs = [(hip.event(), hip.event()) for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        step(i, evs[i][0], evs[i][1])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    kernel_ms = [hip.elapsed_ms(a, b) for a, b in evs]
+    for a, b in evs:
+        hip.destroy(a)
+        hip.destroy(b)
+
+    # the same steps replayed from a HIP graph (launch overhead removed)
+    graph_value = None
+    if not args.no_graph:
+        g = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(stream)
+        with torch.cuda.stream(s):
+            step(0)
+            torch.cuda.synchronize()
+            with torch.cuda.graph(g, stream=s):
+                for i in range(nsets):
+                    step(i)
+        torch.cuda.synchronize()
+        reps = max(1, K // nsets)
+        g.replay()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        for _ in range(reps):
+            g.replay()
+        torch.cuda.synchronize()
+        graph_elapsed = time.perf_counter() - t1
+        graph_value = T * H * nsets * reps / graph_elapsed
+
+    avg_kernel_s = float(np.mean(kernel_ms)) / 1e3
+    algo_bytes = T * H * 8 * d * (1 if w["dtype"] == "bf16" else 2)
+    achieved = algo_bytes / avg_kernel_s / 1e9
+    sha = sources_sha(KERNEL_SOURCES)
+    traffic = load_traffic("la_prefill_main_kernel", name, sha)
+    value = T * H * K / elapsed
+    roof_th = HBM_PEAK_GBS * 1e9 / (algo_bytes / (T * H))  # whole step at HBM peak
+    rec = {
+        "metric": "prefill tokens·heads/s (bf16, d=128) + % roofline; decode steps/s",
+        "value": value,
+        "unit": "token·heads/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": elapsed / K * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w["dtype"],
+        "data": "synthetic",
+        "config": {"workload": name, "documents": num_seqs, "heads": H, "tokens": T, "head_dim": d, "block": block,
+                   "seg_len": plan["seg_len"], "value_slices": plan["value_slices"],
+                   "segments": plan["num_segments"], "scan": plan["scan"], "workgroups": plan["units"],
+                   "input_sets": nsets},
+        "roofline": {"bound": "hbm", "kernel": "la_prefill_main_kernel", "achieved": achieved,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": traffic, "kernel_ms": avg_kernel_s * 1e3,
+                     "algorithmic_bytes": algo_bytes, "kernel_sources_sha": sha},
+        "path_roofline": {"token_heads_per_s": roof_th, "frac": value / roof_th},
+        "graph_replay_value": graph_value,
+    }
+    return rec, w
+
+
+def bench_decode(args, la, torch, hip):
+    import la_inputs
+
+    cfg = la_inputs.WORKLOADS["decode_256x64"]
+    ns, H, d, seed, pool = cfg["num_seqs"], cfg["H"], cfg["d"], cfg["seed"], cfg["pool"]
+    lo, hi = cfg["prefix"]
+    steps = args.decode_steps
+    S0 = la_inputs.decode_states(seed, ns, H, d, lo, hi)
+    S = torch.from_numpy(S0.reshape(ns, H, d, d)).cuda()
+    del S0
+    dev = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+    sets = [tuple(dev(x) for x in la_inputs.decode_step_inputs(seed, s, ns, H, d, "bf16")) for s in range(pool)]
+    o = torch.empty((ns, H, d), dtype=torch.bfloat16, device="cuda")
+    for i in range(10):
+        la.decode(*sets[i % pool], S, out=o)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream().cuda_stream
+    e0, e1 = hip.event(), hip.event()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    hip.record(e0, stream)
+    for i in range(steps):
+        la.decode(*sets[i % pool], S, out=o)
+    hip.record(e1, stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_s = hip.elapsed_ms(e0, e1) / 1e3
+    hip.destroy(e0)
+    hip.destroy(e1)
+    bytes_step = ns * H * (2 * d * d * 4 + 4 * d * 2)
+    achieved = bytes_step * steps / gpu_s / 1e9
+    return {"workload": "decode_256x64", "value": steps / wall, "unit": "steps/s", "steps": steps,
+            "ms_per_step": wall / steps * 1e3, "gpu_ms_per_step": gpu_s / steps * 1e3,
+            "roofline": {"bound": "hbm", "kernel": "la_decode_kernel", "achieved": achieved, "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "bytes_per_step": bytes_step,
+                         "kernel_sources_sha": sources_sha(DECODE_SOURCES)}}
+
+
+def profile_pass(args, la, torch):
+    """Short run for rocprofv3 counter passes: a 256 MiB device copy (the
+    calibration kernel) then a few prefill steps of the workload."""
+    import la_inputs
+
+    src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    w = la_inputs.prefill_inputs(args.workload)
+    dev = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+    q, k, v = dev(w["q"]), dev(w["k"]), dev(w["v"])
+    cu = torch.from_numpy(w["cu"]).cuda()
+    for _ in range(args.steps):
+        la.prefill(q, k, v, cu, block=args.block or w["block"])
+    torch.cuda.synchronize()
+    print(json.dumps({"profile_pass": args.workload, "steps": args.steps}))
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--workload", default="prefill_8k",
+                    choices=["prefill_8k", "varlen_128k", "long_1m", "tiny_fp32"])
+    ap.add_argument("--block", type=int, default=0)
+    ap.add_argument("--seg-len", type=int, default=0)
+    ap.add_argument("--slices", type=int, default=0)
+    ap.add_argument("--force-scan", action="store_true")
+    ap.add_argument("--rotate", type=int, default=8, help="input sets cycled through the timed steps")
+    ap.add_argument("--decode-steps", type=int, default=1000)
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--profile-pass", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path (use --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import causal_linear_attention_la_amd as la
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    la.load()
+    if args.profile_pass:
+        profile_pass(args, la, torch)
+        return
+    hip = Hip()
+    rec, w = bench_prefill(args, la, torch, hip)
+    if not args.no_decode:
+        rec["decode"] = bench_decode(args, la, torch, hip)
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(w)
+    else:
+        rec["cpu_baseline"] = None
+    print(json.dumps(rec))
+
+
+if __name__ == "__main__":
+    main()

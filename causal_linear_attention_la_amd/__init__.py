@@ -31,7 +31,7 @@ class LAError(RuntimeError):
 
 class la_prefill_opts(ctypes.Structure):
     _fields_ = [("seg_len", ctypes.c_int32), ("value_slices", ctypes.c_int32), ("force_scan", ctypes.c_int32),
-                ("reserved", ctypes.c_int32), ("main_begin_event", ctypes.c_void_p),
+                ("variant", ctypes.c_int32), ("main_begin_event", ctypes.c_void_p),
                 ("main_end_event", ctypes.c_void_p)]
 
 
@@ -103,8 +103,8 @@ def la_prefill_workspace_size(total_tokens, num_seqs, H, d, block, dtype) -> int
 
 
 def make_opts(seg_len: int = 0, value_slices: int = 0, force_scan: bool = False, begin_event=None,
-              end_event=None) -> la_prefill_opts:
-    return la_prefill_opts(int(seg_len), int(value_slices), 1 if force_scan else 0, 0,
+              end_event=None, variant: int = 0) -> la_prefill_opts:
+    return la_prefill_opts(int(seg_len), int(value_slices), 1 if force_scan else 0, int(variant),
                            _event_ptr(begin_event), _event_ptr(end_event))
 
 
@@ -126,8 +126,12 @@ def la_prefill_plan(total_tokens, num_seqs, H, d, block, dtype, opts=None) -> di
 # ------------------------------------------------------------ torch layer
 
 def _event_ptr(ev):
+    """hipEvent_t handle from a ctypes pointer, an int, or a torch.cuda.Event
+    (which must have been recorded once, so that it exists)."""
     if ev is None:
         return None
+    if isinstance(ev, ctypes.c_void_p):
+        return ev
     return ctypes.c_void_p(int(ev.cuda_event) if hasattr(ev, "cuda_event") else int(ev))
 
 
@@ -154,7 +158,7 @@ def _ptr(t):
 
 def prefill(q, k, v, cu_seqlens, block: int = 64, want_state: bool = True, out=None, kv_state_out=None,
             workspace=None, seg_len: int = 0, value_slices: int = 0, force_scan: bool = False, stream=None,
-            begin_event=None, end_event=None):
+            begin_event=None, end_event=None, variant: int = 0):
     """Lightning-style causal linear attention over packed documents.
 
     q, k, v: [T, H, d] bf16/fp32 CUDA tensors; cu_seqlens: int32 [num_seqs + 1]
@@ -170,7 +174,7 @@ def prefill(q, k, v, cu_seqlens, block: int = 64, want_state: bool = True, out=N
     kv = kv_state_out
     if kv is None and want_state:
         kv = torch.empty((num_seqs, H, d, d), dtype=torch.float32, device=q.device)
-    opts = make_opts(seg_len, value_slices, force_scan, begin_event, end_event)
+    opts = make_opts(seg_len, value_slices, force_scan, begin_event, end_event, variant)
     need = la_prefill_workspace_size_ex(T, num_seqs, H, d, block, dt, opts)
     ws = workspace
     if need and (ws is None or ws.numel() * ws.element_size() < need):

@@ -12,7 +12,7 @@ namespace {
 constexpr int kNumCUs = 256;      // MI355X compute units
 constexpr int kUnitsTarget = 256; // block-loop workgroups to aim for (one per CU)
 constexpr int kMinSegment = 1024; // shorter segments spend too much on state traffic
-constexpr int kMaxLookback = 8;   // a unit sums at most this many segment states
+constexpr int kMaxLookback = 16;  // a unit sums at most this many segment states
 
 bool is_pow2_in(int32_t x, int32_t lo, int32_t hi) {
     if (x < lo || x > hi) return false;
@@ -51,6 +51,10 @@ la_status make_plan(int64_t T, int32_t num_seqs, int32_t H, int32_t d, int32_t b
         if (S < 1 || d % S != 0) return false;
         return main_fits((int)es, d, block, d / S);
     };
+    // the transpose-read block loop: bf16, d >= 64, 64-token blocks, slices >= 64 columns
+    auto v2_ok = [&](int32_t S) { return dtype == LA_BF16 && d >= 64 && block == 64 && d / S >= 64; };
+    const int32_t variant = opts ? opts->variant : 0;
+    if (variant < 0 || variant > 2) return LA_ERR_UNSUPPORTED;
 
     Plan p;
     const int64_t work = T * (int64_t)H;
@@ -59,8 +63,10 @@ la_status make_plan(int64_t T, int32_t num_seqs, int32_t H, int32_t d, int32_t b
         p.S = opts->value_slices;
     } else {
         int32_t chosen = 0;
+        const bool want_v2 = variant != 1 && v2_ok(1);
         for (int32_t S = 1; S <= 4; S *= 2) {
             if (!slice_ok(S)) continue;
+            if (want_v2 && !v2_ok(S)) break;  // keep the faster loop rather than split further
             chosen = S;
             if (work * S / kUnitsTarget >= kMinSegment) break;
         }
@@ -68,6 +74,8 @@ la_status make_plan(int64_t T, int32_t num_seqs, int32_t H, int32_t d, int32_t b
         p.S = chosen;
     }
     p.W = d / p.S;
+    if (variant == 2 && !v2_ok(p.S)) return LA_ERR_UNSUPPORTED;
+    p.variant = variant;
 
     if (opts && opts->seg_len != 0) {
         if (opts->seg_len < block || opts->seg_len % block != 0) return LA_ERR_UNSUPPORTED;

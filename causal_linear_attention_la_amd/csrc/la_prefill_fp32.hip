@@ -3,8 +3,8 @@
 #include "la_prefill_launch.inl"
 
 namespace la {
-hipError_t launch_prefill_fp32(const PrefillParams& p, int D, int B, int W, hipStream_t st, hipEvent_t e0,
+hipError_t launch_prefill_fp32(const PrefillParams& p, int D, int B, int W, int variant, hipStream_t st, hipEvent_t e0,
                                hipEvent_t e1) {
-    return dispatch_prefill<float>(p, D, B, W, st, e0, e1);
+    return dispatch_prefill<float>(p, D, B, W, variant, st, e0, e1);
 }
 }  // namespace la

@@ -211,7 +211,8 @@ __global__ __launch_bounds__(kThreads, 2) void la_segment_state_kernel(PrefillPa
     int u, h, s;
     if (!unit_of(p, u, h, s)) return;
     if (u >= p.nseg - 1) return;  // nothing after the last segment
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, li = lane & 15, g = lane >> 4;
+    const int tid = threadIdx.x, lane = tid & 63, li = lane & 15, g = lane >> 4;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int t_beg = u * p.L, t_end = (u + 1) * p.L;  // t_end < T here
     const int de = doc_at(p.cu, p.num_seqs, t_end - 1);
     const int dstart = p.cu[de];
@@ -311,7 +312,8 @@ __global__ __launch_bounds__(kThreads, 1) void la_prefill_main_kernel(PrefillPar
 
     int u, h, s;
     if (!unit_of(p, u, h, s)) return;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, li = lane & 15, g = lane >> 4;
+    const int tid = threadIdx.x, lane = tid & 63, li = lane & 15, g = lane >> 4;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int t0 = u * p.L, t1 = min(p.T, t0 + p.L);
     const TIn* qg = static_cast<const TIn*>(p.q);
     const TIn* kg = static_cast<const TIn*>(p.k);

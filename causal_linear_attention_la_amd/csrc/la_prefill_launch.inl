@@ -4,15 +4,30 @@
 namespace la {
 namespace {
 
+// The transpose-read block loop (la_prefill_v2.h) covers bf16, d >= 64,
+// 64-token blocks and slices of at least 64 value columns.
 template <typename T, int D, int B, int W>
-hipError_t run_prefill(const PrefillParams& p, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
+constexpr bool has_v2() {
+    return sizeof(T) == 2 && D >= 64 && B == 64 && W >= 64;
+}
+
+template <typename T, int D, int B, int W>
+hipError_t run_prefill(const PrefillParams& p, int variant, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
     if constexpr (!main_fits((int)sizeof(T), D, B, W)) {
         return hipErrorInvalidValue;
     } else {
         const dim3 block(kThreads);
         const dim3 grid((unsigned)(8 * p.per_xcd));
+        bool use_v2 = false;
+        if constexpr (has_v2<T, D, B, W>()) use_v2 = (variant != 1);
+        if (variant == 2 && !use_v2) return hipErrorInvalidValue;
         if (p.nseg > 1) {
-            la_segment_state_kernel<T, D, B, W><<<grid, block, 0, st>>>(p);
+            if constexpr (has_v2<T, D, B, W>()) {
+                if (use_v2) v2::la_segment_state_v2<D, B, W><<<grid, block, 0, st>>>(p);
+                else la_segment_state_kernel<T, D, B, W><<<grid, block, 0, st>>>(p);
+            } else {
+                la_segment_state_kernel<T, D, B, W><<<grid, block, 0, st>>>(p);
+            }
             if (p.scan) {
                 const int64_t entries = (int64_t)p.H * D * D;
                 la_segment_scan_kernel<8><<<dim3((unsigned)((entries + kThreads - 1) / kThreads)), block, 0, st>>>(
@@ -23,7 +38,12 @@ hipError_t run_prefill(const PrefillParams& p, hipStream_t st, hipEvent_t e0, hi
             hipError_t e = hipEventRecord(e0, st);
             if (e != hipSuccess) return e;
         }
-        la_prefill_main_kernel<T, D, B, W><<<grid, block, 0, st>>>(p);
+        if constexpr (has_v2<T, D, B, W>()) {
+            if (use_v2) v2::la_prefill_main_v2<D, B, W><<<grid, block, 0, st>>>(p);
+            else la_prefill_main_kernel<T, D, B, W><<<grid, block, 0, st>>>(p);
+        } else {
+            la_prefill_main_kernel<T, D, B, W><<<grid, block, 0, st>>>(p);
+        }
         if (e1) {
             hipError_t e = hipEventRecord(e1, st);
             if (e != hipSuccess) return e;
@@ -33,34 +53,35 @@ hipError_t run_prefill(const PrefillParams& p, hipStream_t st, hipEvent_t e0, hi
 }
 
 template <typename T, int D, int B>
-hipError_t by_width(const PrefillParams& p, int W, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
-    if (W == D) return run_prefill<T, D, B, D>(p, st, e0, e1);
+hipError_t by_width(const PrefillParams& p, int W, int variant, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
+    if (W == D) return run_prefill<T, D, B, D>(p, variant, st, e0, e1);
     if constexpr (D / 2 >= 16) {
-        if (W == D / 2) return run_prefill<T, D, B, D / 2>(p, st, e0, e1);
+        if (W == D / 2) return run_prefill<T, D, B, D / 2>(p, variant, st, e0, e1);
     }
     if constexpr (D / 4 >= 16) {
-        if (W == D / 4) return run_prefill<T, D, B, D / 4>(p, st, e0, e1);
+        if (W == D / 4) return run_prefill<T, D, B, D / 4>(p, variant, st, e0, e1);
     }
     return hipErrorInvalidValue;
 }
 
 template <typename T, int D>
-hipError_t by_block(const PrefillParams& p, int B, int W, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
+hipError_t by_block(const PrefillParams& p, int B, int W, int variant, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
     switch (B) {
-        case 32: return by_width<T, D, 32>(p, W, st, e0, e1);
-        case 64: return by_width<T, D, 64>(p, W, st, e0, e1);
-        case 128: return by_width<T, D, 128>(p, W, st, e0, e1);
+        case 32: return by_width<T, D, 32>(p, W, variant, st, e0, e1);
+        case 64: return by_width<T, D, 64>(p, W, variant, st, e0, e1);
+        case 128: return by_width<T, D, 128>(p, W, variant, st, e0, e1);
         default: return hipErrorInvalidValue;
     }
 }
 
 template <typename T>
-hipError_t dispatch_prefill(const PrefillParams& p, int D, int B, int W, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
+hipError_t dispatch_prefill(const PrefillParams& p, int D, int B, int W, int variant, hipStream_t st, hipEvent_t e0,
+                            hipEvent_t e1) {
     switch (D) {
-        case 16: return by_block<T, 16>(p, B, W, st, e0, e1);
-        case 32: return by_block<T, 32>(p, B, W, st, e0, e1);
-        case 64: return by_block<T, 64>(p, B, W, st, e0, e1);
-        case 128: return by_block<T, 128>(p, B, W, st, e0, e1);
+        case 16: return by_block<T, 16>(p, B, W, variant, st, e0, e1);
+        case 32: return by_block<T, 32>(p, B, W, variant, st, e0, e1);
+        case 64: return by_block<T, 64>(p, B, W, variant, st, e0, e1);
+        case 128: return by_block<T, 128>(p, B, W, variant, st, e0, e1);
         default: return hipErrorInvalidValue;
     }
 }

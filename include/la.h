@@ -124,7 +124,10 @@ typedef struct {
     int32_t seg_len;        /* tokens per segment, a multiple of block; 0 = automatic */
     int32_t value_slices;   /* 1, 2 or 4 value-column slices per head; 0 = automatic */
     int32_t force_scan;     /* 1 = always run the separate prefix-scan kernel */
-    int32_t reserved;
+    int32_t variant;        /* block-loop kernel: 0 = automatic, 1 = the generic loop
+                               (every dtype/d/block), 2 = the transpose-read loop
+                               (bf16, d >= 64, block 64, slices of >= 64 columns);
+                               an unavailable choice returns LA_ERR_UNSUPPORTED */
     void* main_begin_event; /* hipEvent_t recorded on the stream right before the
                                block-loop kernel is launched, or NULL */
     void* main_end_event;   /* hipEvent_t recorded right after it, or NULL */
