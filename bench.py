@@ -36,7 +36,9 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 
-KERNEL_SOURCES = ["la_prefill_kernels.h", "la_device.h", "la_tiles.h", "la_prefill_launch.inl", "la_host.cpp"]
+KERNEL_SOURCES = ["la_prefill_kernels.h", "la_prefill_v2.h", "la_device.h", "la_tiles.h", "la_prefill_launch.inl",
+                  "la_prefill_bf16.hip", "la_host.cpp"]
+MAIN_KERNEL = {1: "la_prefill_main_kernel", 2: "la_prefill_main_v2"}  # by the plan's block-loop variant
 DECODE_SOURCES = ["la_decode_kernels.h", "la_device.h"]
 
 
@@ -199,7 +201,8 @@ def bench_prefill(args, la, torch, hip):
     algo_bytes = T * H * 8 * d * (1 if w["dtype"] == "bf16" else 2)
     achieved = algo_bytes / avg_kernel_s / 1e9
     sha = sources_sha(KERNEL_SOURCES)
-    traffic = load_traffic("la_prefill_main_kernel", name, sha)
+    kname = MAIN_KERNEL[plan["variant"]]
+    traffic = load_traffic(kname, name, sha)
     value = T * H * K / elapsed
     roof_th = HBM_PEAK_GBS * 1e9 / (algo_bytes / (T * H))  # whole step at HBM peak
     rec = {
@@ -219,7 +222,7 @@ def bench_prefill(args, la, torch, hip):
                    "seg_len": plan["seg_len"], "value_slices": plan["value_slices"],
                    "segments": plan["num_segments"], "scan": plan["scan"], "workgroups": plan["units"],
                    "input_sets": nsets},
-        "roofline": {"bound": "hbm", "kernel": "la_prefill_main_kernel", "achieved": achieved,
+        "roofline": {"bound": "hbm", "kernel": kname, "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": traffic, "kernel_ms": avg_kernel_s * 1e3,
                      "algorithmic_bytes": algo_bytes, "kernel_sources_sha": sha},

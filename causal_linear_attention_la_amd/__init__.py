@@ -37,7 +37,8 @@ class la_prefill_opts(ctypes.Structure):
 
 class la_prefill_plan_info(ctypes.Structure):
     _fields_ = [("seg_len", ctypes.c_int32), ("value_slices", ctypes.c_int32), ("num_segments", ctypes.c_int32),
-                ("scan", ctypes.c_int32), ("units", ctypes.c_int64), ("workspace_bytes", ctypes.c_size_t)]
+                ("scan", ctypes.c_int32), ("units", ctypes.c_int64), ("workspace_bytes", ctypes.c_size_t),
+                ("variant", ctypes.c_int32)]
 
 
 _lib = None
@@ -120,7 +121,7 @@ def la_prefill_plan(total_tokens, num_seqs, H, d, block, dtype, opts=None) -> di
     if st != LA_OK:
         raise LAError(st, "la_prefill_plan")
     return dict(seg_len=info.seg_len, value_slices=info.value_slices, num_segments=info.num_segments,
-                scan=info.scan, units=info.units, workspace_bytes=info.workspace_bytes)
+                scan=info.scan, units=info.units, workspace_bytes=info.workspace_bytes, variant=info.variant)
 
 
 # ------------------------------------------------------------ torch layer

@@ -32,6 +32,7 @@ la_status la_prefill_plan(int64_t total_tokens, int32_t num_seqs, int32_t H, int
         out->scan = p.scan;
         out->units = p.units;
         out->workspace_bytes = p.ws_bytes;
+        out->variant = p.variant;
     }
     return LA_OK;
 }
@@ -77,9 +78,8 @@ la_status la_prefill_ex(const void* q, const void* k, const void* v, void* o, co
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipEvent_t e0 = opts ? static_cast<hipEvent_t>(opts->main_begin_event) : nullptr;
     hipEvent_t e1 = opts ? static_cast<hipEvent_t>(opts->main_end_event) : nullptr;
-    const int variant = opts ? opts->variant : 0;
-    hipError_t e = dtype == LA_BF16 ? la::launch_prefill_bf16(p, d, block, plan.W, variant, s, e0, e1)
-                                    : la::launch_prefill_fp32(p, d, block, plan.W, variant, s, e0, e1);
+    hipError_t e = dtype == LA_BF16 ? la::launch_prefill_bf16(p, d, block, plan.W, plan.variant, s, e0, e1)
+                                    : la::launch_prefill_fp32(p, d, block, plan.W, plan.variant, s, e0, e1);
     return e == hipSuccess ? LA_OK : LA_ERR_HIP;
 }
 

@@ -11,7 +11,7 @@ namespace {
 
 constexpr int kNumCUs = 256;      // MI355X compute units
 constexpr int kUnitsTarget = 256; // block-loop workgroups to aim for (one per CU)
-constexpr int kMinSegment = 1024; // shorter segments spend too much on state traffic
+constexpr int kMinSegment = 256;  // shorter segments spend more on state traffic than they gain
 constexpr int kMaxLookback = 16;  // a unit sums at most this many segment states
 
 bool is_pow2_in(int32_t x, int32_t lo, int32_t hi) {
@@ -75,7 +75,7 @@ la_status make_plan(int64_t T, int32_t num_seqs, int32_t H, int32_t d, int32_t b
     }
     p.W = d / p.S;
     if (variant == 2 && !v2_ok(p.S)) return LA_ERR_UNSUPPORTED;
-    p.variant = variant;
+    p.variant = (variant == 0 ? v2_ok(p.S) : variant == 2) ? 2 : 1;  // the loop that will run
 
     if (opts && opts->seg_len != 0) {
         if (opts->seg_len < block || opts->seg_len % block != 0) return LA_ERR_UNSUPPORTED;

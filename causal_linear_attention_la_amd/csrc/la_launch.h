@@ -1,5 +1,6 @@
 // Internal launch entry points (one translation unit per dtype / kernel family).
 #pragma once
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include "la_decode_kernels.h"

@@ -11,6 +11,19 @@ constexpr bool has_v2() {
     return sizeof(T) == 2 && D >= 64 && B == 64 && W >= 64;
 }
 
+// Launches the block-loop kernel; with events, through hipExtLaunchKernel, so
+// that they timestamp the kernel's own start and end.
+inline hipError_t launch_main(void (*kernel)(PrefillParams), dim3 grid, dim3 block, const PrefillParams& p,
+                              hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
+    if (!e0 && !e1) {
+        kernel<<<grid, block, 0, st>>>(p);
+        return hipSuccess;
+    }
+    PrefillParams arg = p;
+    void* args[] = {&arg};
+    return hipExtLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, args, 0, st, e0, e1, 0);
+}
+
 template <typename T, int D, int B, int W>
 hipError_t run_prefill(const PrefillParams& p, int variant, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
     if constexpr (!main_fits((int)sizeof(T), D, B, W)) {
@@ -34,20 +47,12 @@ hipError_t run_prefill(const PrefillParams& p, int variant, hipStream_t st, hipE
                     p.ws, p.flags, p.nseg, entries);
             }
         }
-        if (e0) {
-            hipError_t e = hipEventRecord(e0, st);
-            if (e != hipSuccess) return e;
-        }
+        void (*main_kernel)(PrefillParams) = la_prefill_main_kernel<T, D, B, W>;
         if constexpr (has_v2<T, D, B, W>()) {
-            if (use_v2) v2::la_prefill_main_v2<D, B, W><<<grid, block, 0, st>>>(p);
-            else la_prefill_main_kernel<T, D, B, W><<<grid, block, 0, st>>>(p);
-        } else {
-            la_prefill_main_kernel<T, D, B, W><<<grid, block, 0, st>>>(p);
+            if (use_v2) main_kernel = v2::la_prefill_main_v2<D, B, W>;
         }
-        if (e1) {
-            hipError_t e = hipEventRecord(e1, st);
-            if (e != hipSuccess) return e;
-        }
+        hipError_t e = launch_main(main_kernel, grid, block, p, st, e0, e1);
+        if (e != hipSuccess) return e;
         return hipGetLastError();
     }
 }

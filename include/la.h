@@ -128,9 +128,10 @@ typedef struct {
                                (every dtype/d/block), 2 = the transpose-read loop
                                (bf16, d >= 64, block 64, slices of >= 64 columns);
                                an unavailable choice returns LA_ERR_UNSUPPORTED */
-    void* main_begin_event; /* hipEvent_t recorded on the stream right before the
-                               block-loop kernel is launched, or NULL */
-    void* main_end_event;   /* hipEvent_t recorded right after it, or NULL */
+    void* main_begin_event; /* hipEvent_t stamped when the block-loop kernel starts
+                               executing, or NULL (the kernel is then launched with
+                               hipExtLaunchKernel, which records both events) */
+    void* main_end_event;   /* hipEvent_t stamped when it completes, or NULL */
 } la_prefill_opts;
 
 /* The decomposition a prefill call will use (for reports and tests). */
@@ -141,6 +142,7 @@ typedef struct {
     int32_t scan;          /* 1 if the prefix-scan kernel runs */
     int64_t units;         /* workgroups of the block-loop kernel */
     size_t workspace_bytes;
+    int32_t variant;       /* the block-loop kernel that runs: 1 = generic, 2 = transpose-read */
 } la_prefill_plan_info;
 
 la_status la_prefill_plan(int64_t total_tokens, int32_t num_seqs, int32_t H, int32_t d, int32_t block,

@@ -137,13 +137,17 @@ def test_varlen_tails_and_empty_docs():
             for i, n in enumerate(lens):
                 if n == 0:
                     assert np.all(kv[i] == 0.0)
-    # packed == separate runs
-    o_all, kv_all = run_gpu(q, k, v, cu, 64)
+    # packed == separate runs, bit for bit, when neither is cut into segments
+    # (segment cuts sit at packed-token offsets, so they would fall at
+    # different document offsets in the two runs and change summation order)
+    one = dict(seg_len=1024)
+    assert T <= one["seg_len"]
+    o_all, kv_all = run_gpu(q, k, v, cu, 64, **one)
     for i, n in enumerate(lens):
         if n == 0:
             continue
         a, b = cu[i], cu[i + 1]
-        oi, kvi = run_gpu(q[a:b], k[a:b], v[a:b], np.array([0, n], np.int32), 64)
+        oi, kvi = run_gpu(q[a:b], k[a:b], v[a:b], np.array([0, n], np.int32), 64, **one)
         assert np.array_equal(oi, o_all[a:b]) and np.array_equal(kvi[0], kv_all[i])
 
 
