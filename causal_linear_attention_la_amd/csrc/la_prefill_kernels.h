@@ -86,17 +86,22 @@ struct Cursor {
     int b0;       // first token of the block
     int nb;       // tokens in it (0: no more blocks)
     int doc;
-    int doc_end;  // cu[doc + 1]
-    bool first_of_doc;
+    int doc_end;       // cu[doc + 1]
+    int first_of_doc;  // 1 if the block starts its document (an int: the struct stays all-register)
 };
 
 __device__ __forceinline__ void cursor_first(Cursor& c, const int32_t* cu, int n, int t0, int t1, int B) {
-    if (t0 >= t1) { c.nb = 0; return; }
+    c.b0 = t0;
+    c.nb = 0;
+    c.doc = 0;
+    c.doc_end = 0;
+    c.first_of_doc = 0;
+    if (t0 >= t1) return;
     c.doc = doc_at(cu, n, t0);
     c.doc_end = cu[c.doc + 1];
     c.b0 = t0;
     c.nb = min(B, min(t1, c.doc_end) - t0);
-    c.first_of_doc = (cu[c.doc] == t0);
+    c.first_of_doc = (cu[c.doc] == t0) ? 1 : 0;
 }
 
 __device__ __forceinline__ void cursor_next(Cursor& c, const int32_t* cu, int n, int t1, int B) {
@@ -105,7 +110,7 @@ __device__ __forceinline__ void cursor_next(Cursor& c, const int32_t* cu, int n,
     if (nb0 < piece_end) {
         c.b0 = nb0;
         c.nb = min(B, piece_end - nb0);
-        c.first_of_doc = false;
+        c.first_of_doc = 0;
         return;
     }
     int d = c.doc + 1;
@@ -115,7 +120,7 @@ __device__ __forceinline__ void cursor_next(Cursor& c, const int32_t* cu, int n,
     c.b0 = cu[d];
     c.doc_end = cu[d + 1];
     c.nb = min(B, min(t1, c.doc_end) - c.b0);
-    c.first_of_doc = true;
+    c.first_of_doc = 1;
 }
 
 // Register staging of a ROWS x COLS tile of one head (row stride ld elements):

@@ -4,22 +4,32 @@
 // Same work decomposition and results contract as la_prefill_kernels.h; the
 // block loop is organised for gfx950:
 //  * Q, K, V tiles go from HBM straight into LDS with buffer loads in LDS-DMA
-//    mode (no staging registers), three blocks deep: the loads of block j+2
-//    are issued when block j starts, so two iterations hide each load.  Rows
+//    mode (no staging registers), double buffered: the loads of block j+1
+//    are issued when block j starts, so one iteration hides each load.  Rows
 //    past the end of a partial block lie outside the buffer range and arrive
 //    as zeros.
 //  * Tiles are row-major with 128- or 256-byte rows and no padding; the
 //    8-byte units of row r are permuted by XOR with an even mask, so 16-byte
-//    DMA slots stay whole.  The masks make the two read patterns conflict
-//    free: 16 rows at one column (row fragments) and 8 rows x 4 units
-//    (transpose reads), 32 lanes per LDS cycle.
-//  * Operands that contract over tokens (K^T and V^T fragments) are read with
-//    ds_read_b64_tr_b16, which hands each lane 4 consecutive rows of one
-//    column: one half of the kset fragment used by the MFMA helpers.
+//    DMA slots stay whole.  The masks make every read pattern conflict free
+//    within 16 lanes: 16 rows at one 16-byte chunk (row fragments), and 4
+//    rows x 4 units with unit stride 1 or 2 (transpose reads).
+//  * MFMA fragments here use a contiguous contraction set: within each
+//    32-wide chunk, lane group g = lane / 16 holds indices 8g..8g+7.  A row
+//    fragment (Q, K, P: contraction along the row) is then one 16-byte LDS
+//    read.  Operands that contract over tokens (K^T and V^T fragments) are
+//    read with ds_read_b64_tr_b16, which hands each lane 4 consecutive rows of
+//    one column: two such reads (rows 8g..8g+3 and 8g+4..8g+7) make a fragment.
 //  * Wave w owns value columns [w W/4, (w+1) W/4) of the state for all d
-//    rows.  The fp32 state tiles stay in registers; for the inter product
-//    O^T += KV^T Q^T two vertically adjacent state tiles are, lane for lane,
-//    the A operand of one 32-wide chunk, so the state never goes through LDS.
+//    rows.  The fp32 state tiles stay in registers.  State tile 2m + p holds,
+//    in its accumulator row 4g + r, key dimension 32m + 8g + 4p + r, so the
+//    tile pair (2m, 2m+1) is, lane for lane, the A operand of chunk m of the
+//    inter product O^T += KV^T Q^T: the state never goes through LDS.
+//  * LDS reads are the scarce resource next to the tile DMA (they delay the
+//    DMA's writes into LDS), so the loop reads each operand as few times as
+//    it can: the scores P^T = mask(K Q^T) are computed inside the inter
+//    product's loop, from the same Q fragments, with wave w taking key band
+//    w against every query band (masked tiles come out as the zeros the
+//    intra product needs).
 //  * The intra product of block j (it needs the scores P of block j) runs in
 //    iteration j+1 between its two barriers, where no tile buffer is being
 //    written; its output rows are stored with buffer stores (rows past a
@@ -42,24 +52,39 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kRsrcWord3);
 }
 
+// The waits and the barrier go through builtins (not inline asm), so the
+// compiler's own wait insertion knows what they cover; the empty asm
+// statements keep it from moving memory accesses across them.
+//
 // Workgroup barrier for LDS hand-offs: waits for this wave's outstanding LDS
-// operations, then s_barrier.  Outstanding vector-memory operations are
-// accounted for explicitly with vm_wait.
-__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+// operations (lgkmcnt(0); expcnt and vmcnt at their maximum, i.e. no wait),
+// then s_barrier.  Outstanding vector-memory operations are accounted for
+// explicitly with vm_wait.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
 
 // s_waitcnt vmcnt(N): at most N of this wave's vector-memory operations
 // (loads, LDS-DMA loads, stores; they retire in issue order) stay in flight.
+// gfx9 encoding: vmcnt bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8].
 template <int N>
 __device__ __forceinline__ void vm_wait() {
     static_assert(N >= 0 && N <= 63, "vmcnt range");
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+    asm volatile("" ::: "memory");
 }
 
 // Unit permutation masks (8-byte units, even: 16-byte chunks stay whole).
 template <int PITCH>
 __device__ __forceinline__ int hmask(int r) {
-    if constexpr (PITCH == 128) return 4 * (r & 7) + 2 * ((r >> 3) & 1);   // 256-byte rows
-    else return 4 * ((r >> 1) & 3) + 2 * ((r >> 3) & 1);                   // 128-byte rows: two per 64 banks
+    if constexpr (PITCH == 128)  // 256-byte rows
+        return (8 * (r & 1)) ^ (16 * ((r >> 1) & 1)) ^ (2 * ((r >> 2) & 1)) ^ (4 * ((r >> 3) & 1));
+    else  // 128-byte rows: two per 64 banks (row bit 0 picks the half)
+        return (8 * ((r >> 1) & 1)) ^ (2 * ((r >> 2) & 1)) ^ (4 * ((r >> 3) & 1));
 }
 
 // Element offset of the unit holding logical columns [col, col + 4) of `row`.
@@ -68,27 +93,34 @@ __device__ __forceinline__ int soff(int row, int col) {
     return row * PITCH + ((((col >> 2) ^ hmask<PITCH>(row))) << 2);
 }
 
-// kset fragment of a row: lane (row, g) receives T[row][k0 + kset(g)].
+// Row fragment: lane (row, g) receives T[row][k0 + 8g .. k0 + 8g + 7], one
+// 16-byte read (the even unit masks keep 16-byte chunks whole and aligned).
 template <int PITCH>
-__device__ __forceinline__ void load_frag_sw(Frag<bf16_t>& f, const bf16_t* tile, int row, int k0, int g) {
-    f.lo = *reinterpret_cast<const uint2*>(tile + soff<PITCH>(row, k0 + 4 * g));
-    f.hi = *reinterpret_cast<const uint2*>(tile + soff<PITCH>(row, k0 + 16 + 4 * g));
+__device__ __forceinline__ void load_row(Frag<bf16_t>& f, const bf16_t* tile, int row, int k0, int g) {
+    const uint4 v = *reinterpret_cast<const uint4*>(tile + soff<PITCH>(row, k0 + 8 * g));
+    f.lo = make_uint2(v.x, v.y);
+    f.hi = make_uint2(v.z, v.w);
 }
 
-// kset fragment of a column: lane (s = lane % 16, g) receives
-// T[t0 + kset(g)][n0 + s] (rows t0 + 4g..+3 and t0 + 16 + 4g..+3), through
-// ds_read_b64_tr_b16: within each 16-lane group, lane s names row
-// (first + s / 4) at columns n0 + 4 (s % 4)..+3 and receives column n0 + s
-// of those 4 rows.
-template <int PITCH>
-__device__ __forceinline__ void load_frag_tr(Frag<bf16_t>& f, const bf16_t* tile, int t0, int n0, int lane) {
+// Column fragment over tokens: lane (s = lane % 16, g) receives
+// T[t0 + 8g .. t0 + 8g + 7][col(s)] through two ds_read_b64_tr_b16.  Within
+// each 16-lane group, lane s names row (first + s / 4) and the 4-column unit
+// starting at n0 + STRIDE (s % 4) + off, and receives element s % 4 of the
+// unit named by lane 4i + s / 4 for rows first + i.  So
+//   STRIDE 4, off 0: col(s) = n0 + s                          (16 columns)
+//   STRIDE 8, off 4p: col(s) = n0 + 8 (s / 4) + 4p + s % 4    (a state tile's key dims)
+template <int PITCH, int STRIDE>
+__device__ __forceinline__ void load_tr(Frag<bf16_t>& f, const bf16_t* tile, int t0, int n0, int off, int lane) {
     const int s = lane & 15, g = lane >> 4;
-    const int r = t0 + 4 * g + (s >> 2), c = n0 + 4 * (s & 3);
+    const int r = t0 + 8 * g + (s >> 2), c = n0 + STRIDE * (s & 3) + off;
     s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(tile + soff<PITCH>(r, c)));
-    s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(tile + soff<PITCH>(r + 16, c)));
+    s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(tile + soff<PITCH>(r + 4, c)));
     f.lo = __builtin_bit_cast(uint2, lo);
     f.hi = __builtin_bit_cast(uint2, hi);
 }
+
+// Key dimension held by accumulator row 4g + r of state tile a.
+__device__ __forceinline__ int state_row(int a, int g, int r) { return 32 * (a >> 1) + 8 * g + 4 * (a & 1) + r; }
 
 __device__ __forceinline__ uint32_t pack2(float a, float b) { return pack_bf16x2(a, b); }
 
@@ -122,6 +154,11 @@ struct DmaTile {
     }
 };
 
+template <int N>
+struct Slot {
+    static constexpr int value = N;
+};
+
 template <int D, int B, int W>
 struct Geo {
     static constexpr int NQT = B / 16;
@@ -146,11 +183,11 @@ __device__ __forceinline__ void state_update(f32x4_t (&kv)[NA][NC], Frag<bf16_t>
 #pragma unroll
     for (int kc = 0; kc < B / 32; ++kc) {
 #pragma unroll
-        for (int c = 0; c < G::NCW; ++c) load_frag_tr<W>(vfr[c][kc], Vs, 32 * kc, col0 + 16 * c, lane);
+        for (int c = 0; c < G::NCW; ++c) load_tr<W, 4>(vfr[c][kc], Vs, 32 * kc, col0 + 16 * c, 0, lane);
 #pragma unroll
         for (int a = 0; a < G::NDT; ++a) {
             Frag<bf16_t> kf;
-            load_frag_tr<D>(kf, Ks, 32 * kc, 16 * a, lane);
+            load_tr<D, 8>(kf, Ks, 32 * kc, 32 * (a >> 1), 4 * (a & 1), lane);
 #pragma unroll
             for (int c = 0; c < G::NCW; ++c) mma(kv[a][c], kf, vfr[c][kc]);
         }
@@ -166,7 +203,7 @@ __device__ __forceinline__ void load_prefix(f32x4_t (&kv)[NA][NC], const float* 
 #pragma unroll
         for (int c = 0; c < G::NCW; ++c)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) kv[a][c][r] += src[(int64_t)(16 * a + 4 * g + r) * D + 16 * c + li];
+            for (int r = 0; r < 4; ++r) kv[a][c][r] += src[(int64_t)state_row(a, g, r) * D + 16 * c + li];
 }
 
 template <int D, int B, int W, int NA, int NC>
@@ -178,7 +215,7 @@ __device__ __forceinline__ void store_state(const f32x4_t (&kv)[NA][NC], float* 
 #pragma unroll
         for (int c = 0; c < G::NCW; ++c)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) dst[(int64_t)(16 * a + 4 * g + r) * D + 16 * c + li] = kv[a][c][r];
+            for (int r = 0; r < 4; ++r) dst[(int64_t)state_row(a, g, r) * D + 16 * c + li] = kv[a][c][r];
 }
 
 // ---------------------------------------------------------------------------
@@ -187,10 +224,11 @@ __device__ __forceinline__ void store_state(const f32x4_t (&kv)[NA][NC], float* 
 template <int D, int B, int W>
 __global__ __launch_bounds__(kThreads, 1) void la_segment_state_v2(PrefillParams p) {
     using G = Geo<D, B, W>;
-    constexpr int NBUF = 3;
-    constexpr int LOADS = DmaTile<D>::NI + DmaTile<W>::NI;
-    __shared__ __align__(16) bf16_t Kb[NBUF][B * D];
-    __shared__ __align__(16) bf16_t Vb[NBUF][B * W];
+    // two tile slots, one LDS variable each (see the block loop below)
+    __shared__ __align__(16) bf16_t Kb0[B * D], Kb1[B * D];
+    __shared__ __align__(16) bf16_t Vb0[B * W], Vb1[B * W];
+    auto kbuf = [&](auto slot) -> bf16_t* { if constexpr (decltype(slot)::value == 0) return Kb0; else return Kb1; };
+    auto vbuf = [&](auto slot) -> bf16_t* { if constexpr (decltype(slot)::value == 0) return Vb0; else return Vb1; };
     int u, h, s;
     if (!unit_of(p, u, h, s)) return;
     if (u >= p.nseg - 1) return;
@@ -221,19 +259,27 @@ __global__ __launch_bounds__(kThreads, 1) void la_segment_state_v2(PrefillParams
 
     const int first = max(t_beg, dstart);
     const int nblk = (t_end - first + B - 1) / B;
-    auto issue = [&](int j) {
-        const int b0 = first + j * B, nb = min(B, t_end - b0);
-        const int64_t e0 = ((int64_t)b0 * p.H + h) * D;
-        dk.issue(make_rsrc(kg + e0, (uint32_t)nb * row_bytes), Kb[j % NBUF]);
-        dv.issue(make_rsrc(vg + e0 + s * W, (uint32_t)nb * row_bytes), Vb[j % NBUF]);
+    // blocks past the last one are issued with an empty range (no reads)
+    auto issue = [&](int j, auto slot) {
+        const int b0 = first + j * B, nb = max(0, min(B, t_end - b0));
+        const int64_t e0 = ((int64_t)min(b0, t_end) * p.H + h) * D;
+        dk.issue(make_rsrc(kg + e0, (uint32_t)nb * row_bytes), kbuf(slot));
+        dv.issue(make_rsrc(vg + e0 + s * W, (uint32_t)nb * row_bytes), vbuf(slot));
     };
-    issue(0);
-    if (nblk > 1) issue(1);
-    for (int j = 0; j < nblk; ++j) {
-        if (j + 1 < nblk) vm_wait<LOADS>(); else vm_wait<0>();
+    int j = 0;
+    auto step = [&](auto slot) {
+        constexpr int SLOT = decltype(slot)::value;
+        vm_wait<0>();
         lds_barrier();  // block j in LDS; block j-1 no longer read
-        if (j + 2 < nblk) issue(j + 2);
-        state_update<D, B, W>(kv, vfr, Kb[j % NBUF], Vb[j % NBUF], col0, lane);
+        issue(j + 1, Slot<1 - SLOT>{});
+        state_update<D, B, W>(kv, vfr, kbuf(slot), vbuf(slot), col0, lane);
+        ++j;
+    };
+    issue(0, Slot<0>{});
+    while (j < nblk) {
+        step(Slot<0>{});
+        if (j >= nblk) break;
+        step(Slot<1>{});
     }
     store_state<D, B, W>(kv, p.ws + (((int64_t)u * p.H + h) * D) * D + s * W + col0, g, li);
 }
@@ -244,13 +290,19 @@ template <int D, int B, int W>
 __global__ __launch_bounds__(kThreads, 1) void la_prefill_main_v2(PrefillParams p) {
     using G = Geo<D, B, W>;
     constexpr int NQT = G::NQT, NCW = G::NCW, NDT = G::NDT;
-    constexpr int NTRI = NQT * (NQT + 1) / 2, NZT = NQT / 2;
-    constexpr int NBUF = 3;
+    static_assert(NQT == kWaves, "wave w takes key band w");
     constexpr int PP = B;  // P[query][key] rows: 128 bytes
-    __shared__ __align__(16) bf16_t Qb[NBUF][B * D];
-    __shared__ __align__(16) bf16_t Kb[NBUF][B * D];
-    __shared__ __align__(16) bf16_t Vb[NBUF][B * W];
+    // Two tile slots, each tile its own LDS variable: with the loop unrolled
+    // by two, every LDS access names its slot at compile time, so the
+    // compiler sees that reads of one slot do not alias the DMA writes in
+    // flight to the other and adds no waits of its own.
+    __shared__ __align__(16) bf16_t Qb0[B * D], Qb1[B * D];
+    __shared__ __align__(16) bf16_t Kb0[B * D], Kb1[B * D];
+    __shared__ __align__(16) bf16_t Vb0[B * W], Vb1[B * W];
     __shared__ __align__(16) bf16_t Ps[B * PP];
+    auto qbuf = [&](auto slot) -> bf16_t* { if constexpr (decltype(slot)::value == 0) return Qb0; else return Qb1; };
+    auto kbuf = [&](auto slot) -> bf16_t* { if constexpr (decltype(slot)::value == 0) return Kb0; else return Kb1; };
+    auto vbuf = [&](auto slot) -> bf16_t* { if constexpr (decltype(slot)::value == 0) return Vb0; else return Vb1; };
 
     int u, h, s;
     if (!unit_of(p, u, h, s)) return;
@@ -289,12 +341,16 @@ __global__ __launch_bounds__(kThreads, 1) void la_prefill_main_v2(PrefillParams 
         for (int c = 0; c < NCW; ++c) oacc[b][c] = zero4();
     Frag<bf16_t> vfr[NCW][B / 32];
 
-    auto issue = [&](const Cursor& c, int buf) {
+    // A cursor past the end (nb = 0) still issues its loads, with an empty
+    // buffer range: nothing is read, zeros land in the unused slot, and every
+    // path through the loop issues the same vector-memory operations (the
+    // compiler's wait bookkeeping then stays exact instead of conservative).
+    auto issue = [&](const Cursor& c, auto slot) {
         const int64_t e0 = ((int64_t)c.b0 * p.H + h) * D;
-        const uint32_t bytes = (uint32_t)c.nb * row_bytes;
-        dq.issue(make_rsrc(qg + e0, bytes), Qb[buf]);
-        dq.issue(make_rsrc(kg + e0, bytes), Kb[buf]);
-        dv.issue(make_rsrc(vg + e0 + s * W, bytes), Vb[buf]);
+        const uint32_t bytes = (uint32_t)max(c.nb, 0) * row_bytes;
+        dq.issue(make_rsrc(qg + e0, bytes), qbuf(slot));
+        dq.issue(make_rsrc(kg + e0, bytes), kbuf(slot));
+        dv.issue(make_rsrc(vg + e0 + s * W, bytes), vbuf(slot));
     };
     // O^T += V^T P^T for the previous block, then its rows are stored.
     auto finish = [&](int pb0, int pnb) {
@@ -303,7 +359,7 @@ __global__ __launch_bounds__(kThreads, 1) void la_prefill_main_v2(PrefillParams 
 #pragma unroll
             for (int kc = 0; kc <= b / 2; ++kc) {
                 Frag<bf16_t> pf;
-                load_frag_sw<PP>(pf, Ps, 16 * b + li, 32 * kc, g);
+                load_row<PP>(pf, Ps, 16 * b + li, 32 * kc, g);
 #pragma unroll
                 for (int c = 0; c < NCW; ++c) mma(oacc[b][c], vfr[c][kc], pf);
             }
@@ -322,34 +378,34 @@ __global__ __launch_bounds__(kThreads, 1) void la_prefill_main_v2(PrefillParams 
             }
     };
 
-    Cursor c1 = c0;
-    if (c1.nb > 0) cursor_next(c1, p.cu, p.num_seqs, t1, B);
-    if (c0.nb > 0) issue(c0, 0);
-    if (c1.nb > 0) issue(c1, 1);
-    int pb0 = 0, pnb = 0;
-    bool have_prev = false;
+    if (c0.nb > 0) issue(c0, Slot<0>{});
+    int pb0 = t0, pnb = 0;
     int j = 0;
-    while (c0.nb > 0) {
-        Cursor c2 = c1;
-        if (c2.nb > 0) cursor_next(c2, p.cu, p.num_seqs, t1, B);
-        // Loads of block j are done once at most the younger operations are
-        // in flight: loads of block j+1 and the stores of block j-2 (the
-        // stores of block j-3 sit between them and are waited for too).
-        if (c1.nb > 0) {
-            if (j >= 2) vm_wait<G::LOADS + G::STORES>();
-            else vm_wait<G::LOADS>();
-        } else {
-            vm_wait<0>();
-        }
+    // One block; its tiles sit in slot SLOT, the next block's go to the other.
+    auto step = [&](auto slot) {
+        constexpr int SLOT = decltype(slot)::value;
+        Cursor c1 = c0;
+        cursor_next(c1, p.cu, p.num_seqs, t1, B);
+        // Loads of block j (issued one iteration ago) are done once at most
+        // the younger operations are in flight: the stores of block j-2.
+        if (j >= 1) vm_wait<G::STORES>();
+        else vm_wait<0>();
         lds_barrier();  // (A) block j visible; block j-1's tiles no longer read
-        if (c2.nb > 0) issue(c2, (j + 2) % NBUF);
-        if (have_prev) finish(pb0, pnb);
+        issue(c1, Slot<1 - SLOT>{});
+        // block j-1's output; in the first iteration pnb = 0 and the stores
+        // (of whatever the accumulators hold) fall outside the buffer range
+        finish(pb0, pnb);
         lds_barrier();  // (B) scores of block j-1 consumed
 
-        const bf16_t* Qs = Qb[j % NBUF];
-        const bf16_t* Ks = Kb[j % NBUF];
-        const bf16_t* Vs = Vb[j % NBUF];
-        // inter: O^T += KV^T Q^T with the state before this block
+        const bf16_t* Qs = qbuf(slot);
+        const bf16_t* Ks = kbuf(slot);
+        const bf16_t* Vs = vbuf(slot);
+        // inter: O^T += KV^T Q^T with the state before this block, and the
+        // scores S^T = K_w Q^T of key band w (= this wave) against every
+        // query band, from the same Q fragments
+        f32x4_t sacc[NQT];
+#pragma unroll
+        for (int b = 0; b < NQT; ++b) sacc[b] = zero4();
 #pragma unroll
         for (int m = 0; m < D / 32; ++m) {
             Frag<bf16_t> kvf[NCW];
@@ -359,50 +415,32 @@ __global__ __launch_bounds__(kThreads, 1) void la_prefill_main_v2(PrefillParams 
                 kvf[c].hi = make_uint2(pack2(kv[2 * m + 1][c][0], kv[2 * m + 1][c][1]),
                                        pack2(kv[2 * m + 1][c][2], kv[2 * m + 1][c][3]));
             }
+            Frag<bf16_t> kf;
+            load_row<D>(kf, Ks, 16 * wave + li, 32 * m, g);
 #pragma unroll
             for (int b = 0; b < NQT; ++b) {
                 Frag<bf16_t> qf;
-                load_frag_sw<D>(qf, Qs, 16 * b + li, 32 * m, g);
+                load_row<D>(qf, Qs, 16 * b + li, 32 * m, g);
 #pragma unroll
                 for (int c = 0; c < NCW; ++c) mma(oacc[b][c], kvf[c], qf);
+                mma(sacc[b], kf, qf);
             }
         }
         // state: KV += K^T V (after the inter product read it)
         state_update<D, B, W>(kv, vfr, Ks, Vs, col0, lane);
 
-        // scores, transposed, lower-triangular tiles; P[query][key] to LDS
-        for (int t = wave; t < NTRI + NZT; t += kWaves) {
-            int a, b;
-            if (t < NTRI) {
-                b = 0;
-                while ((b + 1) * (b + 2) / 2 <= t) ++b;
-                a = t - b * (b + 1) / 2;
-            } else {
-                b = 2 * (t - NTRI);
-                a = b + 1;
-            }
-            bf16_t* prow = Ps + soff<PP>(16 * b + li, 16 * a + 4 * g);
-            if (t >= NTRI) {
-                store4_zero(prow);
-                continue;
-            }
-            f32x4_t acc = zero4();
+        // P[query][key] for keys of band w: causal mask (key <= query), the
+        // tiles above the diagonal come out as zeros
 #pragma unroll
-            for (int m = 0; m < D / 32; ++m) {
-                Frag<bf16_t> fa, fb;
-                load_frag_sw<D>(fa, Ks, 16 * a + li, 32 * m, g);
-                load_frag_sw<D>(fb, Qs, 16 * b + li, 32 * m, g);
-                mma(acc, fa, fb);
-            }
-            if (a == b) {
+        for (int b = 0; b < NQT; ++b) {
 #pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    if (4 * g + r > li) acc[r] = 0.f;
-            }
-            store4(prow, acc[0], acc[1], acc[2], acc[3]);
+            for (int r = 0; r < 4; ++r)
+                if (16 * wave + 4 * g + r > 16 * b + li) sacc[b][r] = 0.f;
+            store4(Ps + soff<PP>(16 * b + li, 16 * wave + 4 * g), sacc[b][0], sacc[b][1], sacc[b][2], sacc[b][3]);
         }
 
         if (c0.b0 + c0.nb == c0.doc_end) {  // the document ends with this block
+            vm_wait<0>();  // rare path: keeps the loop's wait bookkeeping exact
             if (p.kv_out)
                 store_state<D, B, W>(kv, p.kv_out + (((int64_t)c0.doc * p.H + h) * D) * D + s * W + col0, g, li);
 #pragma unroll
@@ -412,12 +450,15 @@ __global__ __launch_bounds__(kThreads, 1) void la_prefill_main_v2(PrefillParams 
         }
         pb0 = c0.b0;
         pnb = c0.nb;
-        have_prev = true;
         c0 = c1;
-        c1 = c2;
         ++j;
+    };
+    while (c0.nb > 0) {
+        step(Slot<0>{});
+        if (c0.nb <= 0) break;
+        step(Slot<1>{});
     }
-    if (have_prev) {
+    if (j > 0) {
         lds_barrier();  // scores of the last block visible
         finish(pb0, pnb);
     }
