@@ -345,12 +345,21 @@ __global__ __launch_bounds__(kThreads, 1) void la_prefill_main_v2(PrefillParams 
     // buffer range: nothing is read, zeros land in the unused slot, and every
     // path through the loop issues the same vector-memory operations (the
     // compiler's wait bookkeeping then stays exact instead of conservative).
-    auto issue = [&](const Cursor& c, auto slot) {
+    // The three tiles of a block (TILE 0 = Q, 1 = K, 2 = V) can be issued at
+    // different points of an iteration, so the address unit works through
+    // them while the wave computes instead of stalling every wave at once.
+    auto issue_tile = [&](const Cursor& c, auto slot, auto tile) {
+        constexpr int TILE = decltype(tile)::value;
         const int64_t e0 = ((int64_t)c.b0 * p.H + h) * D;
         const uint32_t bytes = (uint32_t)max(c.nb, 0) * row_bytes;
-        dq.issue(make_rsrc(qg + e0, bytes), qbuf(slot));
-        dq.issue(make_rsrc(kg + e0, bytes), kbuf(slot));
-        dv.issue(make_rsrc(vg + e0 + s * W, bytes), vbuf(slot));
+        if constexpr (TILE == 0) dq.issue(make_rsrc(qg + e0, bytes), qbuf(slot));
+        else if constexpr (TILE == 1) dq.issue(make_rsrc(kg + e0, bytes), kbuf(slot));
+        else dv.issue(make_rsrc(vg + e0 + s * W, bytes), vbuf(slot));
+    };
+    auto issue = [&](const Cursor& c, auto slot) {
+        issue_tile(c, slot, Slot<0>{});
+        issue_tile(c, slot, Slot<1>{});
+        issue_tile(c, slot, Slot<2>{});
     };
     // O^T += V^T P^T for the previous block, then its rows are stored.
     auto finish = [&](int pb0, int pnb) {
@@ -386,15 +395,15 @@ __global__ __launch_bounds__(kThreads, 1) void la_prefill_main_v2(PrefillParams 
         constexpr int SLOT = decltype(slot)::value;
         Cursor c1 = c0;
         cursor_next(c1, p.cu, p.num_seqs, t1, B);
-        // Loads of block j (issued one iteration ago) are done once at most
-        // the younger operations are in flight: the stores of block j-2.
-        if (j >= 1) vm_wait<G::STORES>();
-        else vm_wait<0>();
+        // Loads of block j (issued during the previous iteration, the last
+        // tile after its stores) are all done: nothing younger is in flight.
+        vm_wait<0>();
         lds_barrier();  // (A) block j visible; block j-1's tiles no longer read
-        issue(c1, Slot<1 - SLOT>{});
+        issue_tile(c1, Slot<1 - SLOT>{}, Slot<0>{});
         // block j-1's output; in the first iteration pnb = 0 and the stores
         // (of whatever the accumulators hold) fall outside the buffer range
         finish(pb0, pnb);
+        issue_tile(c1, Slot<1 - SLOT>{}, Slot<1>{});
         lds_barrier();  // (B) scores of block j-1 consumed
 
         const bf16_t* Qs = qbuf(slot);
@@ -426,6 +435,7 @@ __global__ __launch_bounds__(kThreads, 1) void la_prefill_main_v2(PrefillParams 
                 mma(sacc[b], kf, qf);
             }
         }
+        issue_tile(c1, Slot<1 - SLOT>{}, Slot<2>{});
         // state: KV += K^T V (after the inter product read it)
         state_update<D, B, W>(kv, vfr, Ks, Vs, col0, lane);
 
