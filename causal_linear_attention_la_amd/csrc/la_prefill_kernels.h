@@ -269,20 +269,31 @@ __global__ __launch_bounds__(kThreads, 2) void la_segment_state_kernel(PrefillPa
 // ---------------------------------------------------------------------------
 // Per-document inclusive scan of the segment states, in place: afterwards
 // ws[u] is the state of segment u's last document at the end of segment u.
-// One thread per state entry (h, i, j); the loop over segments is sequential.
-template <int UNROLL>
-__global__ __launch_bounds__(kThreads) void la_segment_scan_kernel(float* ws, const int32_t* flags, int nseg,
+// One thread per 4 consecutive state entries (h, i, j..j+3); the segments are
+// taken CH at a time: CH independent 16-byte loads in flight, then the
+// running sums and CH stores.
+template <int CH>
+__global__ __launch_bounds__(kThreads) void la_segment_scan_kernel(float* __restrict__ ws,
+                                                                   const int32_t* __restrict__ flags, int nseg,
                                                                    int64_t entries) {
-    const int64_t idx = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    const int64_t idx = ((int64_t)blockIdx.x * kThreads + threadIdx.x) * 4;
     if (idx >= entries) return;
-    float carry = 0.f;
-#pragma unroll UNROLL
-    for (int u = 0; u < nseg - 1; ++u) {
-        const int f = flags[u];
-        if (f & 1) {
-            const float a = ws[(int64_t)u * entries + idx];
-            carry = (f & 2) ? carry + a : a;
-            ws[(int64_t)u * entries + idx] = carry;
+    f32x4_t carry = zero4();
+    for (int u0 = 0; u0 < nseg - 1; u0 += CH) {
+        f32x4_t a[CH];
+        int f[CH];
+#pragma unroll
+        for (int c = 0; c < CH; ++c) {
+            const int u = u0 + c;
+            f[c] = u < nseg - 1 ? flags[u] : 0;
+            a[c] = (f[c] & 1) ? *reinterpret_cast<const f32x4_t*>(ws + (int64_t)u * entries + idx) : zero4();
+        }
+#pragma unroll
+        for (int c = 0; c < CH; ++c) {
+            if (f[c] & 1) {
+                carry = (f[c] & 2) ? carry + a[c] : a[c];
+                *reinterpret_cast<f32x4_t*>(ws + (int64_t)(u0 + c) * entries + idx) = carry;
+            }
         }
     }
 }

@@ -42,8 +42,9 @@ hipError_t run_prefill(const PrefillParams& p, int variant, hipStream_t st, hipE
                 la_segment_state_kernel<T, D, B, W><<<grid, block, 0, st>>>(p);
             }
             if (p.scan) {
-                const int64_t entries = (int64_t)p.H * D * D;
-                la_segment_scan_kernel<8><<<dim3((unsigned)((entries + kThreads - 1) / kThreads)), block, 0, st>>>(
+                const int64_t entries = (int64_t)p.H * D * D;  // a multiple of 4
+                const int64_t threads = entries / 4;
+                la_segment_scan_kernel<16><<<dim3((unsigned)((threads + kThreads - 1) / kThreads)), block, 0, st>>>(
                     p.ws, p.flags, p.nseg, entries);
             }
         }

@@ -41,6 +41,7 @@ namespace la {
 namespace v2 {
 
 typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 typedef __attribute__((address_space(3))) void lds_void_t;
@@ -122,6 +123,16 @@ __device__ __forceinline__ void load_tr(Frag<bf16_t>& f, const bf16_t* tile, int
 // Key dimension held by accumulator row 4g + r of state tile a.
 __device__ __forceinline__ int state_row(int a, int g, int r) { return 32 * (a >> 1) + 8 * g + 4 * (a & 1) + r; }
 
+// Value column (relative to the wave's first column) held by lane column s of
+// state tile c.  A wave with two tile columns interleaves them in runs of 4,
+// so that lane group g of the output accumulators of tiles 0 and 1 holds 8
+// consecutive columns 8g..8g+7: one 16-byte store per row.
+template <int NCW>
+__device__ __forceinline__ int state_col(int c, int s) {
+    if constexpr (NCW == 2) return 8 * (s >> 2) + 4 * c + (s & 3);
+    else return 16 * c + s;
+}
+
 __device__ __forceinline__ uint32_t pack2(float a, float b) { return pack_bf16x2(a, b); }
 
 // A 64 x COLS bf16 tile moved HBM -> LDS by LDS-DMA buffer loads.  Wave w
@@ -166,7 +177,7 @@ struct Geo {
     static constexpr int CW = W / 4;   // value columns per wave
     static constexpr int NCW = CW / 16;
     static constexpr int LOADS = DmaTile<D>::NI * 2 + DmaTile<W>::NI;  // VMEM loads per wave and block
-    static constexpr int STORES = NQT * NCW;                          // VMEM stores per wave and block
+    static constexpr int STORES = NCW == 2 ? NQT : NQT * NCW;         // VMEM stores per wave and block
     static_assert(B == 64, "one 16-row band per wave");
     static_assert(CW % 16 == 0, "each wave owns whole 16-column tiles");
     static_assert(D == 64 || D == 128, "row widths");
@@ -183,7 +194,10 @@ __device__ __forceinline__ void state_update(f32x4_t (&kv)[NA][NC], Frag<bf16_t>
 #pragma unroll
     for (int kc = 0; kc < B / 32; ++kc) {
 #pragma unroll
-        for (int c = 0; c < G::NCW; ++c) load_tr<W, 4>(vfr[c][kc], Vs, 32 * kc, col0 + 16 * c, 0, lane);
+        for (int c = 0; c < G::NCW; ++c) {
+            if constexpr (G::NCW == 2) load_tr<W, 8>(vfr[c][kc], Vs, 32 * kc, col0, 4 * c, lane);
+            else load_tr<W, 4>(vfr[c][kc], Vs, 32 * kc, col0 + 16 * c, 0, lane);
+        }
 #pragma unroll
         for (int a = 0; a < G::NDT; ++a) {
             Frag<bf16_t> kf;
@@ -203,7 +217,7 @@ __device__ __forceinline__ void load_prefix(f32x4_t (&kv)[NA][NC], const float* 
 #pragma unroll
         for (int c = 0; c < G::NCW; ++c)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) kv[a][c][r] += src[(int64_t)state_row(a, g, r) * D + 16 * c + li];
+            for (int r = 0; r < 4; ++r) kv[a][c][r] += src[(int64_t)state_row(a, g, r) * D + state_col<NC>(c, li)];
 }
 
 template <int D, int B, int W, int NA, int NC>
@@ -215,7 +229,7 @@ __device__ __forceinline__ void store_state(const f32x4_t (&kv)[NA][NC], float* 
 #pragma unroll
         for (int c = 0; c < G::NCW; ++c)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) dst[(int64_t)state_row(a, g, r) * D + 16 * c + li] = kv[a][c][r];
+            for (int r = 0; r < 4; ++r) dst[(int64_t)state_row(a, g, r) * D + state_col<NC>(c, li)] = kv[a][c][r];
 }
 
 // ---------------------------------------------------------------------------
@@ -224,9 +238,10 @@ __device__ __forceinline__ void store_state(const f32x4_t (&kv)[NA][NC], float* 
 template <int D, int B, int W>
 __global__ __launch_bounds__(kThreads, 1) void la_segment_state_v2(PrefillParams p) {
     using G = Geo<D, B, W>;
-    // two tile slots, one LDS variable each (see the block loop below)
-    __shared__ __align__(16) bf16_t Kb0[B * D], Kb1[B * D];
-    __shared__ __align__(16) bf16_t Vb0[B * W], Vb1[B * W];
+    // Two slots of two blocks each, one LDS variable per tile; the loads of
+    // blocks 2i+2, 2i+3 are issued when blocks 2i, 2i+1 start.
+    __shared__ __align__(16) bf16_t Kb0[2 * B * D], Kb1[2 * B * D];
+    __shared__ __align__(16) bf16_t Vb0[2 * B * W], Vb1[2 * B * W];
     auto kbuf = [&](auto slot) -> bf16_t* { if constexpr (decltype(slot)::value == 0) return Kb0; else return Kb1; };
     auto vbuf = [&](auto slot) -> bf16_t* { if constexpr (decltype(slot)::value == 0) return Vb0; else return Vb1; };
     int u, h, s;
@@ -235,9 +250,12 @@ __global__ __launch_bounds__(kThreads, 1) void la_segment_state_v2(PrefillParams
     const int tid = threadIdx.x, lane = tid & 63, li = lane & 15, g = lane >> 4;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int t_beg = u * p.L, t_end = (u + 1) * p.L;
-    const int de = doc_at(p.cu, p.num_seqs, t_end - 1);
-    const int dstart = p.cu[de];
-    const bool needs = p.cu[de + 1] > t_end;
+    // values loaded from cu are the same in every lane: readfirstlane makes
+    // that visible to the compiler, which then keeps the buffer descriptors
+    // built from them in scalar registers (no per-lane waterfall loops)
+    const int de = __builtin_amdgcn_readfirstlane(doc_at(p.cu, p.num_seqs, t_end - 1));
+    const int dstart = __builtin_amdgcn_readfirstlane(p.cu[de]);
+    const bool needs = __builtin_amdgcn_readfirstlane(p.cu[de + 1]) > t_end;
     const bool chain = dstart < t_beg;
     if (h == 0 && s == 0 && tid == 0) p.flags[u] = (needs ? 1 : 0) | (chain ? 2 : 0);
     if (!needs) return;
@@ -259,27 +277,38 @@ __global__ __launch_bounds__(kThreads, 1) void la_segment_state_v2(PrefillParams
 
     const int first = max(t_beg, dstart);
     const int nblk = (t_end - first + B - 1) / B;
-    // blocks past the last one are issued with an empty range (no reads)
-    auto issue = [&](int j, auto slot) {
-        const int b0 = first + j * B, nb = max(0, min(B, t_end - b0));
-        const int64_t e0 = ((int64_t)min(b0, t_end) * p.H + h) * D;
-        dk.issue(make_rsrc(kg + e0, (uint32_t)nb * row_bytes), kbuf(slot));
-        dv.issue(make_rsrc(vg + e0 + s * W, (uint32_t)nb * row_bytes), vbuf(slot));
+    // Pair jj = blocks 2jj and 2jj+1.  Blocks past the last one are issued
+    // with an empty range: nothing is read, their rows arrive as zeros and
+    // add nothing to the state.
+    auto issue = [&](int jj, auto slot) {
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            const int b0 = first + (2 * jj + half) * B;
+            // (clamp kept scalar: the descriptor built from it must live in
+            // scalar registers)
+            const int nb = __builtin_amdgcn_readfirstlane(max(0, min(B, t_end - b0)));
+            const int64_t e0 = ((int64_t)min(b0, t_end) * p.H + h) * D;
+            dk.issue(make_rsrc(kg + e0, (uint32_t)nb * row_bytes), kbuf(slot) + half * B * D);
+            dv.issue(make_rsrc(vg + e0 + s * W, (uint32_t)nb * row_bytes), vbuf(slot) + half * B * W);
+        }
     };
-    int j = 0;
+    const int npairs = (nblk + 1) / 2;
+    int jj = 0;
     auto step = [&](auto slot) {
         constexpr int SLOT = decltype(slot)::value;
-        vm_wait<0>();
-        lds_barrier();  // block j in LDS; block j-1 no longer read
-        issue(j + 1, Slot<1 - SLOT>{});
+        vm_wait<0>();   // pair jj in (issued one step ago, nothing younger)
+        lds_barrier();  // pair jj visible; pair jj-1 no longer read
+        issue(jj + 1, Slot<1 - SLOT>{});
         state_update<D, B, W>(kv, vfr, kbuf(slot), vbuf(slot), col0, lane);
-        ++j;
+        state_update<D, B, W>(kv, vfr, kbuf(slot) + B * D, vbuf(slot) + B * W, col0, lane);
+        ++jj;
     };
     issue(0, Slot<0>{});
-    while (j < nblk) {
+    while (true) {
         step(Slot<0>{});
-        if (j >= nblk) break;
+        if (jj >= npairs) break;
         step(Slot<1>{});
+        if (jj >= npairs) break;
     }
     store_state<D, B, W>(kv, p.ws + (((int64_t)u * p.H + h) * D) * D + s * W + col0, g, li);
 }
@@ -329,11 +358,6 @@ __global__ __launch_bounds__(kThreads, 1) void la_prefill_main_v2(PrefillParams 
     for (int a = 0; a < NDT; ++a)
 #pragma unroll
         for (int c = 0; c < NCW; ++c) kv[a][c] = zero4();
-    if (c0.nb > 0 && !c0.first_of_doc) {
-        const int u_first = p.scan ? u - 1 : p.cu[c0.doc] / p.L;
-        for (int uu = u_first; uu < u; ++uu)
-            load_prefix<D, B, W>(kv, p.ws + (((int64_t)uu * p.H + h) * D) * D + s * W + col0, g, li);
-    }
     f32x4_t oacc[NQT][NCW];
 #pragma unroll
     for (int b = 0; b < NQT; ++b)
@@ -376,18 +400,34 @@ __global__ __launch_bounds__(kThreads, 1) void la_prefill_main_v2(PrefillParams 
         const __amdgpu_buffer_rsrc_t ro =
             make_rsrc(og + ((int64_t)pb0 * p.H + h) * D + s * W + col0, (uint32_t)pnb * row_bytes);
 #pragma unroll
-        for (int b = 0; b < NQT; ++b)
+        for (int b = 0; b < NQT; ++b) {
+            if constexpr (NCW == 2) {  // columns 8g..8g+7 of row 16b + li: one 16-byte store
+                u32x4_t v;
+                v.x = pack2(oacc[b][0][0], oacc[b][0][1]);
+                v.y = pack2(oacc[b][0][2], oacc[b][0][3]);
+                v.z = pack2(oacc[b][1][0], oacc[b][1][1]);
+                v.w = pack2(oacc[b][1][2], oacc[b][1][3]);
+                __builtin_amdgcn_raw_buffer_store_b128(v, ro, (16 * b + li) * row_bytes + (8 * g) * 2, 0, 0);
+            } else {
 #pragma unroll
-            for (int c = 0; c < NCW; ++c) {
-                u32x2_t v;
-                v.x = pack2(oacc[b][c][0], oacc[b][c][1]);
-                v.y = pack2(oacc[b][c][2], oacc[b][c][3]);
-                __builtin_amdgcn_raw_buffer_store_b64(v, ro, (16 * b + li) * row_bytes + (16 * c + 4 * g) * 2, 0, 0);
-                oacc[b][c] = zero4();
+                for (int c = 0; c < NCW; ++c) {
+                    u32x2_t v;
+                    v.x = pack2(oacc[b][c][0], oacc[b][c][1]);
+                    v.y = pack2(oacc[b][c][2], oacc[b][c][3]);
+                    __builtin_amdgcn_raw_buffer_store_b64(v, ro, (16 * b + li) * row_bytes + (16 * c + 4 * g) * 2, 0, 0);
+                }
             }
+#pragma unroll
+            for (int c = 0; c < NCW; ++c) oacc[b][c] = zero4();
+        }
     };
 
-    if (c0.nb > 0) issue(c0, Slot<0>{});
+    if (c0.nb > 0) issue(c0, Slot<0>{});  // before the prefix loads, so the two overlap
+    if (c0.nb > 0 && !c0.first_of_doc) {
+        const int u_first = p.scan ? u - 1 : p.cu[c0.doc] / p.L;
+        for (int uu = u_first; uu < u; ++uu)
+            load_prefix<D, B, W>(kv, p.ws + (((int64_t)uu * p.H + h) * D) * D + s * W + col0, g, li);
+    }
     int pb0 = t0, pnb = 0;
     int j = 0;
     // One block; its tiles sit in slot SLOT, the next block's go to the other.
