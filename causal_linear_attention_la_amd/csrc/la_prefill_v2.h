@@ -208,16 +208,37 @@ __device__ __forceinline__ void state_update(f32x4_t (&kv)[NA][NC], Frag<bf16_t>
     }
 }
 
+// Segment states in the workspace are private to these kernels, so they are
+// kept in register order: the (D x W) state of one (segment, head, slice) is
+// 4 consecutive wave blocks of D * W / 4 floats, each [tile a][tile c][lane]
+// of 4-float runs -- 16-byte, fully coalesced loads and stores.  (The scan
+// kernel adds states entry by entry and does not care about the order.)
 template <int D, int B, int W, int NA, int NC>
-__device__ __forceinline__ void load_prefix(f32x4_t (&kv)[NA][NC], const float* src, int g, int li) {
+__device__ __forceinline__ void load_ws(f32x4_t (&kv)[NA][NC], const float* src, int lane) {
     using G = Geo<D, B, W>;
     static_assert(NA == G::NDT && NC == G::NCW, "tile counts");
+    const f32x4_t* s4 = reinterpret_cast<const f32x4_t*>(src);
 #pragma unroll
     for (int a = 0; a < G::NDT; ++a)
 #pragma unroll
-        for (int c = 0; c < G::NCW; ++c)
+        for (int c = 0; c < G::NCW; ++c) kv[a][c] += s4[(a * G::NCW + c) * 64 + lane];
+}
+
+template <int D, int B, int W, int NA, int NC>
+__device__ __forceinline__ void store_ws(const f32x4_t (&kv)[NA][NC], float* dst, int lane) {
+    using G = Geo<D, B, W>;
+    static_assert(NA == G::NDT && NC == G::NCW, "tile counts");
+    f32x4_t* d4 = reinterpret_cast<f32x4_t*>(dst);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) kv[a][c][r] += src[(int64_t)state_row(a, g, r) * D + state_col<NC>(c, li)];
+    for (int a = 0; a < G::NDT; ++a)
+#pragma unroll
+        for (int c = 0; c < G::NCW; ++c) d4[(a * G::NCW + c) * 64 + lane] = kv[a][c];
+}
+
+// A wave's block of the workspace state of unit (u, h, s).
+template <int D, int W>
+__device__ __forceinline__ int64_t ws_offset(const PrefillParams& p, int u, int h, int s, int wave) {
+    return (((int64_t)u * p.H + h) * D) * D + (int64_t)s * D * W + (int64_t)wave * (D * W / 4);
 }
 
 template <int D, int B, int W, int NA, int NC>
@@ -310,7 +331,7 @@ __global__ __launch_bounds__(kThreads, 1) void la_segment_state_v2(PrefillParams
         step(Slot<1>{});
         if (jj >= npairs) break;
     }
-    store_state<D, B, W>(kv, p.ws + (((int64_t)u * p.H + h) * D) * D + s * W + col0, g, li);
+    store_ws<D, B, W>(kv, p.ws + ws_offset<D, W>(p, u, h, s, wave), lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -426,7 +447,7 @@ __global__ __launch_bounds__(kThreads, 1) void la_prefill_main_v2(PrefillParams 
     if (c0.nb > 0 && !c0.first_of_doc) {
         const int u_first = p.scan ? u - 1 : p.cu[c0.doc] / p.L;
         for (int uu = u_first; uu < u; ++uu)
-            load_prefix<D, B, W>(kv, p.ws + (((int64_t)uu * p.H + h) * D) * D + s * W + col0, g, li);
+            load_ws<D, B, W>(kv, p.ws + ws_offset<D, W>(p, uu, h, s, wave), lane);
     }
     int pb0 = t0, pnb = 0;
     int j = 0;
