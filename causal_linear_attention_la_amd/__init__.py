@@ -20,7 +20,7 @@ LA_OK, LA_ERR_INVALID_ARG, LA_ERR_UNSUPPORTED, LA_ERR_WORKSPACE, LA_ERR_HIP = ra
 LA_BF16, LA_FP32 = 0, 1
 
 EXPORTED = ("la_prefill", "la_decode", "la_prefill_workspace_size", "la_status_string", "la_prefill_plan",
-            "la_prefill_workspace_size_ex", "la_prefill_ex")
+            "la_prefill_workspace_size_ex", "la_prefill_ex", "la_prefill_resume")
 
 
 class LAError(RuntimeError):
@@ -61,6 +61,9 @@ def load():
     lib.la_prefill.restype = ctypes.c_int
     lib.la_prefill_ex.argtypes = lib.la_prefill.argtypes + [ctypes.POINTER(la_prefill_opts)]
     lib.la_prefill_ex.restype = ctypes.c_int
+    lib.la_prefill_resume.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, vp, vp, i32, i64, ctypes.c_int, vp, sz, vp,
+                                      ctypes.POINTER(la_prefill_opts)]
+    lib.la_prefill_resume.restype = ctypes.c_int
     lib.la_decode.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, ctypes.c_int, vp]
     lib.la_decode.restype = ctypes.c_int
     lib.la_prefill_workspace_size.argtypes = [i64, i32, i32, i32, i32, ctypes.c_int]
@@ -93,6 +96,13 @@ def la_prefill_ex(q, k, v, o, cu_seqlens, H, d, block, kv_state_out, num_seqs, t
                   workspace_bytes, stream, opts: la_prefill_opts | None) -> int:
     return load().la_prefill_ex(q, k, v, o, cu_seqlens, H, d, block, kv_state_out, num_seqs, total_tokens, dtype,
                                 workspace, workspace_bytes, stream, ctypes.byref(opts) if opts is not None else None)
+
+
+def la_prefill_resume(q, k, v, o, cu_seqlens, H, d, block, kv_state_in, kv_state_out, num_seqs, total_tokens, dtype,
+                      workspace, workspace_bytes, stream, opts: la_prefill_opts | None) -> int:
+    return load().la_prefill_resume(q, k, v, o, cu_seqlens, H, d, block, kv_state_in, kv_state_out, num_seqs,
+                                    total_tokens, dtype, workspace, workspace_bytes, stream,
+                                    ctypes.byref(opts) if opts is not None else None)
 
 
 def la_decode(q, k, v, kv_state_inout, o, num_seqs, H, d, dtype, stream) -> int:
@@ -159,12 +169,14 @@ def _ptr(t):
 
 def prefill(q, k, v, cu_seqlens, block: int = 64, want_state: bool = True, out=None, kv_state_out=None,
             workspace=None, seg_len: int = 0, value_slices: int = 0, force_scan: bool = False, stream=None,
-            begin_event=None, end_event=None, variant: int = 0):
+            begin_event=None, end_event=None, variant: int = 0, kv_state_in=None):
     """Lightning-style causal linear attention over packed documents.
 
     q, k, v: [T, H, d] bf16/fp32 CUDA tensors; cu_seqlens: int32 [num_seqs + 1]
     CUDA tensor.  Returns (o, kv_state) with kv_state fp32 [num_seqs, H, d, d]
-    (None when want_state is False).  Asynchronous on the current stream.
+    (None when want_state is False).  kv_state_in (fp32 [num_seqs, H, d, d],
+    optional) is each document's state before its first token (la_prefill_resume).
+    Asynchronous on the current stream (or `stream`).
     """
     import torch
 
@@ -181,8 +193,9 @@ def prefill(q, k, v, cu_seqlens, block: int = 64, want_state: bool = True, out=N
     if need and (ws is None or ws.numel() * ws.element_size() < need):
         ws = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_bytes = ws.numel() * ws.element_size() if ws is not None else 0
-    st = la_prefill_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(cu_seqlens), H, d, block, _ptr(kv), num_seqs, T, dt,
-                       _ptr(ws) if need else None, ws_bytes if need else 0, _stream_ptr(stream), opts)
+    st = la_prefill_resume(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(cu_seqlens), H, d, block, _ptr(kv_state_in),
+                           _ptr(kv), num_seqs, T, dt, _ptr(ws) if need else None, ws_bytes if need else 0,
+                           _stream_ptr(stream), opts)
     if st != LA_OK:
         raise LAError(st, "la_prefill")
     return o, kv

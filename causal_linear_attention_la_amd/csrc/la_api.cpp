@@ -49,13 +49,13 @@ size_t la_prefill_workspace_size(int64_t total_tokens, int32_t num_seqs, int32_t
     return la_prefill_workspace_size_ex(total_tokens, num_seqs, H, d, block, dtype, nullptr);
 }
 
-la_status la_prefill_ex(const void* q, const void* k, const void* v, void* o, const int32_t* cu_seqlens, int32_t H,
-                        int32_t d, int32_t block, float* kv_state_out, int32_t num_seqs, int64_t total_tokens,
-                        la_dtype dtype, void* workspace, size_t workspace_bytes, void* stream,
-                        const la_prefill_opts* opts) {
+la_status la_prefill_resume(const void* q, const void* k, const void* v, void* o, const int32_t* cu_seqlens,
+                            int32_t H, int32_t d, int32_t block, const float* kv_state_in, float* kv_state_out,
+                            int32_t num_seqs, int64_t total_tokens, la_dtype dtype, void* workspace,
+                            size_t workspace_bytes, void* stream, const la_prefill_opts* opts) {
     Plan plan;
-    la_status st = la::validate_prefill(q, k, v, o, cu_seqlens, H, d, block, kv_state_out, num_seqs, total_tokens,
-                                        (int)dtype, workspace, workspace_bytes, opts, &plan);
+    la_status st = la::validate_prefill(q, k, v, o, cu_seqlens, H, d, block, kv_state_in, kv_state_out, num_seqs,
+                                        total_tokens, (int)dtype, workspace, workspace_bytes, opts, &plan);
     if (st != LA_OK) return st;
     la::PrefillParams p{};
     p.q = q;
@@ -63,6 +63,7 @@ la_status la_prefill_ex(const void* q, const void* k, const void* v, void* o, co
     p.v = v;
     p.o = o;
     p.cu = cu_seqlens;
+    p.kv_in = kv_state_in;
     p.kv_out = kv_state_out;
     p.ws = plan.ws_bytes ? reinterpret_cast<float*>(static_cast<char*>(workspace) + plan.ws_states_off) : nullptr;
     p.flags = plan.ws_bytes ? reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + plan.ws_flags_off) : nullptr;
@@ -81,6 +82,14 @@ la_status la_prefill_ex(const void* q, const void* k, const void* v, void* o, co
     hipError_t e = dtype == LA_BF16 ? la::launch_prefill_bf16(p, d, block, plan.W, plan.variant, s, e0, e1)
                                     : la::launch_prefill_fp32(p, d, block, plan.W, plan.variant, s, e0, e1);
     return e == hipSuccess ? LA_OK : LA_ERR_HIP;
+}
+
+la_status la_prefill_ex(const void* q, const void* k, const void* v, void* o, const int32_t* cu_seqlens, int32_t H,
+                        int32_t d, int32_t block, float* kv_state_out, int32_t num_seqs, int64_t total_tokens,
+                        la_dtype dtype, void* workspace, size_t workspace_bytes, void* stream,
+                        const la_prefill_opts* opts) {
+    return la_prefill_resume(q, k, v, o, cu_seqlens, H, d, block, nullptr, kv_state_out, num_seqs, total_tokens,
+                             dtype, workspace, workspace_bytes, stream, opts);
 }
 
 la_status la_prefill(const void* q, const void* k, const void* v, void* o, const int32_t* cu_seqlens, int32_t H,

@@ -110,8 +110,9 @@ la_status make_plan(int64_t T, int32_t num_seqs, int32_t H, int32_t d, int32_t b
 }
 
 la_status validate_prefill(const void* q, const void* k, const void* v, const void* o, const int32_t* cu, int32_t H,
-                           int32_t d, int32_t block, const float* kv_out, int32_t num_seqs, int64_t T, int dtype,
-                           const void* ws, size_t ws_bytes, const la_prefill_opts* opts, Plan* plan) {
+                           int32_t d, int32_t block, const float* kv_in, const float* kv_out, int32_t num_seqs,
+                           int64_t T, int dtype, const void* ws, size_t ws_bytes, const la_prefill_opts* opts,
+                           Plan* plan) {
     if (!q || !k || !v || !o || !cu) return LA_ERR_INVALID_ARG;
     la_status st = make_plan(T, num_seqs, H, d, block, dtype, opts, plan);
     if (st != LA_OK) return st;
@@ -125,6 +126,10 @@ la_status validate_prefill(const void* q, const void* k, const void* v, const vo
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(cu, 4))
         return LA_ERR_INVALID_ARG;
     if (kv_out && !aligned(kv_out, 16)) return LA_ERR_INVALID_ARG;
+    if (kv_in && !aligned(kv_in, 16)) return LA_ERR_INVALID_ARG;
+    // the incoming states are read while outputs are written: no overlap with any output
+    if (kv_in && (overlap(kv_in, state, o, tensor) || overlap(kv_in, state, kv_out, state)))
+        return LA_ERR_INVALID_ARG;
     if (overlap(o, tensor, q, tensor) || overlap(o, tensor, k, tensor) || overlap(o, tensor, v, tensor))
         return LA_ERR_INVALID_ARG;
     if (kv_out && (overlap(kv_out, state, q, tensor) || overlap(kv_out, state, k, tensor) ||
@@ -135,7 +140,8 @@ la_status validate_prefill(const void* q, const void* k, const void* v, const vo
         if (!aligned(ws, 256)) return LA_ERR_INVALID_ARG;
         const size_t wn = plan->ws_bytes;
         if (overlap(ws, wn, q, tensor) || overlap(ws, wn, k, tensor) || overlap(ws, wn, v, tensor) ||
-            overlap(ws, wn, o, tensor) || (kv_out && overlap(ws, wn, kv_out, state)))
+            overlap(ws, wn, o, tensor) || (kv_out && overlap(ws, wn, kv_out, state)) ||
+            (kv_in && overlap(ws, wn, kv_in, state)))
             return LA_ERR_INVALID_ARG;
     }
     return LA_OK;

@@ -32,8 +32,9 @@ la_status make_plan(int64_t T, int32_t num_seqs, int32_t H, int32_t d, int32_t b
 
 // Full prefill validation (shapes, plan, pointers, alignment, overlap, workspace).
 la_status validate_prefill(const void* q, const void* k, const void* v, const void* o, const int32_t* cu, int32_t H,
-                           int32_t d, int32_t block, const float* kv_out, int32_t num_seqs, int64_t T, int dtype,
-                           const void* ws, size_t ws_bytes, const la_prefill_opts* opts, Plan* plan);
+                           int32_t d, int32_t block, const float* kv_in, const float* kv_out, int32_t num_seqs,
+                           int64_t T, int dtype, const void* ws, size_t ws_bytes, const la_prefill_opts* opts,
+                           Plan* plan);
 
 la_status validate_decode(const void* q, const void* k, const void* v, const float* S, const void* o,
                           int32_t num_seqs, int32_t H, int32_t d, int dtype);

@@ -31,6 +31,7 @@ struct PrefillParams {
     const void* v;
     void* o;
     const int32_t* cu;
+    const float* kv_in;  // [num_seqs][H][D][D] state before each document, or null (zero)
     float* kv_out;   // [num_seqs][H][D][D] or null
     float* ws;       // segment states [nseg][H][D][D] (null when nseg == 1)
     int32_t* flags;  // [nseg]: bit 0 = the segment's last document continues past it,
@@ -299,6 +300,26 @@ __global__ __launch_bounds__(kThreads) void la_segment_scan_kernel(float* __rest
 }
 
 // ---------------------------------------------------------------------------
+// Final state of the empty documents whose start lies in segment u (the last
+// segment also takes those at the very end): the incoming state, or zero.
+template <int D, int W>
+__device__ __forceinline__ void empty_doc_states(const PrefillParams& p, int u, int h, int s, int t0, int t1,
+                                                 int tid) {
+    const int lo = doc_lower(p.cu, p.num_seqs, t0);
+    const int hi = (u == p.nseg - 1) ? p.num_seqs : doc_lower(p.cu, p.num_seqs, t1);
+    for (int d = lo; d < hi; ++d) {
+        if (p.cu[d + 1] != p.cu[d]) continue;
+        const int64_t base = (((int64_t)d * p.H + h) * D) * D + s * W;
+        float* dst = p.kv_out + base;
+        const float* src = p.kv_in ? p.kv_in + base : nullptr;
+        for (int i = tid; i < D * W; i += kThreads) {
+            const int64_t e = (int64_t)(i / W) * D + (i % W);
+            dst[e] = src ? src[e] : 0.f;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // The block loop.
 template <typename TIn, int D, int B, int W>
 __global__ __launch_bounds__(kThreads, 1) void la_prefill_main_kernel(PrefillParams p) {
@@ -366,6 +387,20 @@ __global__ __launch_bounds__(kThreads, 1) void la_prefill_main_kernel(PrefillPar
             }
         }
     }
+    // A caller-supplied state before the document's first token joins the prefix.
+    auto add_kv_in = [&](int doc) {
+        const float* src = p.kv_in + (((int64_t)doc * p.H + h) * D) * D + s * W;
+#pragma unroll
+        for (int j = 0; j < KVPW; ++j) {
+            const int t = wave + kWaves * j;
+            if (t < NKV) {
+                const int a = t / NCT, c = t % NCT;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) kv[j][r] += src[(int64_t)(16 * a + 4 * g + r) * D + 16 * c + li];
+            }
+        }
+    };
+    if (p.kv_in && cur.nb > 0) add_kv_in(cur.doc);
     __syncthreads();  // LDS zeroed before the state copy below
 #pragma unroll
     for (int j = 0; j < KVPW; ++j) {
@@ -490,6 +525,7 @@ __global__ __launch_bounds__(kThreads, 1) void la_prefill_main_kernel(PrefillPar
         if (nxt.nb > 0 && nxt.first_of_doc) {
 #pragma unroll
             for (int j = 0; j < KVPW; ++j) kv[j] = zero4();
+            if (p.kv_in) add_kv_in(nxt.doc);
         }
 #pragma unroll
         for (int j = 0; j < KVPW; ++j) {
@@ -502,16 +538,9 @@ __global__ __launch_bounds__(kThreads, 1) void la_prefill_main_kernel(PrefillPar
         cur = nxt;
     }
 
-    // Empty documents placed in this segment get a zero final state.
-    if (p.kv_out) {
-        const int lo = doc_lower(p.cu, p.num_seqs, t0);
-        const int hi = (u == p.nseg - 1) ? p.num_seqs : doc_lower(p.cu, p.num_seqs, t1);
-        for (int d = lo; d < hi; ++d) {
-            if (p.cu[d + 1] != p.cu[d]) continue;
-            float* dst = p.kv_out + (((int64_t)d * p.H + h) * D) * D + s * W;
-            for (int i = tid; i < D * W; i += kThreads) dst[(int64_t)(i / W) * D + (i % W)] = 0.f;
-        }
-    }
+    // Empty documents placed in this segment keep their incoming state (zero
+    // when none is given).
+    if (p.kv_out) empty_doc_states<D, W>(p, u, h, s, t0, t1, tid);
 }
 
 }  // namespace la

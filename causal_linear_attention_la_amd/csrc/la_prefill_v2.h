@@ -241,6 +241,19 @@ __device__ __forceinline__ int64_t ws_offset(const PrefillParams& p, int u, int 
     return (((int64_t)u * p.H + h) * D) * D + (int64_t)s * D * W + (int64_t)wave * (D * W / 4);
 }
 
+// Adds a state stored in the documented [key][value] layout (kv_in).
+template <int D, int B, int W, int NA, int NC>
+__device__ __forceinline__ void add_state(f32x4_t (&kv)[NA][NC], const float* src, int g, int li) {
+    using G = Geo<D, B, W>;
+    static_assert(NA == G::NDT && NC == G::NCW, "tile counts");
+#pragma unroll
+    for (int a = 0; a < G::NDT; ++a)
+#pragma unroll
+        for (int c = 0; c < G::NCW; ++c)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) kv[a][c][r] += src[(int64_t)state_row(a, g, r) * D + state_col<NC>(c, li)];
+}
+
 template <int D, int B, int W, int NA, int NC>
 __device__ __forceinline__ void store_state(const f32x4_t (&kv)[NA][NC], float* dst, int g, int li) {
     using G = Geo<D, B, W>;
@@ -449,6 +462,9 @@ __global__ __launch_bounds__(kThreads, 1) void la_prefill_main_v2(PrefillParams 
         for (int uu = u_first; uu < u; ++uu)
             load_ws<D, B, W>(kv, p.ws + ws_offset<D, W>(p, uu, h, s, wave), lane);
     }
+    // a caller-supplied state before the document's first token joins the prefix
+    if (p.kv_in && c0.nb > 0)
+        add_state<D, B, W>(kv, p.kv_in + (((int64_t)c0.doc * p.H + h) * D) * D + s * W + col0, g, li);
     int pb0 = t0, pnb = 0;
     int j = 0;
     // One block; its tiles sit in slot SLOT, the next block's go to the other.
@@ -518,6 +534,10 @@ __global__ __launch_bounds__(kThreads, 1) void la_prefill_main_v2(PrefillParams 
             for (int a = 0; a < NDT; ++a)
 #pragma unroll
                 for (int c = 0; c < NCW; ++c) kv[a][c] = zero4();
+            if (p.kv_in && c1.nb > 0 && c1.first_of_doc) {  // the next document starts here
+                add_state<D, B, W>(kv, p.kv_in + (((int64_t)c1.doc * p.H + h) * D) * D + s * W + col0, g, li);
+                vm_wait<0>();
+            }
         }
         pb0 = c0.b0;
         pnb = c0.nb;
@@ -534,15 +554,7 @@ __global__ __launch_bounds__(kThreads, 1) void la_prefill_main_v2(PrefillParams 
         finish(pb0, pnb);
     }
 
-    if (p.kv_out) {
-        const int lo = doc_lower(p.cu, p.num_seqs, t0);
-        const int hi = (u == p.nseg - 1) ? p.num_seqs : doc_lower(p.cu, p.num_seqs, t1);
-        for (int d = lo; d < hi; ++d) {
-            if (p.cu[d + 1] != p.cu[d]) continue;
-            float* dst = p.kv_out + (((int64_t)d * p.H + h) * D) * D + s * W;
-            for (int i = tid; i < D * W; i += kThreads) dst[(int64_t)(i / W) * D + (i % W)] = 0.f;
-        }
-    }
+    if (p.kv_out) empty_doc_states<D, W>(p, u, h, s, t0, t1, tid);
 }
 
 }  // namespace v2

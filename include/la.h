@@ -156,6 +156,28 @@ la_status la_prefill_ex(const void* q, const void* k, const void* v, void* o, co
                         la_dtype dtype, void* workspace, size_t workspace_bytes, void* stream,
                         const la_prefill_opts* opts);
 
+/* Prefill that resumes from given states (chunked prefill, prefix-cache
+ * resume): identical to la_prefill_ex except that document delta starts from
+ * kv_state_in[delta, h] instead of zero, i.e. for t in the document
+ *     KV_t = kv_state_in + sum_{s <= t, s in the document} k_s^T v_s ,  o_t = q_t . KV_t .
+ * This is the recurrence continued across a cut ("MiniMax-01技术报告解读",
+ * §3.3 item 1: prefix KV cache; §3.2 item 3: a sequence piece starts from the
+ * state its predecessors leave).  A sequence prefilled in chunks, each chunk
+ * resuming from the previous chunk's kv_state_out, gives the single-call
+ * result up to floating-point summation order.
+ *
+ *   kv_state_in  [num_seqs, H, d, d] fp32, device, 16-byte aligned, read only,
+ *                or NULL (then exactly la_prefill_ex).  An empty document's
+ *                kv_state_out is its kv_state_in.  Must not overlap o,
+ *                kv_state_out or the workspace (so the state cannot be
+ *                updated in place: use two buffers and swap).
+ *   Everything else as in la_prefill / la_prefill_ex (opts may be NULL).
+ */
+la_status la_prefill_resume(const void* q, const void* k, const void* v, void* o, const int32_t* cu_seqlens,
+                            int32_t H, int32_t d, int32_t block, const float* kv_state_in, float* kv_state_out,
+                            int32_t num_seqs, int64_t total_tokens, la_dtype dtype, void* workspace,
+                            size_t workspace_bytes, void* stream, const la_prefill_opts* opts);
+
 #ifdef __cplusplus
 }
 #endif

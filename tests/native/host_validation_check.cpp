@@ -67,20 +67,27 @@ int main() {
     const int64_t T = 8192;
     EXPECT(make_plan(T, 1, 8, 128, 64, LA_BF16, nullptr, &p) == LA_OK);
     const size_t need = p.ws_bytes;
-    EXPECT(validate_prefill(q, k, v, o, cu, 8, 128, 64, kv, 1, T, LA_BF16, ws, need, nullptr, &p) == LA_OK);
-    EXPECT(validate_prefill(nullptr, k, v, o, cu, 8, 128, 64, kv, 1, T, LA_BF16, ws, need, nullptr, &p) == LA_ERR_INVALID_ARG);
-    EXPECT(validate_prefill(q, k, v, nullptr, cu, 8, 128, 64, kv, 1, T, LA_BF16, ws, need, nullptr, &p) == LA_ERR_INVALID_ARG);
-    EXPECT(validate_prefill(q, k, v, o, nullptr, 8, 128, 64, kv, 1, T, LA_BF16, ws, need, nullptr, &p) == LA_ERR_INVALID_ARG);
-    EXPECT(validate_prefill(P(G + 8), k, v, o, cu, 8, 128, 64, kv, 1, T, LA_BF16, ws, need, nullptr, &p) == LA_ERR_INVALID_ARG);
-    EXPECT(validate_prefill(q, k, v, P(G + 4096), cu, 8, 128, 64, kv, 1, T, LA_BF16, ws, need, nullptr, &p) == LA_ERR_INVALID_ARG);
-    EXPECT(validate_prefill(q, k, v, o, cu, 8, 128, 64, static_cast<float*>(P(4 * G + 64)), 1, T, LA_BF16, ws, need, nullptr, &p) == LA_ERR_INVALID_ARG);
-    EXPECT(validate_prefill(q, k, v, o, cu, 8, 128, 64, kv, 1, T, LA_BF16, nullptr, need, nullptr, &p) == (need ? LA_ERR_WORKSPACE : LA_OK));
+    EXPECT(validate_prefill(q, k, v, o, cu, 8, 128, 64, nullptr, kv, 1, T, LA_BF16, ws, need, nullptr, &p) == LA_OK);
+    EXPECT(validate_prefill(nullptr, k, v, o, cu, 8, 128, 64, nullptr, kv, 1, T, LA_BF16, ws, need, nullptr, &p) == LA_ERR_INVALID_ARG);
+    EXPECT(validate_prefill(q, k, v, nullptr, cu, 8, 128, 64, nullptr, kv, 1, T, LA_BF16, ws, need, nullptr, &p) == LA_ERR_INVALID_ARG);
+    EXPECT(validate_prefill(q, k, v, o, nullptr, 8, 128, 64, nullptr, kv, 1, T, LA_BF16, ws, need, nullptr, &p) == LA_ERR_INVALID_ARG);
+    EXPECT(validate_prefill(P(G + 8), k, v, o, cu, 8, 128, 64, nullptr, kv, 1, T, LA_BF16, ws, need, nullptr, &p) == LA_ERR_INVALID_ARG);
+    EXPECT(validate_prefill(q, k, v, P(G + 4096), cu, 8, 128, 64, nullptr, kv, 1, T, LA_BF16, ws, need, nullptr, &p) == LA_ERR_INVALID_ARG);
+    EXPECT(validate_prefill(q, k, v, o, cu, 8, 128, 64, nullptr, static_cast<float*>(P(4 * G + 64)), 1, T, LA_BF16, ws, need, nullptr, &p) == LA_ERR_INVALID_ARG);
+    EXPECT(validate_prefill(q, k, v, o, cu, 8, 128, 64, nullptr, kv, 1, T, LA_BF16, nullptr, need, nullptr, &p) == (need ? LA_ERR_WORKSPACE : LA_OK));
     if (need) {
-        EXPECT(validate_prefill(q, k, v, o, cu, 8, 128, 64, kv, 1, T, LA_BF16, ws, need - 1, nullptr, &p) == LA_ERR_WORKSPACE);
-        EXPECT(validate_prefill(q, k, v, o, cu, 8, 128, 64, kv, 1, T, LA_BF16, P(7 * G + 16), need, nullptr, &p) == LA_ERR_INVALID_ARG);
-        EXPECT(validate_prefill(q, k, v, o, cu, 8, 128, 64, kv, 1, T, LA_BF16, P(G), need, nullptr, &p) == LA_ERR_INVALID_ARG);
+        EXPECT(validate_prefill(q, k, v, o, cu, 8, 128, 64, nullptr, kv, 1, T, LA_BF16, ws, need - 1, nullptr, &p) == LA_ERR_WORKSPACE);
+        EXPECT(validate_prefill(q, k, v, o, cu, 8, 128, 64, nullptr, kv, 1, T, LA_BF16, P(7 * G + 16), need, nullptr, &p) == LA_ERR_INVALID_ARG);
+        EXPECT(validate_prefill(q, k, v, o, cu, 8, 128, 64, nullptr, kv, 1, T, LA_BF16, P(G), need, nullptr, &p) == LA_ERR_INVALID_ARG);
     }
-    EXPECT(validate_prefill(q, k, v, o, cu, 8, 128, 64, nullptr, 1, T, LA_BF16, ws, need, nullptr, &p) == LA_OK);
+    EXPECT(validate_prefill(q, k, v, o, cu, 8, 128, 64, nullptr, nullptr, 1, T, LA_BF16, ws, need, nullptr, &p) == LA_OK);
+    // incoming states: aligned, and overlapping no output
+    float* kin = static_cast<float*>(P(8 * G));
+    EXPECT(validate_prefill(q, k, v, o, cu, 8, 128, 64, kin, kv, 1, T, LA_BF16, ws, need, nullptr, &p) == LA_OK);
+    EXPECT(validate_prefill(q, k, v, o, cu, 8, 128, 64, static_cast<float*>(P(8 * G + 4)), kv, 1, T, LA_BF16, ws, need, nullptr, &p) == LA_ERR_INVALID_ARG);
+    EXPECT(validate_prefill(q, k, v, o, cu, 8, 128, 64, kv, kv, 1, T, LA_BF16, ws, need, nullptr, &p) == LA_ERR_INVALID_ARG);
+    EXPECT(validate_prefill(q, k, v, o, cu, 8, 128, 64, static_cast<float*>(P(4 * G + 256)), kv, 1, T, LA_BF16, ws, need, nullptr, &p) == LA_ERR_INVALID_ARG);
+    if (need) EXPECT(validate_prefill(q, k, v, o, cu, 8, 128, 64, static_cast<float*>(ws), kv, 1, T, LA_BF16, ws, need, nullptr, &p) == LA_ERR_INVALID_ARG);
 
     // decode
     EXPECT(validate_decode(q, k, v, kv, o, 256, 64, 128, LA_BF16) == LA_OK);
