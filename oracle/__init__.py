@@ -41,6 +41,7 @@ def _bind(lib):
     lib.ora_recurrent.argtypes = [vp, vp, vp, ctypes.c_int, vp, i32, i32, i32, i32, i32, vp, vp, vp, ctypes.c_int]
     lib.ora_quadratic.argtypes = [vp, vp, vp, ctypes.c_int, vp, i32, i32, i32, vp, vp, vp]
     lib.ora_decode_step.argtypes = [vp, vp, vp, ctypes.c_int, i64, i32, vp, vp, ctypes.c_int]
+    lib.ora_backward.argtypes = [vp, vp, vp, vp, ctypes.c_int, vp, i32, i32, i32, vp, vp, vp, vp, vp, vp, ctypes.c_int]
     lib.ora_last_threads.restype = ctypes.c_int
     return lib
 
@@ -116,6 +117,27 @@ def quadratic(q, k, v, cu_seqlens, kv_in=None, lib=None):
     if rc != 0:
         raise ValueError("ora_quadratic rejected its arguments")
     return o, kvo
+
+
+def backward(q, k, v, dout, cu_seqlens, kv_in=None, dkv_out=None, want_dkv_in=True, nthreads: int = 0, lib=None):
+    """Gradients of sum(dout * o) + sum(dkv_out * kv_out) for the prefill of
+    (q, k, v, cu_seqlens, kv_in).  Returns fp64 (dq, dk, dv, dkv_in or None)."""
+    lib = lib or load()
+    q, k, v, dout = _c(q), _c(k), _c(v), _c(dout)
+    assert q.shape == k.shape == v.shape == dout.shape and q.dtype == k.dtype == v.dtype == dout.dtype
+    T, H, d = q.shape
+    cu = _c(cu_seqlens, np.int32)
+    D = cu.size - 1
+    assert cu[-1] == T
+    kvi = None if kv_in is None else _c(kv_in, np.float64)
+    dko = None if dkv_out is None else _c(dkv_out, np.float64)
+    dq, dk, dv = (np.empty((T, H, d), dtype=np.float64) for _ in range(3))
+    dki = np.empty((D, H, d, d), dtype=np.float64) if want_dkv_in else None
+    rc = lib.ora_backward(_p(q), _p(k), _p(v), _p(dout), _dtype_code(q), _p(cu), D, H, d, _p(kvi), _p(dko), _p(dq),
+                          _p(dk), _p(dv), _p(dki), nthreads)
+    if rc != 0:
+        raise ValueError("ora_backward rejected its arguments")
+    return dq, dk, dv, dki
 
 
 def decode_step(q, k, v, S, nthreads: int = 0, lib=None):

@@ -226,6 +226,90 @@ int ora_quadratic(const void* q, const void* k, const void* v, int dtype, const 
     return 0;
 }
 
+/* ------------------------------------------------------------- backward */
+
+/* Gradients of L = sum_t dO_t . o_t + <dKV_out, KV_out> (per document and
+ * head), written from the definition o_t = q_t . S_t with
+ * S_t = KV_in + sum_{s <= t} k_s^T v_s and KV_out = S_last.  The pages give no
+ * backward; it follows from the forward definition by the chain rule:
+ *   dq_t   = S_t dO_t                  (dq_t[i] = sum_j S_t[i][j] dO_t[j])
+ *   G_s    = dKV_out + sum_{t >= s} q_t^T dO_t
+ *   dk_s   = G_s v_s                   (dk_s[i] = sum_j G_s[i][j] v_s[j])
+ *   dv_s   = k_s G_s                   (dv_s[j] = sum_i k_s[i] G_s[i][j])
+ *   dKV_in = G_first
+ * One task per (document, head): a forward sweep for dq, a backward sweep
+ * for G, dk, dv. */
+typedef struct {
+    const void *q, *k, *v, *dout;
+    int dtype;
+    const int32_t* cu;
+    int32_t num_seqs, H, d;
+    const double *kv_in, *dkv_out;
+    double *dq, *dk, *dv, *dkv_in;
+} bwd_ctx;
+
+static void bwd_task(void* cv, int64_t task) {
+    const bwd_ctx* c = (const bwd_ctx*)cv;
+    const int32_t d = c->d, H = c->H;
+    const int32_t h = (int32_t)(task % H), doc = (int32_t)(task / H);
+    const size_t sbase = ((size_t)doc * H + h) * (size_t)d * d;
+    double* M = (double*)malloc(sizeof(double) * (size_t)d * d);
+    double* a = (double*)malloc(sizeof(double) * (size_t)d);
+    double* b = (double*)malloc(sizeof(double) * (size_t)d);
+
+    /* forward sweep: S_t, dq_t */
+    for (size_t e = 0; e < (size_t)d * d; ++e) M[e] = c->kv_in ? c->kv_in[sbase + e] : 0.0;
+    for (int64_t t = c->cu[doc]; t < c->cu[doc + 1]; ++t) {
+        const int64_t row = (t * H + h) * (int64_t)d;
+        for (int32_t i = 0; i < d; ++i) a[i] = widen(c->k, c->dtype, row + i);
+        for (int32_t j = 0; j < d; ++j) b[j] = widen(c->v, c->dtype, row + j);
+        for (int32_t i = 0; i < d; ++i)
+            for (int32_t j = 0; j < d; ++j) M[(size_t)i * d + j] += a[i] * b[j];
+        for (int32_t j = 0; j < d; ++j) b[j] = widen(c->dout, c->dtype, row + j);
+        for (int32_t i = 0; i < d; ++i) {
+            double acc = 0.0;
+            for (int32_t j = 0; j < d; ++j) acc += M[(size_t)i * d + j] * b[j];
+            c->dq[row + i] = acc;
+        }
+    }
+    /* backward sweep: G_s, dk_s, dv_s */
+    for (size_t e = 0; e < (size_t)d * d; ++e) M[e] = c->dkv_out ? c->dkv_out[sbase + e] : 0.0;
+    for (int64_t t = (int64_t)c->cu[doc + 1] - 1; t >= c->cu[doc]; --t) {
+        const int64_t row = (t * H + h) * (int64_t)d;
+        for (int32_t i = 0; i < d; ++i) a[i] = widen(c->q, c->dtype, row + i);
+        for (int32_t j = 0; j < d; ++j) b[j] = widen(c->dout, c->dtype, row + j);
+        for (int32_t i = 0; i < d; ++i)
+            for (int32_t j = 0; j < d; ++j) M[(size_t)i * d + j] += a[i] * b[j];
+        for (int32_t j = 0; j < d; ++j) b[j] = widen(c->v, c->dtype, row + j);
+        for (int32_t i = 0; i < d; ++i) {
+            double acc = 0.0;
+            for (int32_t j = 0; j < d; ++j) acc += M[(size_t)i * d + j] * b[j];
+            c->dk[row + i] = acc;
+        }
+        for (int32_t i = 0; i < d; ++i) a[i] = widen(c->k, c->dtype, row + i);
+        for (int32_t j = 0; j < d; ++j) {
+            double acc = 0.0;
+            for (int32_t i = 0; i < d; ++i) acc += a[i] * M[(size_t)i * d + j];
+            c->dv[row + j] = acc;
+        }
+    }
+    if (c->dkv_in)
+        for (size_t e = 0; e < (size_t)d * d; ++e) c->dkv_in[sbase + e] = M[e];
+    free(M);
+    free(a);
+    free(b);
+}
+
+int ora_backward(const void* q, const void* k, const void* v, const void* dout, int dtype, const int32_t* cu_seqlens,
+                 int32_t num_seqs, int32_t H, int32_t d, const double* kv_in, const double* dkv_out, double* dq,
+                 double* dk, double* dv, double* dkv_in, int nthreads) {
+    if (!q || !k || !v || !dout || !dq || !dk || !dv || dtype < 0 || dtype > 2 || H < 1 || d < 1) return -1;
+    if (check_cu(cu_seqlens, num_seqs)) return -1;
+    bwd_ctx c = {q, k, v, dout, dtype, cu_seqlens, num_seqs, H, d, kv_in, dkv_out, dq, dk, dv, dkv_in};
+    run_tasks((int64_t)num_seqs * H, nthreads, bwd_task, &c);
+    return 0;
+}
+
 /* ---------------------------------------------------------- decode step */
 
 typedef struct {

@@ -47,6 +47,18 @@ int ora_quadratic(const void* q, const void* k, const void* v, int dtype, const 
 int ora_decode_step(const void* q, const void* k, const void* v, int dtype, int64_t npairs, int32_t d,
                     double* S, double* o, int nthreads);
 
+/* Backward of the prefill (not on the pages; the chain rule applied to the
+ * definition above).  Given dO (dout, [T, H, d], same dtype code as q) and
+ * optionally dKV_out (fp64 [num_seqs, H, d, d], the gradient of a loss with
+ * respect to kv_out), writes fp64 dq, dk, dv [T, H, d] and, if dkv_in is not
+ * NULL, the gradient with respect to kv_in (fp64 [num_seqs, H, d, d]):
+ *   dq_t = S_t dO_t,  G_s = dKV_out + sum_{t >= s} q_t^T dO_t,
+ *   dk_s = G_s v_s,   dv_s = k_s G_s,  dKV_in = G at the document's first token,
+ * with S_t = kv_in + sum_{s <= t} k_s^T v_s. */
+int ora_backward(const void* q, const void* k, const void* v, const void* dout, int dtype, const int32_t* cu_seqlens,
+                 int32_t num_seqs, int32_t H, int32_t d, const double* kv_in, const double* dkv_out, double* dq,
+                 double* dk, double* dv, double* dkv_in, int nthreads);
+
 /* Threads the last call used (for reporting). */
 int ora_last_threads(void);
 

@@ -201,8 +201,38 @@ def pin_decode_continues_prefill(lib):
     return _close(S1, ref_S) and _close(o, np.einsum("pi,pij->pj", qq, ref_S))
 
 
+def pin_backward_finite_differences(lib):
+    """The backward against central differences of the forward.  The loss
+    L = sum(dO * o) + sum(dKV_out * kv_out) is affine in any single input
+    element (o is linear in each of q, k, v and kv_in), so a central
+    difference with step 1 equals the derivative up to rounding."""
+    rng = np.random.default_rng(31)
+    T, H, d = 9, 2, 3
+    cu = np.array([0, 4, 4, 9], np.int32)
+    q, k, v, dout = (rng.standard_normal((T, H, d)) for _ in range(4))
+    kv_in, dkv_out = (rng.standard_normal((3, H, d, d)) for _ in range(2))
+
+    def loss(q_, k_, v_, kv_):
+        o, kvo = oracle.recurrent(q_, k_, v_, cu, kv_in=kv_, nthreads=1, lib=lib)
+        return float(np.sum(dout * o) + np.sum(dkv_out * kvo))
+
+    grads = oracle.backward(q, k, v, dout, cu, kv_in=kv_in, dkv_out=dkv_out, nthreads=1, lib=lib)
+    args = [q, k, v, kv_in]
+    for which, g in enumerate((grads[0], grads[1], grads[2], grads[3])):
+        fd = np.empty_like(args[which])
+        for idx in np.ndindex(args[which].shape):
+            plus = [a.copy() for a in args]
+            minus = [a.copy() for a in args]
+            plus[which][idx] += 1.0
+            minus[which][idx] -= 1.0
+            fd[idx] = 0.5 * (loss(*plus) - loss(*minus))
+        if not _close(g, fd, 1e-10):
+            return False
+    return True
+
+
 PINS = [pin_hand_worked, pin_forms_agree, pin_split_resume, pin_closed_forms, pin_linearity,
-        pin_packed_equals_separate, pin_decode_continues_prefill]
+        pin_packed_equals_separate, pin_decode_continues_prefill, pin_backward_finite_differences]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -268,6 +298,15 @@ MUTANTS = [
     ("decode: output read before the update",
      r"/\* S <- S \+ k\^T v \*/\n(\s+)for \(int32_t i = 0; i < d; \+\+i\) \{\n(\s+)double ki",
      "/* S <- S + k^T v */\n\\1if (c->o) for (int32_t j = 0; j < d; ++j) { double a0 = 0.0; for (int32_t i = 0; i < d; ++i) a0 += widen(c->q, c->dtype, row + i) * S[(size_t)i * d + j]; c->o[row + j] = a0; }\n\\1if (c->o) return;\n\\1for (int32_t i = 0; i < d; ++i) {\n\\2double ki"),
+    ("backward: dKV_out ignored",
+     r"M\[e\] = c->dkv_out \? c->dkv_out\[sbase \+ e\] : 0\.0;", "M[e] = 0.0;"),
+    ("backward: dq from the transposed state",
+     r"acc \+= M\[\(size_t\)i \* d \+ j\] \* b\[j\];\n(\s+)c->dq", "acc += M[(size_t)j * d + i] * b[j];\n\\1c->dq"),
+    ("backward: dv from the transposed reverse state",
+     r"acc \+= a\[i\] \* M\[\(size_t\)i \* d \+ j\];", "acc += a[i] * M[(size_t)j * d + i];"),
+    ("backward: token s left out of its own reverse sum",
+     r"(\s+)for \(int32_t i = 0; i < d; \+\+i\) a\[i\] = widen\(c->q, c->dtype, row \+ i\);",
+     "\\1for (int32_t i = 0; i < d; ++i) a[i] = (t == (int64_t)c->cu[doc + 1] - 1) ? 0.0 : widen(c->q, c->dtype, row + i + H * d);"),
 ]
 
 
