@@ -20,7 +20,7 @@ LA_OK, LA_ERR_INVALID_ARG, LA_ERR_UNSUPPORTED, LA_ERR_WORKSPACE, LA_ERR_HIP = ra
 LA_BF16, LA_FP32 = 0, 1
 
 EXPORTED = ("la_prefill", "la_decode", "la_prefill_workspace_size", "la_status_string", "la_prefill_plan",
-            "la_prefill_workspace_size_ex", "la_prefill_ex", "la_prefill_resume")
+            "la_prefill_workspace_size_ex", "la_prefill_ex", "la_prefill_resume", "la_prefill_backward")
 
 
 class LAError(RuntimeError):
@@ -64,6 +64,9 @@ def load():
     lib.la_prefill_resume.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, vp, vp, i32, i64, ctypes.c_int, vp, sz, vp,
                                       ctypes.POINTER(la_prefill_opts)]
     lib.la_prefill_resume.restype = ctypes.c_int
+    lib.la_prefill_backward.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, vp, vp, vp, vp, vp, vp, i32, i64,
+                                        ctypes.c_int, vp, sz, vp, ctypes.POINTER(la_prefill_opts)]
+    lib.la_prefill_backward.restype = ctypes.c_int
     lib.la_decode.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, ctypes.c_int, vp]
     lib.la_decode.restype = ctypes.c_int
     lib.la_prefill_workspace_size.argtypes = [i64, i32, i32, i32, i32, ctypes.c_int]
@@ -103,6 +106,14 @@ def la_prefill_resume(q, k, v, o, cu_seqlens, H, d, block, kv_state_in, kv_state
     return load().la_prefill_resume(q, k, v, o, cu_seqlens, H, d, block, kv_state_in, kv_state_out, num_seqs,
                                     total_tokens, dtype, workspace, workspace_bytes, stream,
                                     ctypes.byref(opts) if opts is not None else None)
+
+
+def la_prefill_backward(q, k, v, dout, cu_seqlens, H, d, block, kv_state_in, dkv_state_out, dq, dk, dv, dkv_state_in,
+                        num_seqs, total_tokens, dtype, workspace, workspace_bytes, stream,
+                        opts: la_prefill_opts | None) -> int:
+    return load().la_prefill_backward(q, k, v, dout, cu_seqlens, H, d, block, kv_state_in, dkv_state_out, dq, dk, dv,
+                                      dkv_state_in, num_seqs, total_tokens, dtype, workspace, workspace_bytes, stream,
+                                      ctypes.byref(opts) if opts is not None else None)
 
 
 def la_decode(q, k, v, kv_state_inout, o, num_seqs, H, d, dtype, stream) -> int:
@@ -199,6 +210,33 @@ def prefill(q, k, v, cu_seqlens, block: int = 64, want_state: bool = True, out=N
     if st != LA_OK:
         raise LAError(st, "la_prefill")
     return o, kv
+
+
+def backward(q, k, v, dout, cu_seqlens, block: int = 64, kv_state_in=None, dkv_state_out=None,
+             want_dkv_in: bool = True, workspace=None, seg_len: int = 0, value_slices: int = 0,
+             force_scan: bool = False, stream=None, variant: int = 0):
+    """Gradients of the prefill (la_prefill_backward).  dout is dL/do
+    ([T, H, d], same dtype as q); dkv_state_out (fp32 [num_seqs, H, d, d] or
+    None) is dL/dkv_state_out.  Returns (dq, dk, dv, dkv_state_in or None)."""
+    import torch
+
+    T, H, d = q.shape
+    dt = _dtype_code(q)
+    num_seqs = cu_seqlens.numel() - 1
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    dkv_in = torch.empty((num_seqs, H, d, d), dtype=torch.float32, device=q.device) if want_dkv_in else None
+    opts = make_opts(seg_len, value_slices, force_scan, None, None, variant)
+    need = la_prefill_workspace_size_ex(T, num_seqs, H, d, block, dt, opts)
+    ws = workspace
+    if need and (ws is None or ws.numel() * ws.element_size() < need):
+        ws = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = ws.numel() * ws.element_size() if ws is not None else 0
+    st = la_prefill_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(cu_seqlens), H, d, block, _ptr(kv_state_in),
+                             _ptr(dkv_state_out), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dkv_in), num_seqs, T, dt,
+                             _ptr(ws) if need else None, ws_bytes if need else 0, _stream_ptr(stream), opts)
+    if st != LA_OK:
+        raise LAError(st, "la_prefill_backward")
+    return dq, dk, dv, dkv_in
 
 
 def decode(q, k, v, kv_state, out=None, stream=None):

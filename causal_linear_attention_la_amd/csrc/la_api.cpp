@@ -7,6 +7,42 @@
 
 using la::Plan;
 
+namespace {
+
+// Fills the launch parameters of one validated prefill pass and enqueues it.
+la_status enqueue_prefill(const Plan& plan, const void* q, const void* k, const void* v, void* o, const int32_t* cu,
+                          int32_t H, int32_t d, int32_t block, const float* kv_in, int kv_in_t, float* kv_out,
+                          int rev, int32_t num_seqs, int64_t T, la_dtype dtype, void* workspace, void* stream,
+                          hipEvent_t e0, hipEvent_t e1) {
+    la::PrefillParams p{};
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.o = o;
+    p.cu = cu;
+    p.kv_in = kv_in;
+    p.kv_out = kv_out;
+    p.ws = plan.ws_bytes ? reinterpret_cast<float*>(static_cast<char*>(workspace) + plan.ws_states_off) : nullptr;
+    p.flags = plan.ws_bytes ? reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + plan.ws_flags_off) : nullptr;
+    p.T = (int32_t)T;
+    p.num_seqs = num_seqs;
+    p.H = H;
+    p.L = plan.L;
+    p.nseg = plan.nseg;
+    p.S = plan.S;
+    p.scan = plan.scan;
+    p.rev = rev;
+    p.kv_in_t = kv_in_t;
+    p.units = plan.units;
+    p.per_xcd = (plan.units + 7) / 8;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = dtype == LA_BF16 ? la::launch_prefill_bf16(p, d, block, plan.W, plan.variant, s, e0, e1)
+                                    : la::launch_prefill_fp32(p, d, block, plan.W, plan.variant, s, e0, e1);
+    return e == hipSuccess ? LA_OK : LA_ERR_HIP;
+}
+
+}  // namespace
+
 extern "C" {
 
 const char* la_status_string(la_status s) {
@@ -57,31 +93,44 @@ la_status la_prefill_resume(const void* q, const void* k, const void* v, void* o
     la_status st = la::validate_prefill(q, k, v, o, cu_seqlens, H, d, block, kv_state_in, kv_state_out, num_seqs,
                                         total_tokens, (int)dtype, workspace, workspace_bytes, opts, &plan);
     if (st != LA_OK) return st;
-    la::PrefillParams p{};
-    p.q = q;
-    p.k = k;
-    p.v = v;
-    p.o = o;
-    p.cu = cu_seqlens;
-    p.kv_in = kv_state_in;
-    p.kv_out = kv_state_out;
-    p.ws = plan.ws_bytes ? reinterpret_cast<float*>(static_cast<char*>(workspace) + plan.ws_states_off) : nullptr;
-    p.flags = plan.ws_bytes ? reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + plan.ws_flags_off) : nullptr;
-    p.T = (int32_t)total_tokens;
-    p.num_seqs = num_seqs;
-    p.H = H;
-    p.L = plan.L;
-    p.nseg = plan.nseg;
-    p.S = plan.S;
-    p.scan = plan.scan;
-    p.units = plan.units;
-    p.per_xcd = (plan.units + 7) / 8;
-    hipStream_t s = static_cast<hipStream_t>(stream);
     hipEvent_t e0 = opts ? static_cast<hipEvent_t>(opts->main_begin_event) : nullptr;
     hipEvent_t e1 = opts ? static_cast<hipEvent_t>(opts->main_end_event) : nullptr;
-    hipError_t e = dtype == LA_BF16 ? la::launch_prefill_bf16(p, d, block, plan.W, plan.variant, s, e0, e1)
-                                    : la::launch_prefill_fp32(p, d, block, plan.W, plan.variant, s, e0, e1);
-    return e == hipSuccess ? LA_OK : LA_ERR_HIP;
+    return enqueue_prefill(plan, q, k, v, o, cu_seqlens, H, d, block, kv_state_in, 0, kv_state_out, 0, num_seqs,
+                           total_tokens, dtype, workspace, stream, e0, e1);
+}
+
+la_status la_prefill_backward(const void* q, const void* k, const void* v, const void* dout,
+                              const int32_t* cu_seqlens, int32_t H, int32_t d, int32_t block,
+                              const float* kv_state_in, const float* dkv_state_out, void* dq, void* dk, void* dv,
+                              float* dkv_state_in, int32_t num_seqs, int64_t total_tokens, la_dtype dtype,
+                              void* workspace, size_t workspace_bytes, void* stream, const la_prefill_opts* opts) {
+    if (!dout || !dq || !dk || !dv) return LA_ERR_INVALID_ARG;
+    // every pass is a prefill with other operand roles; all are validated before any is enqueued
+    Plan p1, p2, p3;
+    la_status st = la::validate_prefill(dout, v, k, dq, cu_seqlens, H, d, block, kv_state_in, nullptr, num_seqs,
+                                        total_tokens, (int)dtype, workspace, workspace_bytes, opts, &p1);
+    if (st != LA_OK) return st;
+    st = la::validate_prefill(v, dout, q, dk, cu_seqlens, H, d, block, dkv_state_out, nullptr, num_seqs, total_tokens,
+                              (int)dtype, workspace, workspace_bytes, opts, &p2);
+    if (st != LA_OK) return st;
+    st = la::validate_prefill(k, q, dout, dv, cu_seqlens, H, d, block, dkv_state_out, dkv_state_in, num_seqs,
+                              total_tokens, (int)dtype, workspace, workspace_bytes, opts, &p3);
+    if (st != LA_OK) return st;
+    st = la::validate_backward_outputs(q, k, v, dout, kv_state_in, dkv_state_out, dq, dk, dv, dkv_state_in, num_seqs,
+                                       H, d, total_tokens, (int)dtype);
+    if (st != LA_OK) return st;
+    // dQ: forward pass with query dO, key V, value K, from KV_in^T
+    st = enqueue_prefill(p1, dout, v, k, dq, cu_seqlens, H, d, block, kv_state_in, 1, nullptr, 0, num_seqs,
+                         total_tokens, dtype, workspace, stream, nullptr, nullptr);
+    if (st != LA_OK) return st;
+    // dK: reverse pass with query V, key dO, value Q, from dKV_out^T
+    st = enqueue_prefill(p2, v, dout, q, dk, cu_seqlens, H, d, block, dkv_state_out, 1, nullptr, 1, num_seqs,
+                         total_tokens, dtype, workspace, stream, nullptr, nullptr);
+    if (st != LA_OK) return st;
+    // dV (and dKV_in, the reverse state after each document's first token):
+    // reverse pass with query K, key Q, value dO, from dKV_out
+    return enqueue_prefill(p3, k, q, dout, dv, cu_seqlens, H, d, block, dkv_state_out, 0, dkv_state_in, 1, num_seqs,
+                           total_tokens, dtype, workspace, stream, nullptr, nullptr);
 }
 
 la_status la_prefill_ex(const void* q, const void* k, const void* v, void* o, const int32_t* cu_seqlens, int32_t H,

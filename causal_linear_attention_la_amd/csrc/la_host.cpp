@@ -147,6 +147,27 @@ la_status validate_prefill(const void* q, const void* k, const void* v, const vo
     return LA_OK;
 }
 
+la_status validate_backward_outputs(const void* q, const void* k, const void* v, const void* dout, const float* kv_in,
+                                    const float* dkv_out, const void* dq, const void* dk, const void* dv,
+                                    const float* dkv_in, int32_t num_seqs, int32_t H, int32_t d, int64_t T, int dtype) {
+    int64_t n, ns;
+    if (!mul_ok(T, (int64_t)H * d, n) || !mul_ok(n, (int64_t)elem_size(dtype), n)) return LA_ERR_INVALID_ARG;
+    if (!mul_ok(num_seqs, (int64_t)H * d * d, ns) || !mul_ok(ns, 4, ns)) return LA_ERR_INVALID_ARG;
+    const size_t tn = (size_t)n, sn = (size_t)ns;
+    const void* ins[6] = {q, k, v, dout, kv_in, dkv_out};
+    const size_t in_sz[6] = {tn, tn, tn, tn, sn, sn};
+    const void* outs[4] = {dq, dk, dv, dkv_in};
+    const size_t out_sz[4] = {tn, tn, tn, sn};
+    for (int a = 0; a < 4; ++a) {
+        for (int b = 0; b < 6; ++b)
+            if (overlap(outs[a], out_sz[a], ins[b], in_sz[b])) return LA_ERR_INVALID_ARG;
+        for (int b = a + 1; b < 4; ++b)
+            if (overlap(outs[a], out_sz[a], outs[b], out_sz[b])) return LA_ERR_INVALID_ARG;
+    }
+    if (dkv_in && !aligned(dkv_in, 16)) return LA_ERR_INVALID_ARG;
+    return LA_OK;
+}
+
 la_status validate_decode(const void* q, const void* k, const void* v, const float* S, const void* o,
                           int32_t num_seqs, int32_t H, int32_t d, int dtype) {
     if (!q || !k || !v || !S || !o) return LA_ERR_INVALID_ARG;

@@ -36,6 +36,11 @@ la_status validate_prefill(const void* q, const void* k, const void* v, const vo
                            int64_t T, int dtype, const void* ws, size_t ws_bytes, const la_prefill_opts* opts,
                            Plan* plan);
 
+// Backward: outputs (dq, dk, dv, dkv_in) overlap neither an input nor each other.
+la_status validate_backward_outputs(const void* q, const void* k, const void* v, const void* dout, const float* kv_in,
+                                    const float* dkv_out, const void* dq, const void* dk, const void* dv,
+                                    const float* dkv_in, int32_t num_seqs, int32_t H, int32_t d, int64_t T, int dtype);
+
 la_status validate_decode(const void* q, const void* k, const void* v, const float* S, const void* o,
                           int32_t num_seqs, int32_t H, int32_t d, int dtype);
 

@@ -43,13 +43,34 @@ struct PrefillParams {
     int32_t nseg;
     int32_t S;       // value slices per head
     int32_t scan;    // 1: ws holds inclusive per-document states (after the scan kernel)
+    int32_t rev;     // 1: every document is processed from its last token to its first
+    int32_t kv_in_t; // 1: kv_in holds transposed states ([value][key])
     int32_t pad_;
     int64_t units;   // nseg * H * S
     int64_t per_xcd; // ceil(units / 8)
 };
 
+// Document boundaries as the kernels see them.  In reverse mode the packed
+// sequence is read back to front: logical token t is physical token T-1-t,
+// logical document k is physical document n-1-k, and the logical boundaries
+// are T - cu[n - k].  Everything (segments, blocks, the causal mask) then
+// works on logical positions unchanged; only addresses are mirrored.
+struct CuView {
+    const int32_t* cu;
+    int n;
+    int T;
+    int rev;
+    __device__ __forceinline__ int operator[](int k) const { return rev ? T - cu[n - k] : cu[k]; }
+};
+__device__ __forceinline__ CuView cu_view(const PrefillParams& p) { return CuView{p.cu, p.num_seqs, p.T, p.rev}; }
+// Physical document and token of a logical one.
+__device__ __forceinline__ int phys_doc(const PrefillParams& p, int doc) { return p.rev ? p.num_seqs - 1 - doc : doc; }
+__device__ __forceinline__ int phys_tok(const PrefillParams& p, int t) { return p.rev ? p.T - 1 - t : t; }
+// Physical token of the lowest-addressed row of logical block [b0, b0 + nb).
+__device__ __forceinline__ int phys_block(const PrefillParams& p, int b0, int nb) { return p.rev ? p.T - b0 - nb : b0; }
+
 // Largest doc in [0, n-1] with cu[doc] <= t.
-__device__ __forceinline__ int doc_at(const int32_t* cu, int n, int t) {
+__device__ __forceinline__ int doc_at(const CuView& cu, int n, int t) {
     int lo = 0, hi = n - 1;
     while (lo < hi) {
         int mid = (lo + hi + 1) >> 1;
@@ -58,7 +79,7 @@ __device__ __forceinline__ int doc_at(const int32_t* cu, int n, int t) {
     return lo;
 }
 // First doc in [0, n] with cu[doc] >= t.
-__device__ __forceinline__ int doc_lower(const int32_t* cu, int n, int t) {
+__device__ __forceinline__ int doc_lower(const CuView& cu, int n, int t) {
     int lo = 0, hi = n;
     while (lo < hi) {
         int mid = (lo + hi) >> 1;
@@ -91,7 +112,7 @@ struct Cursor {
     int first_of_doc;  // 1 if the block starts its document (an int: the struct stays all-register)
 };
 
-__device__ __forceinline__ void cursor_first(Cursor& c, const int32_t* cu, int n, int t0, int t1, int B) {
+__device__ __forceinline__ void cursor_first(Cursor& c, const CuView& cu, int n, int t0, int t1, int B) {
     c.b0 = t0;
     c.nb = 0;
     c.doc = 0;
@@ -105,7 +126,7 @@ __device__ __forceinline__ void cursor_first(Cursor& c, const int32_t* cu, int n
     c.first_of_doc = (cu[c.doc] == t0) ? 1 : 0;
 }
 
-__device__ __forceinline__ void cursor_next(Cursor& c, const int32_t* cu, int n, int t1, int B) {
+__device__ __forceinline__ void cursor_next(Cursor& c, const CuView& cu, int n, int t1, int B) {
     int nb0 = c.b0 + c.nb;
     int piece_end = min(t1, c.doc_end);
     if (nb0 < piece_end) {
@@ -220,16 +241,17 @@ __global__ __launch_bounds__(kThreads, 2) void la_segment_state_kernel(PrefillPa
     const int tid = threadIdx.x, lane = tid & 63, li = lane & 15, g = lane >> 4;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int t_beg = u * p.L, t_end = (u + 1) * p.L;  // t_end < T here
-    const int de = doc_at(p.cu, p.num_seqs, t_end - 1);
-    const int dstart = p.cu[de];
-    const bool needs = p.cu[de + 1] > t_end;
+    const CuView cu = cu_view(p);
+    const int de = doc_at(cu, p.num_seqs, t_end - 1);
+    const int dstart = cu[de];
+    const bool needs = cu[de + 1] > t_end;
     const bool chain = dstart < t_beg;
     if (h == 0 && s == 0 && tid == 0) p.flags[u] = (needs ? 1 : 0) | (chain ? 2 : 0);
     if (!needs) return;
 
     const TIn* kg = static_cast<const TIn*>(p.k);
     const TIn* vg = static_cast<const TIn*>(p.v);
-    const int64_t ld = (int64_t)p.H * D;
+    const int64_t ld = p.rev ? -(int64_t)p.H * D : (int64_t)p.H * D;  // row step of logical tokens
     f32x4_t kv[KVPW];
 #pragma unroll
     for (int j = 0; j < KVPW; ++j) kv[j] = zero4();
@@ -238,8 +260,8 @@ __global__ __launch_bounds__(kThreads, 2) void la_segment_state_kernel(PrefillPa
     TileRegs<TIn, B, W> lv;
     int b0 = max(t_beg, dstart);
     int nb = min(B, t_end - b0);
-    lk.load(kg + ((int64_t)b0 * p.H + h) * D, ld, nb, tid);
-    lv.load(vg + ((int64_t)b0 * p.H + h) * D + s * W, ld, nb, tid);
+    lk.load(kg + ((int64_t)phys_tok(p, b0) * p.H + h) * D, ld, nb, tid);
+    lv.load(vg + ((int64_t)phys_tok(p, b0) * p.H + h) * D + s * W, ld, nb, tid);
     while (nb > 0) {
         __syncthreads();
         lk.store_cols(Kt, TP, tid);
@@ -247,8 +269,8 @@ __global__ __launch_bounds__(kThreads, 2) void la_segment_state_kernel(PrefillPa
         const int nb0 = b0 + nb;
         const int nnb = min(B, t_end - nb0);
         if (nnb > 0) {
-            lk.load(kg + ((int64_t)nb0 * p.H + h) * D, ld, nnb, tid);
-            lv.load(vg + ((int64_t)nb0 * p.H + h) * D + s * W, ld, nnb, tid);
+            lk.load(kg + ((int64_t)phys_tok(p, nb0) * p.H + h) * D, ld, nnb, tid);
+            lv.load(vg + ((int64_t)phys_tok(p, nb0) * p.H + h) * D + s * W, ld, nnb, tid);
         }
         __syncthreads();
         state_update<TIn, D, B, W, KVPW>(kv, Kt, Vt, wave, li, g);
@@ -305,16 +327,17 @@ __global__ __launch_bounds__(kThreads) void la_segment_scan_kernel(float* __rest
 template <int D, int W>
 __device__ __forceinline__ void empty_doc_states(const PrefillParams& p, int u, int h, int s, int t0, int t1,
                                                  int tid) {
-    const int lo = doc_lower(p.cu, p.num_seqs, t0);
-    const int hi = (u == p.nseg - 1) ? p.num_seqs : doc_lower(p.cu, p.num_seqs, t1);
+    const CuView cu = cu_view(p);
+    const int lo = doc_lower(cu, p.num_seqs, t0);
+    const int hi = (u == p.nseg - 1) ? p.num_seqs : doc_lower(cu, p.num_seqs, t1);
     for (int d = lo; d < hi; ++d) {
-        if (p.cu[d + 1] != p.cu[d]) continue;
-        const int64_t base = (((int64_t)d * p.H + h) * D) * D + s * W;
+        if (cu[d + 1] != cu[d]) continue;
+        const int64_t base = (((int64_t)phys_doc(p, d) * p.H + h) * D) * D;
         float* dst = p.kv_out + base;
         const float* src = p.kv_in ? p.kv_in + base : nullptr;
         for (int i = tid; i < D * W; i += kThreads) {
-            const int64_t e = (int64_t)(i / W) * D + (i % W);
-            dst[e] = src ? src[e] : 0.f;
+            const int r = i / W, c = s * W + i % W;  // key row, value column
+            dst[(int64_t)r * D + c] = src ? (p.kv_in_t ? src[(int64_t)c * D + r] : src[(int64_t)r * D + c]) : 0.f;
         }
     }
 }
@@ -356,7 +379,8 @@ __global__ __launch_bounds__(kThreads, 1) void la_prefill_main_kernel(PrefillPar
     const TIn* kg = static_cast<const TIn*>(p.k);
     const TIn* vg = static_cast<const TIn*>(p.v);
     TIn* og = static_cast<TIn*>(p.o);
-    const int64_t ld = (int64_t)p.H * D;
+    const int64_t ld = p.rev ? -(int64_t)p.H * D : (int64_t)p.H * D;  // row step of logical tokens
+    const CuView cuv = cu_view(p);
 
     // Zero LDS once: pad columns (d >= D) of Qs and KVt must stay finite zeros.
     {
@@ -366,14 +390,14 @@ __global__ __launch_bounds__(kThreads, 1) void la_prefill_main_kernel(PrefillPar
     }
 
     Cursor cur;
-    cursor_first(cur, p.cu, p.num_seqs, t0, t1, B);
+    cursor_first(cur, cuv, p.num_seqs, t0, t1, B);
 
     // Initial state: zero, or the document's state at the segment start.
     f32x4_t kv[KVPW];
 #pragma unroll
     for (int j = 0; j < KVPW; ++j) kv[j] = zero4();
     if (cur.nb > 0 && !cur.first_of_doc) {
-        const int u_first = p.scan ? u - 1 : p.cu[cur.doc] / p.L;
+        const int u_first = p.scan ? u - 1 : cuv[cur.doc] / p.L;
         for (int uu = u_first; uu < u; ++uu) {
             const float* src = p.ws + (((int64_t)uu * p.H + h) * D) * D + s * W;
 #pragma unroll
@@ -389,14 +413,18 @@ __global__ __launch_bounds__(kThreads, 1) void la_prefill_main_kernel(PrefillPar
     }
     // A caller-supplied state before the document's first token joins the prefix.
     auto add_kv_in = [&](int doc) {
-        const float* src = p.kv_in + (((int64_t)doc * p.H + h) * D) * D + s * W;
+        const float* src = p.kv_in + (((int64_t)phys_doc(p, doc) * p.H + h) * D) * D;
 #pragma unroll
         for (int j = 0; j < KVPW; ++j) {
             const int t = wave + kWaves * j;
             if (t < NKV) {
                 const int a = t / NCT, c = t % NCT;
+                const int col = s * W + 16 * c + li;
 #pragma unroll
-                for (int r = 0; r < 4; ++r) kv[j][r] += src[(int64_t)(16 * a + 4 * g + r) * D + 16 * c + li];
+                for (int r = 0; r < 4; ++r) {
+                    const int row = 16 * a + 4 * g + r;
+                    kv[j][r] += p.kv_in_t ? src[(int64_t)col * D + row] : src[(int64_t)row * D + col];
+                }
             }
         }
     };
@@ -414,7 +442,7 @@ __global__ __launch_bounds__(kThreads, 1) void la_prefill_main_kernel(PrefillPar
     TileRegs<TIn, B, D> lq, lk;
     TileRegs<TIn, B, W> lv;
     if (cur.nb > 0) {
-        const int64_t row0 = (int64_t)cur.b0 * p.H + h;
+        const int64_t row0 = (int64_t)phys_tok(p, cur.b0) * p.H + h;
         lq.load(qg + row0 * D, ld, cur.nb, tid);
         lk.load(kg + row0 * D, ld, cur.nb, tid);
         lv.load(vg + row0 * D + s * W, ld, cur.nb, tid);
@@ -433,9 +461,9 @@ __global__ __launch_bounds__(kThreads, 1) void la_prefill_main_kernel(PrefillPar
         lk.store_cols(Kt, TP, tid);
         lv.store_cols(Vt, TP, tid);
         Cursor nxt = cur;
-        cursor_next(nxt, p.cu, p.num_seqs, t1, B);
+        cursor_next(nxt, cuv, p.num_seqs, t1, B);
         if (nxt.nb > 0) {
-            const int64_t row0 = (int64_t)nxt.b0 * p.H + h;
+            const int64_t row0 = (int64_t)phys_tok(p, nxt.b0) * p.H + h;
             lq.load(qg + row0 * D, ld, nxt.nb, tid);
             lk.load(kg + row0 * D, ld, nxt.nb, tid);
             lv.load(vg + row0 * D + s * W, ld, nxt.nb, tid);
@@ -503,7 +531,7 @@ __global__ __launch_bounds__(kThreads, 1) void la_prefill_main_kernel(PrefillPar
         // Coalesced store of the block's output rows.
         {
             constexpr int OCPR = W / CE;
-            TIn* obase = og + ((int64_t)cur.b0 * p.H + h) * D + s * W;
+            TIn* obase = og + ((int64_t)phys_tok(p, cur.b0) * p.H + h) * D + s * W;
             for (int i = tid; i < cur.nb * OCPR; i += kThreads) {
                 const int row = i / OCPR, c = i % OCPR;
                 *reinterpret_cast<uint4*>(obase + (int64_t)row * ld + c * CE) =
@@ -511,7 +539,7 @@ __global__ __launch_bounds__(kThreads, 1) void la_prefill_main_kernel(PrefillPar
             }
         }
         if (cur.b0 + cur.nb == cur.doc_end && p.kv_out) {
-            float* dst = p.kv_out + (((int64_t)cur.doc * p.H + h) * D) * D + s * W;
+            float* dst = p.kv_out + (((int64_t)phys_doc(p, cur.doc) * p.H + h) * D) * D + s * W;
 #pragma unroll
             for (int j = 0; j < KVPW; ++j) {
                 const int t = wave + kWaves * j;

@@ -145,7 +145,8 @@ struct DmaTile {
     static constexpr int CPR = ROWB / 16;  // chunks per row
     static constexpr int RPI = 64 / CPR;   // rows per instruction
     static constexpr int NI = 16 / RPI;    // instructions per wave and block
-    uint32_t voff[NI];
+    uint32_t voff[NI];   // row * row_bytes + chunk * 16
+    uint32_t coff2[NI];  // 2 * chunk * 16
     int row0;
 
     __device__ __forceinline__ void init(int wave, int lane, uint32_t row_bytes) {
@@ -155,13 +156,21 @@ struct DmaTile {
             const int row = row0 + RPI * i + lane / CPR;
             const int chunk = (lane % CPR) ^ (hmask<COLS>(row) >> 1);
             voff[i] = (uint32_t)row * row_bytes + (uint32_t)chunk * 16u;
+            coff2[i] = (uint32_t)chunk * 32u;
         }
     }
-    __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t rsrc, bf16_t* tile) const {
+    // Tile row r takes the buffer's row r, or, in reverse mode, its row
+    // nb - 1 - r (the descriptor then starts at the block's lowest physical
+    // row): rows past nb wrap to huge offsets and read as zeros either way.
+    // last_row_off = (nb - 1) * row_bytes.
+    __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t rsrc, bf16_t* tile, bool rev = false,
+                                          uint32_t last_row_off = 0) const {
 #pragma unroll
-        for (int i = 0; i < NI; ++i)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)(tile + (row0 + RPI * i) * COLS), 16, voff[i],
-                                                     0, 0, 0);
+        for (int i = 0; i < NI; ++i) {
+            const uint32_t off = rev ? last_row_off + coff2[i] - voff[i] : voff[i];
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)(tile + (row0 + RPI * i) * COLS), 16, off, 0,
+                                                     0, 0);
+        }
     }
 };
 
@@ -241,9 +250,12 @@ __device__ __forceinline__ int64_t ws_offset(const PrefillParams& p, int u, int 
     return (((int64_t)u * p.H + h) * D) * D + (int64_t)s * D * W + (int64_t)wave * (D * W / 4);
 }
 
-// Adds a state stored in the documented [key][value] layout (kv_in).
+// Adds a state stored in the documented [key][value] layout (kv_in) -- or,
+// with `transposed`, stored [value][key].  base = the (document, head)
+// matrix, col0 = the first value column this wave owns.
 template <int D, int B, int W, int NA, int NC>
-__device__ __forceinline__ void add_state(f32x4_t (&kv)[NA][NC], const float* src, int g, int li) {
+__device__ __forceinline__ void add_state(f32x4_t (&kv)[NA][NC], const float* base, int col0, int transposed, int g,
+                                          int li) {
     using G = Geo<D, B, W>;
     static_assert(NA == G::NDT && NC == G::NCW, "tile counts");
 #pragma unroll
@@ -251,7 +263,10 @@ __device__ __forceinline__ void add_state(f32x4_t (&kv)[NA][NC], const float* sr
 #pragma unroll
         for (int c = 0; c < G::NCW; ++c)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) kv[a][c][r] += src[(int64_t)state_row(a, g, r) * D + state_col<NC>(c, li)];
+            for (int r = 0; r < 4; ++r) {
+                const int64_t i = state_row(a, g, r), j = col0 + state_col<NC>(c, li);
+                kv[a][c][r] += transposed ? base[j * D + i] : base[i * D + j];
+            }
 }
 
 template <int D, int B, int W, int NA, int NC>
@@ -287,9 +302,10 @@ __global__ __launch_bounds__(kThreads, 1) void la_segment_state_v2(PrefillParams
     // values loaded from cu are the same in every lane: readfirstlane makes
     // that visible to the compiler, which then keeps the buffer descriptors
     // built from them in scalar registers (no per-lane waterfall loops)
-    const int de = __builtin_amdgcn_readfirstlane(doc_at(p.cu, p.num_seqs, t_end - 1));
-    const int dstart = __builtin_amdgcn_readfirstlane(p.cu[de]);
-    const bool needs = __builtin_amdgcn_readfirstlane(p.cu[de + 1]) > t_end;
+    const CuView cu = cu_view(p);
+    const int de = __builtin_amdgcn_readfirstlane(doc_at(cu, p.num_seqs, t_end - 1));
+    const int dstart = __builtin_amdgcn_readfirstlane(cu[de]);
+    const bool needs = __builtin_amdgcn_readfirstlane(cu[de + 1]) > t_end;
     const bool chain = dstart < t_beg;
     if (h == 0 && s == 0 && tid == 0) p.flags[u] = (needs ? 1 : 0) | (chain ? 2 : 0);
     if (!needs) return;
@@ -321,9 +337,10 @@ __global__ __launch_bounds__(kThreads, 1) void la_segment_state_v2(PrefillParams
             // (clamp kept scalar: the descriptor built from it must live in
             // scalar registers)
             const int nb = __builtin_amdgcn_readfirstlane(max(0, min(B, t_end - b0)));
-            const int64_t e0 = ((int64_t)min(b0, t_end) * p.H + h) * D;
-            dk.issue(make_rsrc(kg + e0, (uint32_t)nb * row_bytes), kbuf(slot) + half * B * D);
-            dv.issue(make_rsrc(vg + e0 + s * W, (uint32_t)nb * row_bytes), vbuf(slot) + half * B * W);
+            const int64_t e0 = ((int64_t)phys_block(p, min(b0, t_end), nb) * p.H + h) * D;
+            const uint32_t last = (uint32_t)(nb - 1) * row_bytes;
+            dk.issue(make_rsrc(kg + e0, (uint32_t)nb * row_bytes), kbuf(slot) + half * B * D, p.rev, last);
+            dv.issue(make_rsrc(vg + e0 + s * W, (uint32_t)nb * row_bytes), vbuf(slot) + half * B * W, p.rev, last);
         }
     };
     const int npairs = (nblk + 1) / 2;
@@ -384,8 +401,9 @@ __global__ __launch_bounds__(kThreads, 1) void la_prefill_main_v2(PrefillParams 
     dq.init(wave, lane, row_bytes);
     dv.init(wave, lane, row_bytes);
 
+    const CuView cuv = cu_view(p);
     Cursor c0;
-    cursor_first(c0, p.cu, p.num_seqs, t0, t1, B);
+    cursor_first(c0, cuv, p.num_seqs, t0, t1, B);
 
     f32x4_t kv[NDT][NCW];
 #pragma unroll
@@ -408,11 +426,13 @@ __global__ __launch_bounds__(kThreads, 1) void la_prefill_main_v2(PrefillParams 
     // them while the wave computes instead of stalling every wave at once.
     auto issue_tile = [&](const Cursor& c, auto slot, auto tile) {
         constexpr int TILE = decltype(tile)::value;
-        const int64_t e0 = ((int64_t)c.b0 * p.H + h) * D;
-        const uint32_t bytes = (uint32_t)max(c.nb, 0) * row_bytes;
-        if constexpr (TILE == 0) dq.issue(make_rsrc(qg + e0, bytes), qbuf(slot));
-        else if constexpr (TILE == 1) dq.issue(make_rsrc(kg + e0, bytes), kbuf(slot));
-        else dv.issue(make_rsrc(vg + e0 + s * W, bytes), vbuf(slot));
+        const int nb = max(c.nb, 0);
+        const int64_t e0 = ((int64_t)(nb > 0 ? phys_block(p, c.b0, nb) : 0) * p.H + h) * D;
+        const uint32_t bytes = (uint32_t)nb * row_bytes;
+        const uint32_t last = (uint32_t)(nb - 1) * row_bytes;
+        if constexpr (TILE == 0) dq.issue(make_rsrc(qg + e0, bytes), qbuf(slot), p.rev, last);
+        else if constexpr (TILE == 1) dq.issue(make_rsrc(kg + e0, bytes), kbuf(slot), p.rev, last);
+        else dv.issue(make_rsrc(vg + e0 + s * W, bytes), vbuf(slot), p.rev, last);
     };
     auto issue = [&](const Cursor& c, auto slot) {
         issue_tile(c, slot, Slot<0>{});
@@ -432,7 +452,13 @@ __global__ __launch_bounds__(kThreads, 1) void la_prefill_main_v2(PrefillParams 
             }
         }
         const __amdgpu_buffer_rsrc_t ro =
-            make_rsrc(og + ((int64_t)pb0 * p.H + h) * D + s * W + col0, (uint32_t)pnb * row_bytes);
+            make_rsrc(og + ((int64_t)phys_block(p, pb0, pnb) * p.H + h) * D + s * W + col0, (uint32_t)pnb * row_bytes);
+        // output row 16b + li of the block; in reverse mode its mirror pnb - 1 - (16b + li)
+        // (negative -> a huge unsigned offset -> dropped by the range check)
+        auto orow = [&](int b) -> uint32_t {
+            const int r = 16 * b + li;
+            return (uint32_t)(p.rev ? pnb - 1 - r : r) * row_bytes;
+        };
 #pragma unroll
         for (int b = 0; b < NQT; ++b) {
             if constexpr (NCW == 2) {  // columns 8g..8g+7 of row 16b + li: one 16-byte store
@@ -441,14 +467,14 @@ __global__ __launch_bounds__(kThreads, 1) void la_prefill_main_v2(PrefillParams 
                 v.y = pack2(oacc[b][0][2], oacc[b][0][3]);
                 v.z = pack2(oacc[b][1][0], oacc[b][1][1]);
                 v.w = pack2(oacc[b][1][2], oacc[b][1][3]);
-                __builtin_amdgcn_raw_buffer_store_b128(v, ro, (16 * b + li) * row_bytes + (8 * g) * 2, 0, 0);
+                __builtin_amdgcn_raw_buffer_store_b128(v, ro, orow(b) + (8 * g) * 2, 0, 0);
             } else {
 #pragma unroll
                 for (int c = 0; c < NCW; ++c) {
                     u32x2_t v;
                     v.x = pack2(oacc[b][c][0], oacc[b][c][1]);
                     v.y = pack2(oacc[b][c][2], oacc[b][c][3]);
-                    __builtin_amdgcn_raw_buffer_store_b64(v, ro, (16 * b + li) * row_bytes + (16 * c + 4 * g) * 2, 0, 0);
+                    __builtin_amdgcn_raw_buffer_store_b64(v, ro, orow(b) + (16 * c + 4 * g) * 2, 0, 0);
                 }
             }
 #pragma unroll
@@ -458,20 +484,21 @@ __global__ __launch_bounds__(kThreads, 1) void la_prefill_main_v2(PrefillParams 
 
     if (c0.nb > 0) issue(c0, Slot<0>{});  // before the prefix loads, so the two overlap
     if (c0.nb > 0 && !c0.first_of_doc) {
-        const int u_first = p.scan ? u - 1 : p.cu[c0.doc] / p.L;
+        const int u_first = p.scan ? u - 1 : cuv[c0.doc] / p.L;
         for (int uu = u_first; uu < u; ++uu)
             load_ws<D, B, W>(kv, p.ws + ws_offset<D, W>(p, uu, h, s, wave), lane);
     }
     // a caller-supplied state before the document's first token joins the prefix
     if (p.kv_in && c0.nb > 0)
-        add_state<D, B, W>(kv, p.kv_in + (((int64_t)c0.doc * p.H + h) * D) * D + s * W + col0, g, li);
+        add_state<D, B, W>(kv, p.kv_in + (((int64_t)phys_doc(p, c0.doc) * p.H + h) * D) * D, s * W + col0, p.kv_in_t,
+                           g, li);
     int pb0 = t0, pnb = 0;
     int j = 0;
     // One block; its tiles sit in slot SLOT, the next block's go to the other.
     auto step = [&](auto slot) {
         constexpr int SLOT = decltype(slot)::value;
         Cursor c1 = c0;
-        cursor_next(c1, p.cu, p.num_seqs, t1, B);
+        cursor_next(c1, cuv, p.num_seqs, t1, B);
         // Loads of block j (issued during the previous iteration, the last
         // tile after its stores) are all done: nothing younger is in flight.
         vm_wait<0>();
@@ -529,13 +556,15 @@ __global__ __launch_bounds__(kThreads, 1) void la_prefill_main_v2(PrefillParams 
         if (c0.b0 + c0.nb == c0.doc_end) {  // the document ends with this block
             vm_wait<0>();  // rare path: keeps the loop's wait bookkeeping exact
             if (p.kv_out)
-                store_state<D, B, W>(kv, p.kv_out + (((int64_t)c0.doc * p.H + h) * D) * D + s * W + col0, g, li);
+                store_state<D, B, W>(kv, p.kv_out + (((int64_t)phys_doc(p, c0.doc) * p.H + h) * D) * D + s * W + col0,
+                                     g, li);
 #pragma unroll
             for (int a = 0; a < NDT; ++a)
 #pragma unroll
                 for (int c = 0; c < NCW; ++c) kv[a][c] = zero4();
             if (p.kv_in && c1.nb > 0 && c1.first_of_doc) {  // the next document starts here
-                add_state<D, B, W>(kv, p.kv_in + (((int64_t)c1.doc * p.H + h) * D) * D + s * W + col0, g, li);
+                add_state<D, B, W>(kv, p.kv_in + (((int64_t)phys_doc(p, c1.doc) * p.H + h) * D) * D, s * W + col0,
+                                   p.kv_in_t, g, li);
                 vm_wait<0>();
             }
         }

@@ -178,6 +178,35 @@ la_status la_prefill_resume(const void* q, const void* k, const void* v, void* o
                             int32_t num_seqs, int64_t total_tokens, la_dtype dtype, void* workspace,
                             size_t workspace_bytes, void* stream, const la_prefill_opts* opts);
 
+/* Backward of la_prefill_resume: the gradients of a loss L with respect to
+ * q, k, v and kv_state_in, given dL/do (dout) and dL/dkv_state_out.  The
+ * pages give no backward (they train at long context with LASP+,
+ * "MiniMax-01技术报告解读" §3.2 item 3); it is the chain rule applied to the
+ * definition, per document and head, with S_t = KV_in + sum_{s <= t} k_s^T v_s:
+ *     dq_t   = S_t dO_t                                  (a forward pass)
+ *     G_s    = dKV_out + sum_{t >= s} q_t^T dO_t         (a reverse state)
+ *     dk_s   = G_s v_s ,   dv_s = k_s G_s ,   dKV_in = G at the first token
+ * computed as three passes of the prefill kernels: dq forward with query dO,
+ * key v, value k, starting from KV_in^T; dk and dv with every document read
+ * from its last token to its first (query v / key dO / value q from dKV_out^T,
+ * and query k / key q / value dO from dKV_out).
+ *
+ *   q, k, v, dout      [T, H, d] dtype, device, 16-byte aligned, read only.
+ *   kv_state_in        the forward's incoming states or NULL (zero).
+ *   dkv_state_out      [num_seqs, H, d, d] fp32 gradient of the final states, or NULL (zero).
+ *   dq, dk, dv         [T, H, d] dtype, device, 16-byte aligned, fully overwritten.
+ *   dkv_state_in       [num_seqs, H, d, d] fp32 or NULL: gradient of kv_state_in.
+ *   Outputs overlap neither an input nor each other.  The workspace is that of
+ *   la_prefill_workspace_size_ex for the same shapes and opts (one buffer
+ *   serves the three passes, which run in order on `stream`).  Shapes, dtypes,
+ *   blocks and tuning options as in la_prefill_ex; opts' events are ignored.
+ */
+la_status la_prefill_backward(const void* q, const void* k, const void* v, const void* dout,
+                              const int32_t* cu_seqlens, int32_t H, int32_t d, int32_t block,
+                              const float* kv_state_in, const float* dkv_state_out, void* dq, void* dk, void* dv,
+                              float* dkv_state_in, int32_t num_seqs, int64_t total_tokens, la_dtype dtype,
+                              void* workspace, size_t workspace_bytes, void* stream, const la_prefill_opts* opts);
+
 #ifdef __cplusplus
 }
 #endif

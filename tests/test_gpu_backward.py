@@ -1,0 +1,106 @@
+"""GPU parity of la_prefill_backward against the fp64 oracle's backward
+(which is pinned to finite differences of the forward).
+
+Cases: ragged packed documents (empty ones included) with and without
+incoming states and final-state gradients, on both block loops (bf16 d = 128
+and 64 on the gfx950 loop, bf16 block 32 and fp32 on the generic loop), with
+segment splitting and the scan path (which in the reverse passes run over
+documents read back to front), and the 8192-token x 8-head workload in full."""
+import numpy as np
+import pytest
+
+import causal_linear_attention_la_amd as la
+import la_inputs
+import oracle
+from gpu_helpers import ErrAcc, log, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    la.load()
+    la_inputs.build()
+    oracle.build()
+    yield
+
+
+def inputs(seed, T, H, d, dtype):
+    scale = 1.0 / np.sqrt(d)
+    q, k, v = (la_inputs.normal(seed, i, (T, H, d), dtype, scale) for i in range(3))
+    dout = la_inputs.normal(seed, 8, (T, H, d), dtype, 1.0)
+    return q, k, v, dout
+
+
+def states(seed, tid, D, H, d, scale):
+    return np.ascontiguousarray(la_inputs.normal(seed, tid, (D, H, d, d), "fp32", scale), dtype=np.float32)
+
+
+def run(q, k, v, dout, cu, block, kv_in, dkv_out, **opts):
+    import torch
+
+    dq, dk, dv, dki = la.backward(to_dev(q), to_dev(k), to_dev(v), to_dev(dout), to_dev(np.asarray(cu, np.int32)),
+                                  block=block, kv_state_in=None if kv_in is None else to_dev(kv_in),
+                                  dkv_state_out=None if dkv_out is None else to_dev(dkv_out), **opts)
+    torch.cuda.synchronize()
+    return to_host(dq), to_host(dk), to_host(dv), to_host(dki)
+
+
+def check(q, k, v, dout, cu, kv_in, dkv_out, got, fp32, what):
+    ref = oracle.backward(q, k, v, dout, cu, kv_in=kv_in, dkv_out=dkv_out)
+    for name, g, r in zip(("dq", "dk", "dv"), got[:3], ref[:3]):
+        ErrAcc().add(g, r).check(fp32, f"{what} {name}")
+    # dkv_in is a sum of fp32 outer products: held to the fp32 bound
+    ErrAcc().add(got[3], ref[3]).check(True, f"{what} dkv_in")
+
+
+CASES = [(d, block, dtype, opts, with_states)
+         for d, block, dtype in ((128, 64, "bf16"), (64, 64, "bf16"), (128, 32, "bf16"), (32, 64, "fp32"))
+         for opts in (dict(), dict(seg_len=2 * block, value_slices=2), dict(seg_len=block, force_scan=True))
+         for with_states in (False, True)]
+
+
+@pytest.mark.parametrize("d,block,dtype,opts,with_states", CASES,
+                         ids=[f"d{c[0]}-b{c[1]}-{c[2]}-{c[3]}-{'states' if c[4] else 'zero'}" for c in CASES])
+def test_backward_against_oracle(d, block, dtype, opts, with_states):
+    lens = [300, 0, 1, 700, 64, 0, 129]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    T, H = int(cu[-1]), 3
+    q, k, v, dout = inputs(111 + d, T, H, d, dtype)
+    kv_in = states(112 + d, 7, len(lens), H, d, float(np.sqrt(2000)) / d) if with_states else None
+    dkv_out = states(113 + d, 9, len(lens), H, d, 1.0) if with_states else None
+    log(f"  backward d={d} block={block} {dtype} {opts} states={with_states}")
+    got = run(q, k, v, dout, cu, block, kv_in, dkv_out, **opts)
+    check(q, k, v, dout, cu, kv_in, dkv_out, got, dtype == "fp32", "backward")
+    if with_states:
+        # an empty document passes its final-state gradient straight to its incoming state
+        for i, n in enumerate(lens):
+            if n == 0:
+                assert np.array_equal(got[3][i], dkv_out[i])
+
+
+def test_backward_prefill_8k_workload():
+    w = la_inputs.prefill_inputs("prefill_8k")
+    T, H, d = w["T"], w["H"], w["d"]
+    dout = la_inputs.normal(la_inputs.WORKLOADS["prefill_8k"]["seed"], 8, (T, H, d), "bf16", 1.0)
+    log(f"  backward prefill_8k T={T} H={H}")
+    got = run(w["q"], w["k"], w["v"], dout, w["cu"], w["block"], None, None)
+    check(w["q"], w["k"], w["v"], dout, w["cu"], None, None, got, False, "backward 8k")
+
+
+def test_backward_rejects_aliasing():
+    import torch
+
+    T, H, d = 128, 2, 64
+    q, k, v, dout = (to_dev(x) for x in inputs(121, T, H, d, "bf16"))
+    cu = to_dev(np.array([0, T], np.int32))
+    with pytest.raises(la.LAError):
+        la_dq = q  # gradient written over an input
+        st = la.la_prefill_backward(la._ptr(q), la._ptr(k), la._ptr(v), la._ptr(dout), la._ptr(cu), H, d, 64, None,
+                                    None, la._ptr(la_dq), la._ptr(torch.empty_like(q)), la._ptr(torch.empty_like(q)),
+                                    None, 1, T, la.LA_BF16, None, 0, None, None)
+        if st != la.LA_OK:
+            raise la.LAError(st, "la_prefill_backward")
