@@ -10,7 +10,8 @@ block loop).  The default workload is the 8-head x 8192-token bf16 prefill
 copied to HBM before timing, and rotated over several input sets so that the
 timed steps read HBM rather than the 256 MB last-level cache.  The decode
 workload (256 sequences x 64 heads, fp32 state, 1000 steps) is timed in the
-same run and reported under "decode".
+same run and reported under "decode", and the prefill's backward
+(la_prefill_backward: dq, dk, dv) over the same workload under "backward".
 
 Prints one JSON line.  `roofline` is for the block-loop kernel: algorithmic
 bytes (q, k, v read + o written, 8 d bytes per token-head) per launch over its
@@ -145,6 +146,7 @@ def bench_prefill(args, la, torch, hip):
         sh = i % max(T, 1)
         q, k, v = (torch.roll(x, sh, 0).contiguous() if sh else x for x in (q0, k0, v0))
         sets.append((q, k, v, torch.empty_like(q)))
+    w["dev_sets"] = sets
     cu = torch.from_numpy(w["cu"]).cuda()
     kv = torch.empty((num_seqs, H, d, d), dtype=torch.float32, device="cuda")
     ws_bytes = plan["workspace_bytes"]
@@ -270,6 +272,61 @@ def bench_decode(args, la, torch, hip):
                          "kernel_sources_sha": sources_sha(DECODE_SOURCES)}}
 
 
+def bench_backward(args, la, torch, hip, w, dev_sets):
+    """la_prefill_backward over the same workload: dq, dk, dv from dO with no
+    incoming state and no final-state gradient.  Algorithmic bytes per call:
+    q, k, v, dO read and dq, dk, dv written once, 14 d bytes per token-head
+    in bf16.  Timed with HIP events on the launch stream around all calls."""
+    import la_inputs
+
+    T, H, d = w["T"], w["H"], w["d"]
+    esz = 2 if w["dtype"] == "bf16" else 4
+    block = args.block or w["block"]
+    opts = dict(seg_len=args.seg_len, value_slices=args.slices, force_scan=args.force_scan)
+    cu = torch.from_numpy(w["cu"]).cuda()
+    d0 = la_inputs.normal(la_inputs.WORKLOADS[w["name"]]["seed"], 8, (T, H, d), w["dtype"], 1.0)
+    dout0 = torch.from_numpy(d0.view(np.int16)).view(torch.bfloat16).cuda() if d0.dtype == np.uint16 \
+        else torch.from_numpy(d0).cuda()
+    sets = []
+    for i, (q, k, v, _) in enumerate(dev_sets):
+        dout = torch.roll(dout0, i, 0).contiguous() if i else dout0
+        sets.append((q, k, v, dout))
+    outs = (torch.empty_like(dout0), torch.empty_like(dout0), torch.empty_like(dout0), None)
+    num_seqs = len(w["cu"]) - 1
+    dt = la.LA_BF16 if w["dtype"] == "bf16" else la.LA_FP32
+    need = la.la_prefill_workspace_size_ex(T, num_seqs, H, d, block, dt, la.make_opts(**opts))
+    ws = torch.empty(max(need, 256), dtype=torch.uint8, device="cuda")
+
+    def call(i):
+        q, k, v, dout = sets[i % len(sets)]
+        la.backward(q, k, v, dout, cu, block=block, want_dkv_in=False, workspace=ws, out=outs, **opts)
+
+    for i in range(max(1, args.warmup // 4)):
+        call(i)
+    torch.cuda.synchronize()
+    K = max(1, args.steps // 4)
+    stream = torch.cuda.current_stream().cuda_stream
+    e0, e1 = hip.event(), hip.event()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    hip.record(e0, stream)
+    for i in range(K):
+        call(i)
+    hip.record(e1, stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_s = hip.elapsed_ms(e0, e1) / 1e3
+    hip.destroy(e0)
+    hip.destroy(e1)
+    algo = T * H * 14 * d * esz // 2
+    achieved = algo * K / gpu_s / 1e9
+    return {"workload": w["name"], "value": T * H * K / wall, "unit": "token·heads/s", "steps": K,
+            "ms_per_step": wall / K * 1e3, "gpu_ms_per_step": gpu_s / K * 1e3,
+            "roofline": {"bound": "hbm", "kernel": "la_prefill_backward (3 prefill passes)", "achieved": achieved,
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                         "algorithmic_bytes": algo}}
+
+
 def profile_pass(args, la, torch):
     """Short run for rocprofv3 counter passes: a 256 MiB device copy (the
     calibration kernel) then a few prefill steps of the workload."""
@@ -303,6 +360,7 @@ def main():
     ap.add_argument("--rotate", type=int, default=8, help="input sets cycled through the timed steps")
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--profile-pass", action="store_true")
@@ -325,6 +383,10 @@ def main():
         return
     hip = Hip()
     rec, w = bench_prefill(args, la, torch, hip)
+    if not args.no_backward:
+        rec["backward"] = bench_backward(args, la, torch, hip, w, w.pop("dev_sets"))
+    else:
+        w.pop("dev_sets")
     if not args.no_decode:
         rec["decode"] = bench_decode(args, la, torch, hip)
     if not args.no_cpu_baseline:

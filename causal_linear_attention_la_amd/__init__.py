@@ -214,17 +214,22 @@ def prefill(q, k, v, cu_seqlens, block: int = 64, want_state: bool = True, out=N
 
 def backward(q, k, v, dout, cu_seqlens, block: int = 64, kv_state_in=None, dkv_state_out=None,
              want_dkv_in: bool = True, workspace=None, seg_len: int = 0, value_slices: int = 0,
-             force_scan: bool = False, stream=None, variant: int = 0):
+             force_scan: bool = False, stream=None, variant: int = 0, out=None):
     """Gradients of the prefill (la_prefill_backward).  dout is dL/do
     ([T, H, d], same dtype as q); dkv_state_out (fp32 [num_seqs, H, d, d] or
-    None) is dL/dkv_state_out.  Returns (dq, dk, dv, dkv_state_in or None)."""
+    None) is dL/dkv_state_out.  out = (dq, dk, dv, dkv_in) preallocated
+    (dkv_in may be None), else they are allocated.  Returns (dq, dk, dv,
+    dkv_state_in or None)."""
     import torch
 
     T, H, d = q.shape
     dt = _dtype_code(q)
     num_seqs = cu_seqlens.numel() - 1
-    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
-    dkv_in = torch.empty((num_seqs, H, d, d), dtype=torch.float32, device=q.device) if want_dkv_in else None
+    if out is not None:
+        dq, dk, dv, dkv_in = out
+    else:
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+        dkv_in = torch.empty((num_seqs, H, d, d), dtype=torch.float32, device=q.device) if want_dkv_in else None
     opts = make_opts(seg_len, value_slices, force_scan, None, None, variant)
     need = la_prefill_workspace_size_ex(T, num_seqs, H, d, block, dt, opts)
     ws = workspace
