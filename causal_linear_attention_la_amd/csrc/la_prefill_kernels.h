@@ -294,12 +294,12 @@ __global__ __launch_bounds__(kThreads, 2) void la_segment_state_kernel(PrefillPa
 // ws[u] is the state of segment u's last document at the end of segment u.
 // One thread per 4 consecutive state entries (h, i, j..j+3); the segments are
 // taken CH at a time: CH independent 16-byte loads in flight, then the
-// running sums and CH stores.
-template <int CH>
-__global__ __launch_bounds__(kThreads) void la_segment_scan_kernel(float* __restrict__ ws,
-                                                                   const int32_t* __restrict__ flags, int nseg,
-                                                                   int64_t entries) {
-    const int64_t idx = ((int64_t)blockIdx.x * kThreads + threadIdx.x) * 4;
+// running sums and CH stores.  NT threads per workgroup: small workgroups
+// spread the scan over every CU (each CU's stream of requests is the limit).
+template <int CH, int NT>
+__global__ __launch_bounds__(NT) void la_segment_scan_kernel(float* __restrict__ ws, const int32_t* __restrict__ flags,
+                                                             int nseg, int64_t entries) {
+    const int64_t idx = ((int64_t)blockIdx.x * NT + threadIdx.x) * 4;
     if (idx >= entries) return;
     f32x4_t carry = zero4();
     for (int u0 = 0; u0 < nseg - 1; u0 += CH) {

@@ -44,7 +44,8 @@ hipError_t run_prefill(const PrefillParams& p, int variant, hipStream_t st, hipE
             if (p.scan) {
                 const int64_t entries = (int64_t)p.H * D * D;  // a multiple of 4
                 const int64_t threads = entries / 4;
-                la_segment_scan_kernel<32><<<dim3((unsigned)((threads + kThreads - 1) / kThreads)), block, 0, st>>>(
+                constexpr int NT = 128;
+                la_segment_scan_kernel<32, NT><<<dim3((unsigned)((threads + NT - 1) / NT)), dim3(NT), 0, st>>>(
                     p.ws, p.flags, p.nseg, entries);
             }
         }

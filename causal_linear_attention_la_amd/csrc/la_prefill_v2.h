@@ -344,24 +344,34 @@ __global__ __launch_bounds__(kThreads, 1) void la_segment_state_v2(PrefillParams
         }
     };
     const int npairs = (nblk + 1) / 2;
-    int jj = 0;
+    // Step i fills slot i % 2 with pair i, then reads pair i - 1 from the
+    // other slot while pair i is in flight: the first two pairs go out back to
+    // back, so a segment of up to four blocks waits for memory once.  (The
+    // first fill is issued from the loop, not ahead of it, which keeps the
+    // compiler's record of the slot each DMA in flight writes exact.)
+    constexpr int LP = 2 * (DmaTile<D>::NI + DmaTile<W>::NI);  // loads per wave and pair
+    int i = 0;
     auto step = [&](auto slot) {
         constexpr int SLOT = decltype(slot)::value;
-        vm_wait<0>();   // pair jj in (issued one step ago, nothing younger)
-        lds_barrier();  // pair jj visible; pair jj-1 no longer read
-        issue(jj + 1, Slot<1 - SLOT>{});
-        state_update<D, B, W>(kv, vfr, kbuf(slot), vbuf(slot), col0, lane);
-        state_update<D, B, W>(kv, vfr, kbuf(slot) + B * D, vbuf(slot) + B * W, col0, lane);
-        ++jj;
+        lds_barrier();  // pair i - 2 (read at step i - 1) is done with this slot
+        issue(i, slot);
+        if (i > 0) {
+            vm_wait<LP>();  // pair i - 1 is in (pair i may still be in flight) ...
+            lds_barrier();  // ... for every wave
+            state_update<D, B, W>(kv, vfr, kbuf(Slot<1 - SLOT>{}), vbuf(Slot<1 - SLOT>{}), col0, lane);
+            state_update<D, B, W>(kv, vfr, kbuf(Slot<1 - SLOT>{}) + B * D, vbuf(Slot<1 - SLOT>{}) + B * W, col0,
+                                  lane);
+        }
+        ++i;
     };
-    issue(0, Slot<0>{});
     while (true) {
         step(Slot<0>{});
-        if (jj >= npairs) break;
+        if (i > npairs) break;
         step(Slot<1>{});
-        if (jj >= npairs) break;
+        if (i > npairs) break;
     }
     store_ws<D, B, W>(kv, p.ws + ws_offset<D, W>(p, u, h, s, wave), lane);
+    vm_wait<0>();  // no tile load may still be writing into this workgroup's LDS when it ends
 }
 
 // ---------------------------------------------------------------------------
@@ -584,6 +594,7 @@ __global__ __launch_bounds__(kThreads, 1) void la_prefill_main_v2(PrefillParams 
     }
 
     if (p.kv_out) empty_doc_states<D, W>(p, u, h, s, t0, t1, tid);
+    vm_wait<0>();  // no tile load may still be writing into this workgroup's LDS when it ends
 }
 
 }  // namespace v2
