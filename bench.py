@@ -128,7 +128,7 @@ def bench_prefill(args, la, torch, hip):
     T, H, d, block = w["T"], w["H"], w["d"], args.block or w["block"]
     dt = la.LA_BF16 if w["dtype"] == "bf16" else la.LA_FP32
     num_seqs = len(w["cu"]) - 1
-    opts = dict(seg_len=args.seg_len, value_slices=args.slices, force_scan=args.force_scan)
+    opts = dict(seg_len=args.seg_len, value_slices=args.slices, force_scan=args.force_scan, slots=args.slots)
     plan = la.la_prefill_plan(T, num_seqs, H, d, block, dt, la.make_opts(**opts))
 
     def dev(a):
@@ -222,7 +222,8 @@ def bench_prefill(args, la, torch, hip):
         "data": "synthetic",
         "config": {"workload": name, "documents": num_seqs, "heads": H, "tokens": T, "head_dim": d, "block": block,
                    "seg_len": plan["seg_len"], "value_slices": plan["value_slices"],
-                   "segments": plan["num_segments"], "scan": plan["scan"], "workgroups": plan["units"],
+                   "segments": plan["num_segments"], "scan": plan["scan"], "slots": plan["slots"],
+                   "workgroups": plan["units"],
                    "input_sets": nsets},
         "roofline": {"bound": "hbm", "kernel": kname, "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
@@ -282,7 +283,7 @@ def bench_backward(args, la, torch, hip, w, dev_sets):
     T, H, d = w["T"], w["H"], w["d"]
     esz = 2 if w["dtype"] == "bf16" else 4
     block = args.block or w["block"]
-    opts = dict(seg_len=args.seg_len, value_slices=args.slices, force_scan=args.force_scan)
+    opts = dict(seg_len=args.seg_len, value_slices=args.slices, force_scan=args.force_scan, slots=args.slots)
     cu = torch.from_numpy(w["cu"]).cuda()
     d0 = la_inputs.normal(la_inputs.WORKLOADS[w["name"]]["seed"], 8, (T, H, d), w["dtype"], 1.0)
     dout0 = torch.from_numpy(d0.view(np.int16)).view(torch.bfloat16).cuda() if d0.dtype == np.uint16 \
@@ -357,6 +358,7 @@ def main():
     ap.add_argument("--seg-len", type=int, default=0)
     ap.add_argument("--slices", type=int, default=0)
     ap.add_argument("--force-scan", action="store_true")
+    ap.add_argument("--slots", type=int, default=0, help="tile slots of the block loop: 0 automatic, 2 or 3")
     ap.add_argument("--rotate", type=int, default=8, help="input sets cycled through the timed steps")
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--no-decode", action="store_true")

@@ -32,13 +32,13 @@ class LAError(RuntimeError):
 class la_prefill_opts(ctypes.Structure):
     _fields_ = [("seg_len", ctypes.c_int32), ("value_slices", ctypes.c_int32), ("force_scan", ctypes.c_int32),
                 ("variant", ctypes.c_int32), ("main_begin_event", ctypes.c_void_p),
-                ("main_end_event", ctypes.c_void_p)]
+                ("main_end_event", ctypes.c_void_p), ("slots", ctypes.c_int32)]
 
 
 class la_prefill_plan_info(ctypes.Structure):
     _fields_ = [("seg_len", ctypes.c_int32), ("value_slices", ctypes.c_int32), ("num_segments", ctypes.c_int32),
                 ("scan", ctypes.c_int32), ("units", ctypes.c_int64), ("workspace_bytes", ctypes.c_size_t),
-                ("variant", ctypes.c_int32)]
+                ("variant", ctypes.c_int32), ("slots", ctypes.c_int32)]
 
 
 _lib = None
@@ -125,9 +125,9 @@ def la_prefill_workspace_size(total_tokens, num_seqs, H, d, block, dtype) -> int
 
 
 def make_opts(seg_len: int = 0, value_slices: int = 0, force_scan: bool = False, begin_event=None,
-              end_event=None, variant: int = 0) -> la_prefill_opts:
+              end_event=None, variant: int = 0, slots: int = 0) -> la_prefill_opts:
     return la_prefill_opts(int(seg_len), int(value_slices), 1 if force_scan else 0, int(variant),
-                           _event_ptr(begin_event), _event_ptr(end_event))
+                           _event_ptr(begin_event), _event_ptr(end_event), int(slots))
 
 
 def la_prefill_workspace_size_ex(total_tokens, num_seqs, H, d, block, dtype, opts=None) -> int:
@@ -142,7 +142,8 @@ def la_prefill_plan(total_tokens, num_seqs, H, d, block, dtype, opts=None) -> di
     if st != LA_OK:
         raise LAError(st, "la_prefill_plan")
     return dict(seg_len=info.seg_len, value_slices=info.value_slices, num_segments=info.num_segments,
-                scan=info.scan, units=info.units, workspace_bytes=info.workspace_bytes, variant=info.variant)
+                scan=info.scan, units=info.units, workspace_bytes=info.workspace_bytes, variant=info.variant,
+                slots=info.slots)
 
 
 # ------------------------------------------------------------ torch layer
@@ -180,7 +181,7 @@ def _ptr(t):
 
 def prefill(q, k, v, cu_seqlens, block: int = 64, want_state: bool = True, out=None, kv_state_out=None,
             workspace=None, seg_len: int = 0, value_slices: int = 0, force_scan: bool = False, stream=None,
-            begin_event=None, end_event=None, variant: int = 0, kv_state_in=None):
+            begin_event=None, end_event=None, variant: int = 0, kv_state_in=None, slots: int = 0):
     """Lightning-style causal linear attention over packed documents.
 
     q, k, v: [T, H, d] bf16/fp32 CUDA tensors; cu_seqlens: int32 [num_seqs + 1]
@@ -198,7 +199,7 @@ def prefill(q, k, v, cu_seqlens, block: int = 64, want_state: bool = True, out=N
     kv = kv_state_out
     if kv is None and want_state:
         kv = torch.empty((num_seqs, H, d, d), dtype=torch.float32, device=q.device)
-    opts = make_opts(seg_len, value_slices, force_scan, begin_event, end_event, variant)
+    opts = make_opts(seg_len, value_slices, force_scan, begin_event, end_event, variant, slots)
     need = la_prefill_workspace_size_ex(T, num_seqs, H, d, block, dt, opts)
     ws = workspace
     if need and (ws is None or ws.numel() * ws.element_size() < need):
@@ -214,7 +215,7 @@ def prefill(q, k, v, cu_seqlens, block: int = 64, want_state: bool = True, out=N
 
 def backward(q, k, v, dout, cu_seqlens, block: int = 64, kv_state_in=None, dkv_state_out=None,
              want_dkv_in: bool = True, workspace=None, seg_len: int = 0, value_slices: int = 0,
-             force_scan: bool = False, stream=None, variant: int = 0, out=None):
+             force_scan: bool = False, stream=None, variant: int = 0, out=None, slots: int = 0):
     """Gradients of the prefill (la_prefill_backward).  dout is dL/do
     ([T, H, d], same dtype as q); dkv_state_out (fp32 [num_seqs, H, d, d] or
     None) is dL/dkv_state_out.  out = (dq, dk, dv, dkv_in) preallocated
@@ -230,7 +231,7 @@ def backward(q, k, v, dout, cu_seqlens, block: int = 64, kv_state_in=None, dkv_s
     else:
         dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
         dkv_in = torch.empty((num_seqs, H, d, d), dtype=torch.float32, device=q.device) if want_dkv_in else None
-    opts = make_opts(seg_len, value_slices, force_scan, None, None, variant)
+    opts = make_opts(seg_len, value_slices, force_scan, None, None, variant, slots)
     need = la_prefill_workspace_size_ex(T, num_seqs, H, d, block, dt, opts)
     ws = workspace
     if need and (ws is None or ws.numel() * ws.element_size() < need):

@@ -33,6 +33,7 @@ la_status enqueue_prefill(const Plan& plan, const void* q, const void* k, const 
     p.scan = plan.scan;
     p.rev = rev;
     p.kv_in_t = kv_in_t;
+    p.slots = plan.slots;
     p.units = plan.units;
     p.per_xcd = (plan.units + 7) / 8;
     hipStream_t s = static_cast<hipStream_t>(stream);
@@ -69,6 +70,7 @@ la_status la_prefill_plan(int64_t total_tokens, int32_t num_seqs, int32_t H, int
         out->units = p.units;
         out->workspace_bytes = p.ws_bytes;
         out->variant = p.variant;
+        out->slots = p.slots;
     }
     return LA_OK;
 }

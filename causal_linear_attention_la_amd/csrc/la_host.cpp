@@ -13,6 +13,9 @@ constexpr int kNumCUs = 256;      // MI355X compute units
 constexpr int kUnitsTarget = 256; // block-loop workgroups to aim for (one per CU)
 constexpr int kMinSegment = 256;  // shorter segments spend more on state traffic than they gain
 constexpr int kMaxLookback = 16;  // a unit sums at most this many segment states
+// The transpose-read loop takes three tile slots (loads two blocks ahead) on
+// segments of at least this many blocks; shorter ones start faster with two.
+constexpr int kThreeSlotMinBlocks = 16;
 
 bool is_pow2_in(int32_t x, int32_t lo, int32_t hi) {
     if (x < lo || x > hi) return false;
@@ -96,6 +99,13 @@ la_status make_plan(int64_t T, int32_t num_seqs, int32_t H, int32_t d, int32_t b
     p.units = nseg * (int64_t)H * p.S;
     if (p.units > (int64_t)INT32_MAX * 8) return LA_ERR_UNSUPPORTED;
     p.scan = (p.nseg - 1 > kMaxLookback || (opts && opts->force_scan)) && p.nseg > 1 ? 1 : 0;
+    const int32_t slots = opts ? opts->slots : 0;
+    if (!(slots == 0 || slots == 2 || slots == 3)) return LA_ERR_UNSUPPORTED;
+    const bool three_ok = p.variant == 2 && d == 128;
+    if (slots == 3 && !three_ok) return LA_ERR_UNSUPPORTED;
+    if (slots != 0) p.slots = slots;
+    else p.slots = three_ok && p.L / block >= kThreeSlotMinBlocks ? 3 : 2;
+    if (p.variant != 2) p.slots = 2;  // (the generic loop has no slot choice)
 
     if (p.nseg > 1) {
         int64_t states;

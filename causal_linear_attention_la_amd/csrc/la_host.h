@@ -16,6 +16,7 @@ struct Plan {
     int32_t nseg = 1;
     int32_t scan = 0;   // run the prefix-scan kernel
     int32_t variant = 1;  // block loop: 1 generic, 2 transpose-read
+    int32_t slots = 2;    // tile slots of the transpose-read loop
     int64_t units = 0;  // nseg * H * S
     size_t ws_bytes = 0;
     size_t ws_states_off = 0;

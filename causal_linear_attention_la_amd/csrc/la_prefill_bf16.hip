@@ -5,9 +5,11 @@
 namespace la {
 // Explicit instantiations: the host pass otherwise calls, but does not emit,
 // the launch stubs of the transpose-read kernels.
-template __global__ void v2::la_prefill_main_v2<128, 64, 128>(PrefillParams);
-template __global__ void v2::la_prefill_main_v2<128, 64, 64>(PrefillParams);
-template __global__ void v2::la_prefill_main_v2<64, 64, 64>(PrefillParams);
+template __global__ void v2::la_prefill_main_v2<128, 64, 128, 2>(PrefillParams);
+template __global__ void v2::la_prefill_main_v2<128, 64, 128, 3>(PrefillParams);
+template __global__ void v2::la_prefill_main_v2<128, 64, 64, 2>(PrefillParams);
+template __global__ void v2::la_prefill_main_v2<128, 64, 64, 3>(PrefillParams);
+template __global__ void v2::la_prefill_main_v2<64, 64, 64, 2>(PrefillParams);
 template __global__ void v2::la_segment_state_v2<128, 64, 128>(PrefillParams);
 template __global__ void v2::la_segment_state_v2<128, 64, 64>(PrefillParams);
 template __global__ void v2::la_segment_state_v2<64, 64, 64>(PrefillParams);

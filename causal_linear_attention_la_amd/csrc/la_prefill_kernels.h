@@ -45,7 +45,7 @@ struct PrefillParams {
     int32_t scan;    // 1: ws holds inclusive per-document states (after the scan kernel)
     int32_t rev;     // 1: every document is processed from its last token to its first
     int32_t kv_in_t; // 1: kv_in holds transposed states ([value][key])
-    int32_t pad_;
+    int32_t slots;   // tile slots of the transpose-read block loop (2 or 3)
     int64_t units;   // nseg * H * S
     int64_t per_xcd; // ceil(units / 8)
 };

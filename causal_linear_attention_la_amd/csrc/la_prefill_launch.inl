@@ -51,7 +51,14 @@ hipError_t run_prefill(const PrefillParams& p, int variant, hipStream_t st, hipE
         }
         void (*main_kernel)(PrefillParams) = la_prefill_main_kernel<T, D, B, W>;
         if constexpr (has_v2<T, D, B, W>()) {
-            if (use_v2) main_kernel = v2::la_prefill_main_v2<D, B, W>;
+            if (use_v2) {
+                if constexpr (D == 128) {
+                    main_kernel = p.slots == 3 ? v2::la_prefill_main_v2<D, B, W, 3> : v2::la_prefill_main_v2<D, B, W, 2>;
+                } else {
+                    if (p.slots == 3) return hipErrorInvalidValue;
+                    main_kernel = v2::la_prefill_main_v2<D, B, W, 2>;
+                }
+            }
         }
         hipError_t e = launch_main(main_kernel, grid, block, p, st, e0, e1);
         if (e != hipSuccess) return e;

@@ -375,24 +375,45 @@ __global__ __launch_bounds__(kThreads, 1) void la_segment_state_v2(PrefillParams
 }
 
 // ---------------------------------------------------------------------------
-// The block loop.
-template <int D, int B, int W>
+// The block loop.  NS tile slots: with two, block j + 1's tiles are loaded
+// during iteration j; with three (long segments), block j + 2's are, so each
+// load has a whole iteration more to arrive and twice the bytes are in flight
+// per CU -- what a 4-wave workgroup needs to keep HBM busy.  (On short
+// segments the deeper start costs more than it hides.)
+template <int D, int B, int W, int NS>
 __global__ __launch_bounds__(kThreads, 1) void la_prefill_main_v2(PrefillParams p) {
     using G = Geo<D, B, W>;
     constexpr int NQT = G::NQT, NCW = G::NCW, NDT = G::NDT;
     static_assert(NQT == kWaves, "wave w takes key band w");
+    static_assert(NS == 2 || NS == 3, "two or three tile slots");
     constexpr int PP = B;  // P[query][key] rows: 128 bytes
-    // Two tile slots, each tile its own LDS variable: with the loop unrolled
-    // by two, every LDS access names its slot at compile time, so the
-    // compiler sees that reads of one slot do not alias the DMA writes in
-    // flight to the other and adds no waits of its own.
-    __shared__ __align__(16) bf16_t Qb0[B * D], Qb1[B * D];
-    __shared__ __align__(16) bf16_t Kb0[B * D], Kb1[B * D];
-    __shared__ __align__(16) bf16_t Vb0[B * W], Vb1[B * W];
+    // Each tile of each slot is its own LDS variable: with the loop unrolled
+    // by the slot count, every LDS access names its slot at compile time, so
+    // the compiler sees that reads of one slot do not alias the DMA writes in
+    // flight to the others and adds no waits of its own.
+    constexpr int QN = B * D, VN = B * W, X3 = NS == 3 ? 1 : 0;
+    __shared__ __align__(16) bf16_t Q0[QN], Q1[QN], Q2[X3 ? QN : 8];
+    __shared__ __align__(16) bf16_t K0[QN], K1[QN], K2[X3 ? QN : 8];
+    __shared__ __align__(16) bf16_t V0[VN], V1[VN], V2[X3 ? VN : 8];
     __shared__ __align__(16) bf16_t Ps[B * PP];
-    auto qbuf = [&](auto slot) -> bf16_t* { if constexpr (decltype(slot)::value == 0) return Qb0; else return Qb1; };
-    auto kbuf = [&](auto slot) -> bf16_t* { if constexpr (decltype(slot)::value == 0) return Kb0; else return Kb1; };
-    auto vbuf = [&](auto slot) -> bf16_t* { if constexpr (decltype(slot)::value == 0) return Vb0; else return Vb1; };
+    auto qbuf = [&](auto slot) -> bf16_t* {
+        constexpr int X = decltype(slot)::value;
+        if constexpr (X == 0) return Q0;
+        else if constexpr (X == 1) return Q1;
+        else return Q2;
+    };
+    auto kbuf = [&](auto slot) -> bf16_t* {
+        constexpr int X = decltype(slot)::value;
+        if constexpr (X == 0) return K0;
+        else if constexpr (X == 1) return K1;
+        else return K2;
+    };
+    auto vbuf = [&](auto slot) -> bf16_t* {
+        constexpr int X = decltype(slot)::value;
+        if constexpr (X == 0) return V0;
+        else if constexpr (X == 1) return V1;
+        else return V2;
+    };
 
     int u, h, s;
     if (!unit_of(p, u, h, s)) return;
@@ -492,7 +513,15 @@ __global__ __launch_bounds__(kThreads, 1) void la_prefill_main_v2(PrefillParams 
         }
     };
 
-    if (c0.nb > 0) issue(c0, Slot<0>{});  // before the prefix loads, so the two overlap
+    // the block after c0 (kept from step to step with three slots)
+    Cursor c1 = c0;
+    if constexpr (NS == 3) {
+        if (c0.nb > 0) cursor_next(c1, cuv, p.num_seqs, t1, B);
+    }
+    if (c0.nb > 0) {  // before the prefix loads, so the two overlap
+        issue(c0, Slot<0>{});
+        if constexpr (NS == 3) issue(c1, Slot<1>{});
+    }
     if (c0.nb > 0 && !c0.first_of_doc) {
         const int u_first = p.scan ? u - 1 : cuv[c0.doc] / p.L;
         for (int uu = u_first; uu < u; ++uu)
@@ -504,20 +533,32 @@ __global__ __launch_bounds__(kThreads, 1) void la_prefill_main_v2(PrefillParams 
                            g, li);
     int pb0 = t0, pnb = 0;
     int j = 0;
-    // One block; its tiles sit in slot SLOT, the next block's go to the other.
+    // One block (j); its tiles sit in slot SLOT.  This iteration loads block
+    // j + NS - 1 into slot FILL, the one block j - 1 used.
     auto step = [&](auto slot) {
         constexpr int SLOT = decltype(slot)::value;
-        Cursor c1 = c0;
-        cursor_next(c1, cuv, p.num_seqs, t1, B);
-        // Loads of block j (issued during the previous iteration, the last
-        // tile after its stores) are all done: nothing younger is in flight.
-        vm_wait<0>();
+        constexpr int FILL = (SLOT + NS - 1) % NS;
+        Cursor cf;
+        if constexpr (NS == 2) {
+            cf = c0;
+            cursor_next(cf, cuv, p.num_seqs, t1, B);
+        } else {
+            cf = c1;
+            if (c1.nb > 0) cursor_next(cf, cuv, p.num_seqs, t1, B);
+            else cf.nb = 0;
+        }
+        // Loads of block j are done.  With two slots they were the last
+        // vector-memory operations issued; with three, block j + 1's loads and
+        // the stores issued between them (one iteration's worth) may still be
+        // in flight.
+        if constexpr (NS == 2) vm_wait<0>();
+        else vm_wait<G::LOADS + G::STORES>();
         lds_barrier();  // (A) block j visible; block j-1's tiles no longer read
-        issue_tile(c1, Slot<1 - SLOT>{}, Slot<0>{});
+        issue_tile(cf, Slot<FILL>{}, Slot<0>{});
         // block j-1's output; in the first iteration pnb = 0 and the stores
         // (of whatever the accumulators hold) fall outside the buffer range
         finish(pb0, pnb);
-        issue_tile(c1, Slot<1 - SLOT>{}, Slot<1>{});
+        issue_tile(cf, Slot<FILL>{}, Slot<1>{});
         lds_barrier();  // (B) scores of block j-1 consumed
 
         const bf16_t* Qs = qbuf(slot);
@@ -549,7 +590,7 @@ __global__ __launch_bounds__(kThreads, 1) void la_prefill_main_v2(PrefillParams 
                 mma(sacc[b], kf, qf);
             }
         }
-        issue_tile(c1, Slot<1 - SLOT>{}, Slot<2>{});
+        issue_tile(cf, Slot<FILL>{}, Slot<2>{});
         // state: KV += K^T V (after the inter product read it)
         state_update<D, B, W>(kv, vfr, Ks, Vs, col0, lane);
 
@@ -572,21 +613,31 @@ __global__ __launch_bounds__(kThreads, 1) void la_prefill_main_v2(PrefillParams 
             for (int a = 0; a < NDT; ++a)
 #pragma unroll
                 for (int c = 0; c < NCW; ++c) kv[a][c] = zero4();
-            if (p.kv_in && c1.nb > 0 && c1.first_of_doc) {  // the next document starts here
-                add_state<D, B, W>(kv, p.kv_in + (((int64_t)phys_doc(p, c1.doc) * p.H + h) * D) * D, s * W + col0,
+            const Cursor& cn = NS == 2 ? cf : c1;  // block j + 1
+            if (p.kv_in && cn.nb > 0 && cn.first_of_doc) {  // the next document starts here
+                add_state<D, B, W>(kv, p.kv_in + (((int64_t)phys_doc(p, cn.doc) * p.H + h) * D) * D, s * W + col0,
                                    p.kv_in_t, g, li);
                 vm_wait<0>();
             }
         }
         pb0 = c0.b0;
         pnb = c0.nb;
-        c0 = c1;
+        if constexpr (NS == 2) {
+            c0 = cf;
+        } else {
+            c0 = c1;
+            c1 = cf;
+        }
         ++j;
     };
     while (c0.nb > 0) {
         step(Slot<0>{});
         if (c0.nb <= 0) break;
         step(Slot<1>{});
+        if constexpr (NS == 3) {
+            if (c0.nb <= 0) break;
+            step(Slot<2>{});
+        }
     }
     if (j > 0) {
         lds_barrier();  // scores of the last block visible

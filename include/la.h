@@ -132,6 +132,9 @@ typedef struct {
                                executing, or NULL (the kernel is then launched with
                                hipExtLaunchKernel, which records both events) */
     void* main_end_event;   /* hipEvent_t stamped when it completes, or NULL */
+    int32_t slots;          /* tile slots of the transpose-read loop: 0 = automatic
+                               (3 on segments of 16 blocks or more), 2, or 3 (loads
+                               two blocks ahead; d = 128 only) */
 } la_prefill_opts;
 
 /* The decomposition a prefill call will use (for reports and tests). */
@@ -143,6 +146,7 @@ typedef struct {
     int64_t units;         /* workgroups of the block-loop kernel */
     size_t workspace_bytes;
     int32_t variant;       /* the block-loop kernel that runs: 1 = generic, 2 = transpose-read */
+    int32_t slots;         /* tile slots of the transpose-read loop (2 or 3) */
 } la_prefill_plan_info;
 
 la_status la_prefill_plan(int64_t total_tokens, int32_t num_seqs, int32_t H, int32_t d, int32_t block,

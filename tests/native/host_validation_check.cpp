@@ -53,6 +53,23 @@ int main() {
     EXPECT(make_plan(8192, 1, 8, 128, 64, LA_BF16, &o1, &p) == LA_ERR_UNSUPPORTED);
     o1.value_slices = 8;
     EXPECT(make_plan(8192, 1, 8, 128, 64, LA_BF16, &o1, &p) == LA_ERR_UNSUPPORTED);
+    // tile slots: three on long segments of the d = 128 transpose-read loop, two otherwise
+    EXPECT(make_plan(8192, 1, 8, 128, 64, LA_BF16, nullptr, &p) == LA_OK && p.slots == 2);
+    EXPECT(make_plan(1048576, 1, 8, 128, 64, LA_BF16, nullptr, &p) == LA_OK && p.slots == 3);
+    EXPECT(make_plan(1048576, 1, 8, 64, 64, LA_BF16, nullptr, &p) == LA_OK && p.slots == 2);
+    EXPECT(make_plan(1048576, 1, 8, 128, 64, LA_FP32, nullptr, &p) == LA_OK && p.slots == 2);
+    la_prefill_opts o3{};
+    o3.slots = 3;
+    EXPECT(make_plan(8192, 1, 8, 128, 64, LA_BF16, &o3, &p) == LA_OK && p.slots == 3);
+    EXPECT(make_plan(8192, 1, 8, 64, 64, LA_BF16, &o3, &p) == LA_ERR_UNSUPPORTED);
+    EXPECT(make_plan(8192, 1, 8, 128, 64, LA_FP32, &o3, &p) == LA_ERR_UNSUPPORTED);
+    o3.variant = 1;
+    EXPECT(make_plan(8192, 1, 8, 128, 64, LA_BF16, &o3, &p) == LA_ERR_UNSUPPORTED);
+    o3.variant = 0;
+    o3.slots = 2;
+    EXPECT(make_plan(1048576, 1, 8, 128, 64, LA_BF16, &o3, &p) == LA_OK && p.slots == 2);
+    o3.slots = 1;
+    EXPECT(make_plan(8192, 1, 8, 128, 64, LA_BF16, &o3, &p) == LA_ERR_UNSUPPORTED);
 
     // shape errors
     EXPECT(make_plan(-1, 1, 8, 128, 64, LA_BF16, nullptr, &p) == LA_ERR_INVALID_ARG);

@@ -113,6 +113,12 @@ def test_plans(lib):
     assert p["workspace_bytes"] >= 128 * 8 * 128 * 128 * 4
     with pytest.raises(la.LAError):
         la.la_prefill_plan(8192, 1, 8, 128, 64, la.LA_BF16, la.make_opts(seg_len=100))
+    # tile slots of the transpose-read loop: three on long segments, two on short ones
+    assert la.la_prefill_plan(8192, 1, 8, 128, 64, la.LA_BF16)["slots"] == 2
+    assert la.la_prefill_plan(1048576, 1, 8, 128, 64, la.LA_BF16)["slots"] == 3
+    assert la.la_prefill_plan(8192, 1, 8, 128, 64, la.LA_BF16, la.make_opts(slots=3))["slots"] == 3
+    with pytest.raises(la.LAError):
+        la.la_prefill_plan(8192, 1, 8, 64, 64, la.LA_BF16, la.make_opts(slots=3))
 
 
 def test_host_validation_under_sanitizers(tmp_path):

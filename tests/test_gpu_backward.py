@@ -82,6 +82,21 @@ def test_backward_against_oracle(d, block, dtype, opts, with_states):
                 assert np.array_equal(got[3][i], dkv_out[i])
 
 
+@pytest.mark.parametrize("slots", [2, 3])
+def test_backward_tile_slots(slots):
+    """All three passes (two of them over documents read back to front) with
+    two and three tile slots in the block loop."""
+    lens = [300, 0, 1, 700, 64, 0, 129, 1500]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    T, H, d = int(cu[-1]), 3, 128
+    q, k, v, dout = inputs(131, T, H, d, "bf16")
+    kv_in = states(132, 7, len(lens), H, d, float(np.sqrt(2000)) / d)
+    dkv_out = states(133, 9, len(lens), H, d, 1.0)
+    log(f"  backward slots={slots}")
+    got = run(q, k, v, dout, cu, 64, kv_in, dkv_out, seg_len=1024, slots=slots)
+    check(q, k, v, dout, cu, kv_in, dkv_out, got, False, f"backward slots {slots}")
+
+
 def test_backward_prefill_8k_workload():
     w = la_inputs.prefill_inputs("prefill_8k")
     T, H, d = w["T"], w["H"], w["d"]

@@ -2,8 +2,9 @@
 
 Cases: the tiny fp32 and 8k-token bf16 workloads in full; every (d, block,
 dtype) the library supports on ragged lengths; forced segment splitting and
-value slicing (the LASP+-style prefix path); packed documents with empty and
-ragged ones; exact-integer inputs that must match bit for bit; run-to-run
+value slicing (the LASP+-style prefix path); two and three tile slots in the
+block loop; packed documents with empty and ragged ones; exact-integer
+inputs that must match bit for bit; run-to-run
 determinism; guard bands around the outputs; zero tokens; and the
 131072-token varlen and 1M-token workloads in full, in the launch
 configuration the benchmark uses."""
@@ -99,6 +100,39 @@ def test_segment_splitting(opts):
     log(f"  split {opts} plan={plan}")
     o, kv = run_gpu(q, k, v, cu, block, **opts)
     check_against_oracle(q, k, v, cu, o, kv, False, f"split {opts}")
+
+
+SLOT_CASES = [(S, opts) for S in (1, 2)
+              for opts in (dict(), dict(seg_len=64), dict(seg_len=192, force_scan=True), dict(seg_len=1024))]
+
+
+@pytest.mark.parametrize("S,opts", SLOT_CASES, ids=[f"S{S}-{o}" for S, o in SLOT_CASES])
+def test_three_tile_slots(S, opts):
+    """The transpose-read loop loading two blocks ahead (three tile slots)
+    on ragged packed documents, with incoming states: against the oracle,
+    and bit for bit against two slots (the per-block arithmetic is the same)."""
+    import torch
+
+    lens = [5, 0, 295, 1, 699, 64, 0, 1436, 130]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    T, H, d = int(cu[-1]), 3, 128
+    q, k, v = rand_inputs(141, T, H, d, "bf16")
+    kv_in = np.ascontiguousarray(la_inputs.normal(142, 7, (len(lens), H, d, d), "fp32", float(np.sqrt(2000)) / d),
+                                 dtype=np.float32)
+    o_ref, kv_ref = oracle.recurrent(q, k, v, cu, kv_in=kv_in)
+    outs = []
+    for slots in (3, 2):
+        plan = la.la_prefill_plan(T, len(lens), H, d, 64, la.LA_BF16, la.make_opts(value_slices=S, slots=slots, **opts))
+        assert plan["slots"] == slots and plan["variant"] == 2
+        log(f"  slots={slots} S={S} {opts} plan={plan}")
+        o, kv = la.prefill(to_dev(q), to_dev(k), to_dev(v), to_dev(cu), block=64, value_slices=S, slots=slots,
+                           kv_state_in=to_dev(kv_in), **opts)
+        torch.cuda.synchronize()
+        o, kv = to_host(o), to_host(kv)
+        ErrAcc().add(o, o_ref).check(False, f"slots {slots} o")
+        ErrAcc().add(kv, kv_ref).check(False, f"slots {slots} kv_state")
+        outs.append((o, kv))
+    assert np.array_equal(outs[0][0], outs[1][0]) and np.array_equal(outs[0][1], outs[1][1])
 
 
 VARIANT_CASES = [(d, S, opts) for d, slices in ((128, (1, 2)), (64, (1,))) for S in slices
