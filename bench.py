@@ -113,9 +113,48 @@ def cpu_baseline(w, target_cpu_s: float = 10.0) -> dict:
         if wall * threads >= target_cpu_s or reps >= 50:
             break
     th = w["T"] * w["H"] * reps / wall
+    # one thread on a quarter of the heads, for a per-core figure
+    hq = max(1, w["H"] // 4)
+    t0 = time.perf_counter()
+    oracle.recurrent(w["q"], w["k"], w["v"], w["cu"], want_o=True, want_state=True, heads=(0, hq), nthreads=1)
+    one = w["T"] * hq / (time.perf_counter() - t0)
     return {"value": th, "unit": "token·heads/s", "cores": threads, "kind": "oracle",
             "sample": f"whole {w['name']} workload ({w['T']} tokens x {w['H']} heads, d={w['d']}), "
-                      f"fp64 recurrent form, {reps} repetitions, {wall:.2f} s wall"}
+                      f"fp64 recurrent form, {reps} repetitions, {wall:.2f} s wall",
+            "single_thread_value": one, "cpu_model": cpu_model()}
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def copy_bandwidth(torch, hip, nbytes: int = 1 << 30, reps: int = 20) -> float:
+    """Measured device copy bandwidth (GB/s, read + write bytes) of a 1 GiB
+    device-to-device copy: a second, practical roofline beside the datasheet's."""
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    stream = torch.cuda.current_stream().cuda_stream
+    e0, e1 = hip.event(), hip.event()
+    torch.cuda.synchronize()
+    hip.record(e0, stream)
+    for _ in range(reps):
+        dst.copy_(src)
+    hip.record(e1, stream)
+    torch.cuda.synchronize()
+    s = hip.elapsed_ms(e0, e1) / 1e3
+    hip.destroy(e0)
+    hip.destroy(e1)
+    del src, dst
+    return 2 * nbytes * reps / s / 1e9
 
 
 def bench_prefill(args, la, torch, hip):
@@ -391,6 +430,11 @@ def main():
         w.pop("dev_sets")
     if not args.no_decode:
         rec["decode"] = bench_decode(args, la, torch, hip)
+    copy = copy_bandwidth(torch, hip)
+    for part in (rec, rec.get("backward"), rec.get("decode")):
+        if part:
+            part["roofline"]["measured_copy_GBs"] = copy
+            part["roofline"]["frac_of_measured_copy"] = part["roofline"]["achieved"] / copy
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w)
     else:
