@@ -13,7 +13,7 @@ namespace {
 la_status enqueue_prefill(const Plan& plan, const void* q, const void* k, const void* v, void* o, const int32_t* cu,
                           int32_t H, int32_t d, int32_t block, const float* kv_in, int kv_in_t, float* kv_out,
                           int rev, int32_t num_seqs, int64_t T, la_dtype dtype, void* workspace, void* stream,
-                          hipEvent_t e0, hipEvent_t e1) {
+                          hipEvent_t e0, hipEvent_t e1, int skip_prefix = 0) {
     la::PrefillParams p{};
     p.q = q;
     p.k = k;
@@ -34,6 +34,7 @@ la_status enqueue_prefill(const Plan& plan, const void* q, const void* k, const 
     p.rev = rev;
     p.kv_in_t = kv_in_t;
     p.slots = plan.slots;
+    p.skip_prefix = skip_prefix;
     p.units = plan.units;
     p.per_xcd = (plan.units + 7) / 8;
     hipStream_t s = static_cast<hipStream_t>(stream);
@@ -125,14 +126,25 @@ la_status la_prefill_backward(const void* q, const void* k, const void* v, const
     st = enqueue_prefill(p1, dout, v, k, dq, cu_seqlens, H, d, block, kv_state_in, 1, nullptr, 0, num_seqs,
                          total_tokens, dtype, workspace, stream, nullptr, nullptr);
     if (st != LA_OK) return st;
-    // dK: reverse pass with query V, key dO, value Q, from dKV_out^T
-    st = enqueue_prefill(p2, v, dout, q, dk, cu_seqlens, H, d, block, dkv_state_out, 1, nullptr, 1, num_seqs,
-                         total_tokens, dtype, workspace, stream, nullptr, nullptr);
-    if (st != LA_OK) return st;
     // dV (and dKV_in, the reverse state after each document's first token):
     // reverse pass with query K, key Q, value dO, from dKV_out
-    return enqueue_prefill(p3, k, q, dout, dv, cu_seqlens, H, d, block, dkv_state_out, 0, dkv_state_in, 1, num_seqs,
-                           total_tokens, dtype, workspace, stream, nullptr, nullptr);
+    st = enqueue_prefill(p3, k, q, dout, dv, cu_seqlens, H, d, block, dkv_state_out, 0, dkv_state_in, 1, num_seqs,
+                         total_tokens, dtype, workspace, stream, nullptr, nullptr);
+    if (st != LA_OK) return st;
+    // dK: reverse pass with query V, key dO, value Q, from dKV_out^T.  Its
+    // segment states (sums of dO^T q) are the transposes of the dV pass's
+    // (sums of q^T dO) over the same segments: on the transpose-read loop they
+    // are transposed in place rather than computed again from Q and dO.
+    int reuse = 0;
+    if (p2.variant == 2 && p2.nseg > 1 && p2.L == p3.L && p2.S == p3.S && p2.nseg == p3.nseg && p2.scan == p3.scan) {
+        float* ws = reinterpret_cast<float*>(static_cast<char*>(workspace) + p3.ws_states_off);
+        if (la::launch_ws_transpose(ws, (int64_t)(p3.nseg - 1) * H, d, p3.W, static_cast<hipStream_t>(stream)) !=
+            hipSuccess)
+            return LA_ERR_HIP;
+        reuse = 1;
+    }
+    return enqueue_prefill(p2, v, dout, q, dk, cu_seqlens, H, d, block, dkv_state_out, 1, nullptr, 1, num_seqs,
+                           total_tokens, dtype, workspace, stream, nullptr, nullptr, reuse);
 }
 
 la_status la_prefill_ex(const void* q, const void* k, const void* v, void* o, const int32_t* cu_seqlens, int32_t H,

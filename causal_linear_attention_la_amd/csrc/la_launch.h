@@ -18,5 +18,8 @@ hipError_t launch_prefill_bf16(const PrefillParams& p, int D, int B, int W, int 
 hipError_t launch_prefill_fp32(const PrefillParams& p, int D, int B, int W, int variant, hipStream_t st,
                                hipEvent_t ev_begin, hipEvent_t ev_end);
 hipError_t launch_decode(const DecodeParams& p, int D, int dtype, hipStream_t st);
+// Transposes the first `states` segment states of a transpose-read plan's
+// workspace in place (la_ws_transpose_v2); D, W as in that plan.
+hipError_t launch_ws_transpose(float* ws, int64_t states, int D, int W, hipStream_t st);
 
 }  // namespace la

@@ -46,6 +46,8 @@ struct PrefillParams {
     int32_t rev;     // 1: every document is processed from its last token to its first
     int32_t kv_in_t; // 1: kv_in holds transposed states ([value][key])
     int32_t slots;   // tile slots of the transpose-read block loop (2 or 3)
+    int32_t skip_prefix;  // 1: ws already holds this pass's states; run only the block loop
+    int32_t pad_;
     int64_t units;   // nseg * H * S
     int64_t per_xcd; // ceil(units / 8)
 };

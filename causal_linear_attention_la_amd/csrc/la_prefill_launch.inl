@@ -34,7 +34,7 @@ hipError_t run_prefill(const PrefillParams& p, int variant, hipStream_t st, hipE
         bool use_v2 = false;
         if constexpr (has_v2<T, D, B, W>()) use_v2 = (variant != 1);
         if (variant == 2 && !use_v2) return hipErrorInvalidValue;
-        if (p.nseg > 1) {
+        if (p.nseg > 1 && !p.skip_prefix) {
             if constexpr (has_v2<T, D, B, W>()) {
                 if (use_v2) v2::la_segment_state_v2<D, B, W><<<grid, block, 0, st>>>(p);
                 else la_segment_state_kernel<T, D, B, W><<<grid, block, 0, st>>>(p);

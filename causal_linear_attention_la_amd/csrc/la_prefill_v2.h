@@ -375,6 +375,45 @@ __global__ __launch_bounds__(kThreads, 1) void la_segment_state_v2(PrefillParams
 }
 
 // ---------------------------------------------------------------------------
+// Transposes, in place, the first `states` segment states of the workspace
+// while keeping the block loop's register order: where a (segment, head)
+// entry held the state X, it then holds X^T, laid out as the block loop with
+// the same (D, W) expects a state.  The two reverse passes of the backward
+// sum transposed states over the same segments (q^T dO and dO^T q), so one
+// pass's prefix states serve the other.  One workgroup per entry: the D x D
+// state goes through LDS as a plain matrix (rows padded by 4 floats, so the
+// 16-byte column reads are conflict free).
+template <int D, int W>
+__global__ __launch_bounds__(kThreads) void la_ws_transpose_v2(float* __restrict__ ws, int64_t states) {
+    constexpr int NCW = W / 64;  // 16-column tiles per block-loop wave (W / 4 columns)
+    constexpr int PITCH = D + 4;
+    constexpr int PER_WAVE = D * W / 16, PER_SLICE = D * W / 4;  // 16-byte entries
+    __shared__ __align__(16) float M[D * PITCH];
+    if ((int64_t)blockIdx.x >= states) return;
+    f32x4_t* base = reinterpret_cast<f32x4_t*>(ws + (int64_t)blockIdx.x * D * D);
+    // entry e holds rows i0 .. i0 + 3 of column j (store_ws's order)
+    auto place = [](int e, int& i0, int& j) {
+        const int s = e / PER_SLICE, w = (e % PER_SLICE) / PER_WAVE, q = e % PER_WAVE;
+        const int a = (q / 64) / NCW, c = (q / 64) % NCW, lane = q % 64;
+        i0 = state_row(a, lane >> 4, 0);
+        j = s * W + w * (W / 4) + state_col<NCW>(c, lane & 15);
+    };
+    for (int e = threadIdx.x; e < D * D / 4; e += kThreads) {
+        int i0, j;
+        place(e, i0, j);
+        const f32x4_t x = base[e];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) M[(i0 + r) * PITCH + j] = x[r];
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < D * D / 4; e += kThreads) {
+        int i0, j;
+        place(e, i0, j);
+        base[e] = *reinterpret_cast<const f32x4_t*>(M + j * PITCH + i0);  // (X^T)[i0 + r][j] = X[j][i0 + r]
+    }
+}
+
+// ---------------------------------------------------------------------------
 // The block loop.  NS tile slots: with two, block j + 1's tiles are loaded
 // during iteration j; with three (long segments), block j + 2's are, so each
 // load has a whole iteration more to arrive and twice the bytes are in flight

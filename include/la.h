@@ -191,9 +191,11 @@ la_status la_prefill_resume(const void* q, const void* k, const void* v, void* o
  *     G_s    = dKV_out + sum_{t >= s} q_t^T dO_t         (a reverse state)
  *     dk_s   = G_s v_s ,   dv_s = k_s G_s ,   dKV_in = G at the first token
  * computed as three passes of the prefill kernels: dq forward with query dO,
- * key v, value k, starting from KV_in^T; dk and dv with every document read
- * from its last token to its first (query v / key dO / value q from dKV_out^T,
- * and query k / key q / value dO from dKV_out).
+ * key v, value k, starting from KV_in^T; dv and dk with every document read
+ * from its last token to its first (query k / key q / value dO from dKV_out,
+ * then query v / key dO / value q from dKV_out^T).  The dk pass's segment
+ * states are the transposes of the dv pass's; on the transpose-read loop they
+ * are transposed in the workspace instead of being computed again.
  *
  *   q, k, v, dout      [T, H, d] dtype, device, 16-byte aligned, read only.
  *   kv_state_in        the forward's incoming states or NULL (zero).
