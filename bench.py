@@ -35,6 +35,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, GB/s
+DECODE_SAMPLE = {}  # host copy of a few decode states for the oracle's timing
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 
 KERNEL_SOURCES = ["la_prefill_kernels.h", "la_prefill_v2.h", "la_device.h", "la_tiles.h", "la_prefill_launch.inl",
@@ -106,8 +107,11 @@ def cpu_baseline(w, target_cpu_s: float = 10.0) -> dict:
     reps, wall = 0, 0.0
     while True:
         t0 = time.perf_counter()
-        oracle.recurrent(w["q"], w["k"], w["v"], w["cu"], want_o=True, want_state=True)
+        o_ref, kv_ref = oracle.recurrent(w["q"], w["k"], w["v"], w["cu"], want_o=True, want_state=True)
         wall += time.perf_counter() - t0
+        if reps == 0 and "gpu_o" in w:
+            w["error_vs_oracle"] = error_vs_oracle(w, o_ref, kv_ref)
+        del o_ref, kv_ref
         reps += 1
         threads = oracle.last_threads()
         if wall * threads >= target_cpu_s or reps >= 50:
@@ -271,7 +275,27 @@ def bench_prefill(args, la, torch, hip):
         "path_roofline": {"token_heads_per_s": roof_th, "frac": value / roof_th},
         "graph_replay_value": graph_value,
     }
+    if not args.no_cpu_baseline:
+        # outputs of the seeded input set, for the error against the oracle
+        step(0)
+        torch.cuda.synchronize()
+        o0 = sets[0][3]
+        w["gpu_o"] = (o0.float() if o0.dtype == torch.bfloat16 else o0).cpu().numpy()
+        w["gpu_kv"] = kv.cpu().numpy()
     return rec, w
+
+
+def error_vs_oracle(w, o_ref, kv_ref) -> dict:
+    """rel-L2 and max-abs error (relative to max |ref|) of the GPU outputs
+    of the seeded input set against the fp64 oracle."""
+    def errs(g, r):
+        g = np.asarray(g, dtype=np.float64).ravel()
+        r = np.asarray(r, dtype=np.float64).ravel()
+        den = max(float(np.linalg.norm(r)), 1e-300)
+        return float(np.linalg.norm(g - r) / den), float(np.max(np.abs(g - r)) / max(float(np.max(np.abs(r))), 1e-300))
+    o_l2, o_max = errs(w["gpu_o"], o_ref)
+    kv_l2, kv_max = errs(w["gpu_kv"], kv_ref)
+    return {"o_rel_l2": o_l2, "o_max_abs_rel": o_max, "kv_state_rel_l2": kv_l2, "kv_state_max_abs_rel": kv_max}
 
 
 def bench_decode(args, la, torch, hip):
@@ -283,6 +307,7 @@ def bench_decode(args, la, torch, hip):
     steps = args.decode_steps
     S0 = la_inputs.decode_states(seed, ns, H, d, lo, hi)
     S = torch.from_numpy(S0.reshape(ns, H, d, d)).cuda()
+    DECODE_SAMPLE["S"] = S0[: 8 * H].copy()  # the first 8 sequences, for the oracle's timing
     del S0
     dev = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
     sets = [tuple(dev(x) for x in la_inputs.decode_step_inputs(seed, s, ns, H, d, "bf16")) for s in range(pool)]
@@ -367,6 +392,28 @@ def bench_backward(args, la, torch, hip, w, dev_sets):
                          "algorithmic_bytes": algo}}
 
 
+def decode_cpu_baseline(S_sample, steps: int = 200) -> dict:
+    """The fp64 oracle's decode step on a sample of the decode workload: the
+    incoming states of its first sequences (S_sample, fp32 [pairs, d, d])
+    over `steps` steps, scaled to whole-workload steps/s."""
+    import la_inputs
+    import oracle
+
+    cfg = la_inputs.WORKLOADS["decode_256x64"]
+    ns, H, d, seed = cfg["num_seqs"], cfg["H"], cfg["d"], cfg["seed"]
+    seqs = S_sample.shape[0] // H
+    S = np.ascontiguousarray(S_sample[: seqs * H], dtype=np.float64)
+    ins = [tuple(x[:seqs] for x in la_inputs.decode_step_inputs(seed, s % cfg["pool"], ns, H, d, "bf16"))
+           for s in range(steps)]
+    t0 = time.perf_counter()
+    for q, k, v in ins:
+        oracle.decode_step(q, k, v, S)
+    wall = time.perf_counter() - t0
+    return {"value": steps * (seqs * H) / (ns * H) / wall, "unit": "steps/s", "cores": oracle.last_threads(),
+            "kind": "oracle", "sample": f"{seqs * H} of {ns * H} (sequence, head) pairs x {steps} steps, "
+                                        f"{wall:.2f} s wall, scaled to the whole batch"}
+
+
 def profile_pass(args, la, torch):
     """Short run for rocprofv3 counter passes: a 256 MiB device copy (the
     calibration kernel) then a few prefill steps of the workload."""
@@ -380,10 +427,15 @@ def profile_pass(args, la, torch):
     dev = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
     q, k, v = dev(w["q"]), dev(w["k"]), dev(w["v"])
     cu = torch.from_numpy(w["cu"]).cuda()
-    for _ in range(args.steps):
-        la.prefill(q, k, v, cu, block=args.block or w["block"])
+    if args.profile_backward:
+        dout = dev(la_inputs.normal(la_inputs.WORKLOADS[args.workload]["seed"], 8, q.shape, "bf16", 1.0))
+        for _ in range(args.steps):
+            la.backward(q, k, v, dout, cu, block=args.block or w["block"], want_dkv_in=False)
+    else:
+        for _ in range(args.steps):
+            la.prefill(q, k, v, cu, block=args.block or w["block"])
     torch.cuda.synchronize()
-    print(json.dumps({"profile_pass": args.workload, "steps": args.steps}))
+    print(json.dumps({"profile_pass": args.workload, "steps": args.steps, "backward": args.profile_backward}))
 
 
 def main():
@@ -405,6 +457,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--profile-pass", action="store_true")
+    ap.add_argument("--profile-backward", action="store_true", help="with --profile-pass: backward calls")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -437,6 +490,9 @@ def main():
             part["roofline"]["frac_of_measured_copy"] = part["roofline"]["achieved"] / copy
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w)
+        rec["error_vs_oracle"] = w.get("error_vs_oracle")
+        if "decode" in rec:
+            rec["decode"]["cpu_baseline"] = decode_cpu_baseline(DECODE_SAMPLE["S"])
     else:
         rec["cpu_baseline"] = None
     print(json.dumps(rec))
