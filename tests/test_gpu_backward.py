@@ -5,7 +5,8 @@ Cases: ragged packed documents (empty ones included) with and without
 incoming states and final-state gradients, on both block loops (bf16 d = 128
 and 64 on the gfx950 loop, bf16 block 32 and fp32 on the generic loop), with
 segment splitting and the scan path (which in the reverse passes run over
-documents read back to front), and the 8192-token x 8-head workload in full."""
+documents read back to front), the 8192-token x 8-head workload in full, and
+the 1M-token workload on the GPU in full, checked exactly on windows."""
 import numpy as np
 import pytest
 
@@ -104,6 +105,38 @@ def test_backward_prefill_8k_workload():
     log(f"  backward prefill_8k T={T} H={H}")
     got = run(w["q"], w["k"], w["v"], dout, w["cu"], w["block"], None, None)
     check(w["q"], w["k"], w["v"], dout, w["cu"], None, None, got, False, "backward 8k")
+
+
+def test_backward_long_1m_windows():
+    """The 1M-token x 8-head workload's backward in full on the GPU, checked
+    exactly on windows: the first tokens, a window across a segment end in
+    the middle, and the last tokens.  For a window [a, b) the oracle takes
+    the forward state before it (sum of k^T v over [0, a)) and the reverse
+    state after it (sum of q^T dO over [b, T)) as boundary states and runs
+    its backward on the window alone, which gives that window's dq, dk, dv
+    of the whole sequence."""
+    import torch
+
+    w = la_inputs.prefill_inputs("long_1m")
+    T, H, d = w["T"], w["H"], w["d"]
+    q, k, v = w["q"], w["k"], w["v"]
+    dout = la_inputs.normal(la_inputs.WORKLOADS["long_1m"]["seed"], 8, (T, H, d), "bf16", 1.0)
+    plan = la.la_prefill_plan(T, 1, H, d, 64, la.LA_BF16)
+    log(f"  backward long_1m plan={plan}")
+    dq, dk, dv, _ = la.backward(to_dev(q), to_dev(k), to_dev(v), to_dev(dout), to_dev(w["cu"]), block=64,
+                                want_dkv_in=False)
+    torch.cuda.synchronize()
+    n, L = 4096, plan["seg_len"]
+    for a in (0, (plan["num_segments"] // 2) * L - n // 2, T - n):
+        b = a + n
+        kv_a = oracle.recurrent(q[:a], k[:a], v[:a], np.array([0, a], np.int32), want_o=False)[1] if a else None
+        g_b = oracle.recurrent(q[b:], q[b:], dout[b:], np.array([0, T - b], np.int32), want_o=False)[1] \
+            if b < T else None
+        ref = oracle.backward(q[a:b], k[a:b], v[a:b], dout[a:b], np.array([0, n], np.int32), kv_in=kv_a,
+                              dkv_out=g_b, want_dkv_in=False)
+        for name, g, r in zip(("dq", "dk", "dv"), (dq, dk, dv), ref[:3]):
+            ErrAcc().add(to_host(g[a:b]), r).check(False, f"long_1m window [{a}, {b}) {name}")
+        log(f"    window [{a}, {b}) compared")
 
 
 def test_backward_rejects_aliasing():
