@@ -11,7 +11,9 @@ copied to HBM before timing, and rotated over several input sets so that the
 timed steps read HBM rather than the 256 MB last-level cache.  The decode
 workload (256 sequences x 64 heads, fp32 state, 1000 steps) is timed in the
 same run and reported under "decode", and the prefill's backward
-(la_prefill_backward: dq, dk, dv) over the same workload under "backward".
+(la_prefill_backward: dq, dk, dv) over the same workload under "backward", with
+a forward + backward pair sharing the forward's workspace under
+"backward"/"train_step".
 
 Prints one JSON line.  `roofline` is for the block-loop kernel: algorithmic
 bytes (q, k, v read + o written, 8 d bytes per token-head) per launch over its
@@ -385,11 +387,40 @@ def bench_backward(args, la, torch, hip, w, dev_sets):
     hip.destroy(e1)
     algo = T * H * 14 * d * esz // 2
     achieved = algo * K / gpu_s / 1e9
-    return {"workload": w["name"], "value": T * H * K / wall, "unit": "token·heads/s", "steps": K,
-            "ms_per_step": wall / K * 1e3, "gpu_ms_per_step": gpu_s / K * 1e3,
-            "roofline": {"bound": "hbm", "kernel": "la_prefill_backward (3 prefill passes)", "achieved": achieved,
-                         "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                         "algorithmic_bytes": algo}}
+    rec = {"workload": w["name"], "value": T * H * K / wall, "unit": "token·heads/s", "steps": K,
+           "ms_per_step": wall / K * 1e3, "gpu_ms_per_step": gpu_s / K * 1e3,
+           "roofline": {"bound": "hbm", "kernel": "la_prefill_backward (3 prefill passes)", "achieved": achieved,
+                        "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                        "algorithmic_bytes": algo}}
+
+    # One training step's attention work: the forward, then the backward handed
+    # the forward's workspace (its dq pass reuses the forward's segment states).
+    fo = torch.empty_like(dout0)
+    fkv = torch.empty((num_seqs, H, d, d), dtype=torch.float32, device="cuda")
+
+    def train(i):
+        q, k, v, dout = sets[i % len(sets)]
+        la.prefill(q, k, v, cu, block=block, out=fo, kv_state_out=fkv, workspace=ws, **opts)
+        la.backward(q, k, v, dout, cu, block=block, want_dkv_in=False, out=outs, forward_workspace=ws, **opts)
+
+    for i in range(max(1, args.warmup // 4)):
+        train(i)
+    e0, e1 = hip.event(), hip.event()
+    torch.cuda.synchronize()
+    hip.record(e0, stream)
+    for i in range(K):
+        train(i)
+    hip.record(e1, stream)
+    torch.cuda.synchronize()
+    tr_s = hip.elapsed_ms(e0, e1) / 1e3
+    hip.destroy(e0)
+    hip.destroy(e1)
+    talgo = T * H * 22 * d * esz // 2  # forward 8d + backward 14d bytes per token-head
+    tach = talgo * K / tr_s / 1e9
+    rec["train_step"] = {"value": T * H * K / tr_s, "unit": "token·heads/s", "gpu_ms_per_step": tr_s / K * 1e3,
+                         "roofline": {"bound": "hbm", "achieved": tach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                      "frac": tach / HBM_PEAK_GBS, "algorithmic_bytes": talgo}}
+    return rec
 
 
 def decode_cpu_baseline(S_sample, steps: int = 200) -> dict:

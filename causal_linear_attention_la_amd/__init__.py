@@ -32,7 +32,8 @@ class LAError(RuntimeError):
 class la_prefill_opts(ctypes.Structure):
     _fields_ = [("seg_len", ctypes.c_int32), ("value_slices", ctypes.c_int32), ("force_scan", ctypes.c_int32),
                 ("variant", ctypes.c_int32), ("main_begin_event", ctypes.c_void_p),
-                ("main_end_event", ctypes.c_void_p), ("slots", ctypes.c_int32)]
+                ("main_end_event", ctypes.c_void_p), ("slots", ctypes.c_int32),
+                ("forward_states", ctypes.c_int32)]
 
 
 class la_prefill_plan_info(ctypes.Structure):
@@ -125,9 +126,9 @@ def la_prefill_workspace_size(total_tokens, num_seqs, H, d, block, dtype) -> int
 
 
 def make_opts(seg_len: int = 0, value_slices: int = 0, force_scan: bool = False, begin_event=None,
-              end_event=None, variant: int = 0, slots: int = 0) -> la_prefill_opts:
+              end_event=None, variant: int = 0, slots: int = 0, forward_states: bool = False) -> la_prefill_opts:
     return la_prefill_opts(int(seg_len), int(value_slices), 1 if force_scan else 0, int(variant),
-                           _event_ptr(begin_event), _event_ptr(end_event), int(slots))
+                           _event_ptr(begin_event), _event_ptr(end_event), int(slots), 1 if forward_states else 0)
 
 
 def la_prefill_workspace_size_ex(total_tokens, num_seqs, H, d, block, dtype, opts=None) -> int:
@@ -215,12 +216,15 @@ def prefill(q, k, v, cu_seqlens, block: int = 64, want_state: bool = True, out=N
 
 def backward(q, k, v, dout, cu_seqlens, block: int = 64, kv_state_in=None, dkv_state_out=None,
              want_dkv_in: bool = True, workspace=None, seg_len: int = 0, value_slices: int = 0,
-             force_scan: bool = False, stream=None, variant: int = 0, out=None, slots: int = 0):
+             force_scan: bool = False, stream=None, variant: int = 0, out=None, slots: int = 0,
+             forward_workspace=None):
     """Gradients of the prefill (la_prefill_backward).  dout is dL/do
     ([T, H, d], same dtype as q); dkv_state_out (fp32 [num_seqs, H, d, d] or
     None) is dL/dkv_state_out.  out = (dq, dk, dv, dkv_in) preallocated
-    (dkv_in may be None), else they are allocated.  Returns (dq, dk, dv,
-    dkv_state_in or None)."""
+    (dkv_in may be None), else they are allocated.  forward_workspace: the
+    workspace the forward call on the same inputs and options used, untouched
+    since; the backward then reuses (and overwrites) its segment states.
+    Returns (dq, dk, dv, dkv_state_in or None)."""
     import torch
 
     T, H, d = q.shape
@@ -231,10 +235,12 @@ def backward(q, k, v, dout, cu_seqlens, block: int = 64, kv_state_in=None, dkv_s
     else:
         dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
         dkv_in = torch.empty((num_seqs, H, d, d), dtype=torch.float32, device=q.device) if want_dkv_in else None
-    opts = make_opts(seg_len, value_slices, force_scan, None, None, variant, slots)
+    opts = make_opts(seg_len, value_slices, force_scan, None, None, variant, slots, forward_workspace is not None)
     need = la_prefill_workspace_size_ex(T, num_seqs, H, d, block, dt, opts)
-    ws = workspace
+    ws = forward_workspace if forward_workspace is not None else workspace
     if need and (ws is None or ws.numel() * ws.element_size() < need):
+        if forward_workspace is not None:
+            raise ValueError("forward_workspace is smaller than this plan's workspace")
         ws = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_bytes = ws.numel() * ws.element_size() if ws is not None else 0
     st = la_prefill_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(cu_seqlens), H, d, block, _ptr(kv_state_in),

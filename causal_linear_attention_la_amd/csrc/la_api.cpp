@@ -122,9 +122,20 @@ la_status la_prefill_backward(const void* q, const void* k, const void* v, const
     st = la::validate_backward_outputs(q, k, v, dout, kv_state_in, dkv_state_out, dq, dk, dv, dkv_state_in, num_seqs,
                                        H, d, total_tokens, (int)dtype);
     if (st != LA_OK) return st;
-    // dQ: forward pass with query dO, key V, value K, from KV_in^T
+    // dQ: forward pass with query dO, key V, value K, from KV_in^T.  Its
+    // segment states (sums of v^T k) are the transposes of the forward's
+    // (sums of k^T v): when the caller hands back the forward's workspace, they
+    // are transposed in place instead of computed again.
+    int reuse_fwd = 0;
+    if (opts && opts->forward_states && p1.variant == 2 && p1.nseg > 1) {
+        float* ws = reinterpret_cast<float*>(static_cast<char*>(workspace) + p1.ws_states_off);
+        if (la::launch_ws_transpose(ws, (int64_t)(p1.nseg - 1) * H, d, p1.W, static_cast<hipStream_t>(stream)) !=
+            hipSuccess)
+            return LA_ERR_HIP;
+        reuse_fwd = 1;
+    }
     st = enqueue_prefill(p1, dout, v, k, dq, cu_seqlens, H, d, block, kv_state_in, 1, nullptr, 0, num_seqs,
-                         total_tokens, dtype, workspace, stream, nullptr, nullptr);
+                         total_tokens, dtype, workspace, stream, nullptr, nullptr, reuse_fwd);
     if (st != LA_OK) return st;
     // dV (and dKV_in, the reverse state after each document's first token):
     // reverse pass with query K, key Q, value dO, from dKV_out

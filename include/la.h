@@ -135,6 +135,14 @@ typedef struct {
     int32_t slots;          /* tile slots of the transpose-read loop: 0 = automatic
                                (3 on segments of 16 blocks or more), 2, or 3 (loads
                                two blocks ahead; d = 128 only) */
+    int32_t forward_states; /* la_prefill_backward only (the forward entry points
+                               ignore it): 1 = `workspace` still holds what the
+                               forward call (la_prefill / _ex / _resume) on the same
+                               q, k, v, cu_seqlens, shapes, dtype and opts left in it;
+                               the dq pass then takes those segment states
+                               (transposed) instead of computing them again.  The
+                               contents cannot be checked: with any other workspace
+                               the gradients are wrong. */
 } la_prefill_opts;
 
 /* The decomposition a prefill call will use (for reports and tests). */

@@ -13,7 +13,7 @@ import pytest
 import causal_linear_attention_la_amd as la
 import la_inputs
 import oracle
-from gpu_helpers import ErrAcc, log, to_dev, to_host
+from gpu_helpers import ErrAcc, as_f64, log, to_dev, to_host
 
 pytestmark = pytest.mark.gpu
 
@@ -96,6 +96,39 @@ def test_backward_tile_slots(slots):
     log(f"  backward slots={slots}")
     got = run(q, k, v, dout, cu, 64, kv_in, dkv_out, seg_len=1024, slots=slots)
     check(q, k, v, dout, cu, kv_in, dkv_out, got, False, f"backward slots {slots}")
+
+
+@pytest.mark.parametrize("opts", [dict(seg_len=64), dict(seg_len=192), dict(seg_len=256, force_scan=True),
+                                  dict(seg_len=128, value_slices=2)], ids=str)
+@pytest.mark.parametrize("with_states", [False, True])
+def test_backward_with_forward_states(opts, with_states):
+    """The backward handed the forward's workspace (forward_states): the dq
+    pass takes the forward's segment states, transposed, instead of its own.
+    Against the oracle, and close to the backward computed from scratch."""
+    import torch
+
+    lens = [300, 0, 1, 700, 64, 0, 129, 1500]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    T, H, d = int(cu[-1]), 3, 128
+    q, k, v, dout = inputs(151, T, H, d, "bf16")
+    kv_in = states(152, 7, len(lens), H, d, float(np.sqrt(2000)) / d) if with_states else None
+    dkv_out = states(153, 9, len(lens), H, d, 1.0) if with_states else None
+    qd, kd, vd, dod, cud = to_dev(q), to_dev(k), to_dev(v), to_dev(dout), to_dev(cu)
+    kin = None if kv_in is None else to_dev(kv_in)
+    dko = None if dkv_out is None else to_dev(dkv_out)
+    need = la.la_prefill_workspace_size_ex(T, len(lens), H, d, 64, la.LA_BF16, la.make_opts(**opts))
+    assert need > 0
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    log(f"  backward with forward states {opts} states={with_states}")
+    la.prefill(qd, kd, vd, cud, block=64, workspace=ws, kv_state_in=kin, **opts)
+    got = la.backward(qd, kd, vd, dod, cud, block=64, kv_state_in=kin, dkv_state_out=dko, forward_workspace=ws, **opts)
+    fresh = la.backward(qd, kd, vd, dod, cud, block=64, kv_state_in=kin, dkv_state_out=dko, **opts)
+    torch.cuda.synchronize()
+    got = tuple(to_host(x) for x in got)
+    check(q, k, v, dout, cu, kv_in, dkv_out, got, False, "backward with forward states")
+    ErrAcc().add(got[0], as_f64(to_host(fresh[0]))).check(False, "dq reused vs fresh")
+    for a, b in zip(got[1:], fresh[1:]):
+        assert np.array_equal(a, to_host(b)), "only the dq pass may change"
 
 
 def test_backward_prefill_8k_workload():
