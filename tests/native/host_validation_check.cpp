@@ -53,6 +53,17 @@ int main() {
     EXPECT(make_plan(8192, 1, 8, 128, 64, LA_BF16, &o1, &p) == LA_ERR_UNSUPPORTED);
     o1.value_slices = 8;
     EXPECT(make_plan(8192, 1, 8, 128, 64, LA_BF16, &o1, &p) == LA_ERR_UNSUPPORTED);
+    // short segments that would need the scan go to two slices of twice the length
+    EXPECT(make_plan(8192, 1, 8, 128, 64, LA_BF16, nullptr, &p) == LA_OK && p.S == 2 && p.L == 512 && p.nseg == 16 &&
+           p.scan == 0 && p.units == 256);
+    EXPECT(make_plan(16384, 1, 8, 128, 64, LA_BF16, nullptr, &p) == LA_OK && p.S == 1 && p.L == 512 && p.scan == 1);
+    EXPECT(make_plan(4096, 1, 8, 128, 64, LA_BF16, nullptr, &p) == LA_OK && p.S == 2 && p.L == 256 && p.scan == 0);
+    la_prefill_opts o4{};
+    o4.force_scan = 1;
+    EXPECT(make_plan(8192, 1, 8, 128, 64, LA_BF16, &o4, &p) == LA_OK && p.S == 1 && p.L == 256 && p.scan == 1);
+    o4.force_scan = 0;
+    o4.variant = 1;
+    EXPECT(make_plan(8192, 1, 8, 128, 64, LA_BF16, &o4, &p) == LA_OK && p.S == 1 && p.L == 256);
     // tile slots: three on long segments of the d = 128 transpose-read loop, two otherwise
     EXPECT(make_plan(8192, 1, 8, 128, 64, LA_BF16, nullptr, &p) == LA_OK && p.slots == 2);
     EXPECT(make_plan(1048576, 1, 8, 128, 64, LA_BF16, nullptr, &p) == LA_OK && p.slots == 3);
