@@ -133,7 +133,7 @@ def test_host_validation_under_sanitizers(tmp_path):
 
 def test_no_undefined_library_symbols(lib):
     """Every kernel launch stub the library calls is defined in it (a missing
-    template instantiation would only show up as a load failure on a GPU machine)."""
+    template instantiation would otherwise only show up as a load failure at run time)."""
     out = subprocess.run(["nm", "-D", "--undefined-only", la.LIB_PATH], capture_output=True, text=True).stdout
     missing = [l for l in out.splitlines() if "_ZN2la" in l]
     assert not missing, missing
