@@ -1,6 +1,7 @@
 // Host-only validation and planning (see la_host.h).
 #include "la_host.h"
 
+#include <algorithm>
 #include <climits>
 
 #include "la_tiles.h"
@@ -17,6 +18,7 @@ constexpr int kMaxLookback = 16;  // a unit sums at most this many segment state
 // segments of at least this many blocks; shorter ones start faster with two.
 constexpr int kThreeSlotMinBlocks = 16;
 constexpr int kShortSegmentBlocks = 4;
+constexpr int64_t kMaxLookbackWide = 4;  // the same on the full-width transpose-read loop
 
 bool is_pow2_in(int32_t x, int32_t lo, int32_t hi) {
     if (x < lo || x > hi) return false;
@@ -81,6 +83,24 @@ la_status make_plan(int64_t T, int32_t num_seqs, int32_t H, int32_t d, int32_t b
     if (variant == 2 && !v2_ok(p.S)) return LA_ERR_UNSUPPORTED;
     p.variant = (variant == 0 ? v2_ok(p.S) : variant == 2) ? 2 : 1;  // the loop that will run
 
+    // Look-back or scan for segments of length L with slices of width W.
+    // Without the scan a unit that starts inside a document sums the states of
+    // that document's earlier segments in its prologue, on its own critical
+    // path.  Measured against the scan's extra launch: the look-back wins for
+    // up to kMaxLookback predecessors on the transpose-read loop with
+    // 64-column slices, but for only a few on the full-width loop, whose
+    // registers leave no room to keep those loads in flight (3 predecessors:
+    // look-back 7-10 % faster; 7 or more: 4-10 % slower).  The longest
+    // document is estimated from the mean length.
+    auto needs_scan = [&](int64_t L, int32_t W) {
+        const int64_t ns = T == 0 ? 1 : (T + L - 1) / L;
+        if (ns <= 1) return false;
+        const int64_t mean_len = (T + num_seqs - 1) / num_seqs;
+        const int64_t span = std::min<int64_t>(ns, num_seqs == 1 ? ns : (mean_len + L - 1) / L + 1);
+        const int64_t max_preds = (p.variant == 2 && W >= 128) ? kMaxLookbackWide : kMaxLookback;
+        return ns - 1 > kMaxLookback || span - 1 > max_preds;
+    };
+
     if (opts && opts->seg_len != 0) {
         if (opts->seg_len < block || opts->seg_len % block != 0) return LA_ERR_UNSUPPORTED;
         p.L = opts->seg_len;
@@ -94,14 +114,14 @@ la_status make_plan(int64_t T, int32_t num_seqs, int32_t H, int32_t d, int32_t b
         if (L > INT32_MAX / 2) L = (INT32_MAX / 2 / block) * block;
         // Segments of at most kShortSegmentBlocks blocks whose documents would
         // need the scan: two value slices with twice the segment length keep
-        // the unit count, halve the segments per document and need no scan,
-        // which is faster while segments are this short (8192 tokens x 8
-        // heads: 52.7 -> 48.2 us per call); longer ones do better unsplit.
-        const int64_t nseg0 = (T + L - 1) / L;
+        // the unit count, halve the segments per document and, at half width,
+        // can sum their predecessors without the scan, which is faster while
+        // segments are this short (8192 tokens x 8 heads: 52.7 -> 48.2 us per
+        // call; 2048 x 32: 37.9 -> 34.8 us); longer ones do better unsplit.
         const bool auto_s = !(opts && opts->value_slices != 0);
-        if (auto_s && !(opts && opts->force_scan) && p.variant == 2 && nseg0 - 1 > kMaxLookback &&
-            L / block <= kShortSegmentBlocks && (nseg0 + 1) / 2 - 1 <= kMaxLookback && slice_ok(2 * p.S) &&
-            v2_ok(2 * p.S) && 2 * L <= INT32_MAX / 2) {
+        if (auto_s && !(opts && opts->force_scan) && p.variant == 2 && L / block <= kShortSegmentBlocks &&
+            needs_scan(L, p.W) && slice_ok(2 * p.S) && v2_ok(2 * p.S) && 2 * L <= INT32_MAX / 2 &&
+            !needs_scan(2 * L, d / (2 * p.S))) {
             p.S *= 2;
             p.W = d / p.S;
             L *= 2;
@@ -113,7 +133,7 @@ la_status make_plan(int64_t T, int32_t num_seqs, int32_t H, int32_t d, int32_t b
     p.nseg = (int32_t)nseg;
     p.units = nseg * (int64_t)H * p.S;
     if (p.units > (int64_t)INT32_MAX * 8) return LA_ERR_UNSUPPORTED;
-    p.scan = (p.nseg - 1 > kMaxLookback || (opts && opts->force_scan)) && p.nseg > 1 ? 1 : 0;
+    p.scan = p.nseg > 1 && ((opts && opts->force_scan) || needs_scan(p.L, p.W)) ? 1 : 0;
     const int32_t slots = opts ? opts->slots : 0;
     if (!(slots == 0 || slots == 2 || slots == 3)) return LA_ERR_UNSUPPORTED;
     const bool three_ok = p.variant == 2 && d == 128;

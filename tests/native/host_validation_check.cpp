@@ -58,6 +58,13 @@ int main() {
            p.scan == 0 && p.units == 256);
     EXPECT(make_plan(16384, 1, 8, 128, 64, LA_BF16, nullptr, &p) == LA_OK && p.S == 1 && p.L == 512 && p.scan == 1);
     EXPECT(make_plan(4096, 1, 8, 128, 64, LA_BF16, nullptr, &p) == LA_OK && p.S == 2 && p.L == 256 && p.scan == 0);
+    // look-back or scan: few predecessors on the full-width loop, up to 16 on 64-column slices
+    EXPECT(make_plan(4096, 1, 32, 128, 64, LA_BF16, nullptr, &p) == LA_OK && p.W == 128 && p.nseg == 8 && p.scan == 1);
+    EXPECT(make_plan(2048, 1, 32, 128, 64, LA_BF16, nullptr, &p) == LA_OK && p.S == 2 && p.L == 512 && p.scan == 0);
+    EXPECT(make_plan(4096, 1, 16, 128, 64, LA_BF16, nullptr, &p) == LA_OK && p.S == 2 && p.L == 512 && p.scan == 0);
+    EXPECT(make_plan(4096, 1, 64, 128, 64, LA_BF16, nullptr, &p) == LA_OK && p.W == 128 && p.nseg == 4 && p.scan == 0);
+    EXPECT(make_plan(65536, 64, 16, 128, 64, LA_BF16, nullptr, &p) == LA_OK && p.nseg == 16 && p.scan == 0);
+    EXPECT(make_plan(65536, 1, 16, 128, 64, LA_BF16, nullptr, &p) == LA_OK && p.nseg == 16 && p.scan == 1);
     la_prefill_opts o4{};
     o4.force_scan = 1;
     EXPECT(make_plan(8192, 1, 8, 128, 64, LA_BF16, &o4, &p) == LA_OK && p.S == 1 && p.L == 256 && p.scan == 1);
