@@ -6,7 +6,8 @@ incoming states and final-state gradients, on both block loops (bf16 d = 128
 and 64 on the gfx950 loop, bf16 block 32 and fp32 on the generic loop), with
 segment splitting and the scan path (which in the reverse passes run over
 documents read back to front), the 8192-token x 8-head workload in full, and
-the 1M-token workload on the GPU in full, checked exactly on windows."""
+the 1M-token workload on the GPU in full, checked exactly on windows, and the
+131072-token packed workload in full, two heads compared against the oracle."""
 import numpy as np
 import pytest
 
@@ -170,6 +171,30 @@ def test_backward_long_1m_windows():
         for name, g, r in zip(("dq", "dk", "dv"), (dq, dk, dv), ref[:3]):
             ErrAcc().add(to_host(g[a:b]), r).check(False, f"long_1m window [{a}, {b}) {name}")
         log(f"    window [{a}, {b}) compared")
+
+
+def test_backward_varlen_128k_heads():
+    """The 131072-token x 64-head packed workload (20 documents) backward in
+    full on the GPU; two heads compared in full against the oracle's backward
+    run on those heads alone (heads are independent)."""
+    import torch
+
+    w = la_inputs.prefill_inputs("varlen_128k")
+    T, H, d = w["T"], w["H"], w["d"]
+    q, k, v, cu = w["q"], w["k"], w["v"], w["cu"]
+    dout = la_inputs.normal(la_inputs.WORKLOADS["varlen_128k"]["seed"], 8, (T, H, d), "bf16", 1.0)
+    plan = la.la_prefill_plan(T, len(cu) - 1, H, d, 64, la.LA_BF16)
+    log(f"  backward varlen_128k docs={len(cu) - 1} plan={plan}")
+    dq, dk, dv, dki = la.backward(to_dev(q), to_dev(k), to_dev(v), to_dev(dout), to_dev(cu), block=64)
+    torch.cuda.synchronize()
+    for h0 in (0, 37):
+        sl = slice(h0, h0 + 2)
+        part = [np.ascontiguousarray(x[:, sl]) for x in (q, k, v, dout)]
+        ref = oracle.backward(*part, cu)
+        for name, g, r in zip(("dq", "dk", "dv"), (dq, dk, dv), ref[:3]):
+            ErrAcc().add(to_host(g[:, sl]), r).check(False, f"varlen heads {h0}..{h0 + 1} {name}")
+        ErrAcc().add(to_host(dki[:, sl]), ref[3]).check(True, f"varlen heads {h0}..{h0 + 1} dkv_in")
+        log(f"    heads {h0}..{h0 + 1} compared")
 
 
 def test_backward_rejects_aliasing():
