@@ -511,14 +511,29 @@ __global__ __launch_bounds__(kThreads, 1) void la_prefill_main_v2(PrefillParams 
     };
     // O^T += V^T P^T for the previous block, then its rows are stored.
     auto finish = [&](int pb0, int pnb) {
+        // With one tile column per wave there are registers to fetch every P
+        // fragment before the first product, so the LDS latency is paid once
+        // (the full-width loop has none to spare and reads them one by one).
+        if constexpr (NCW == 1) {
+            Frag<bf16_t> pfs[6];  // (band, chunk) = (0,0) (1,0) (2,0) (2,1) (3,0) (3,1)
 #pragma unroll
-        for (int b = 0; b < NQT; ++b) {
+            for (int b = 0, n = 0; b < NQT; ++b)
 #pragma unroll
-            for (int kc = 0; kc <= b / 2; ++kc) {
-                Frag<bf16_t> pf;
-                load_row<PP>(pf, Ps, 16 * b + li, 32 * kc, g);
+                for (int kc = 0; kc <= b / 2; ++kc, ++n) load_row<PP>(pfs[n], Ps, 16 * b + li, 32 * kc, g);
 #pragma unroll
-                for (int c = 0; c < NCW; ++c) mma(oacc[b][c], vfr[c][kc], pf);
+            for (int b = 0, n = 0; b < NQT; ++b)
+#pragma unroll
+                for (int kc = 0; kc <= b / 2; ++kc, ++n) mma(oacc[b][0], vfr[0][kc], pfs[n]);
+        } else {
+#pragma unroll
+            for (int b = 0; b < NQT; ++b) {
+#pragma unroll
+                for (int kc = 0; kc <= b / 2; ++kc) {
+                    Frag<bf16_t> pf;
+                    load_row<PP>(pf, Ps, 16 * b + li, 32 * kc, g);
+#pragma unroll
+                    for (int c = 0; c < NCW; ++c) mma(oacc[b][c], vfr[c][kc], pf);
+                }
             }
         }
         const __amdgpu_buffer_rsrc_t ro =
@@ -620,13 +635,24 @@ __global__ __launch_bounds__(kThreads, 1) void la_prefill_main_v2(PrefillParams 
             }
             Frag<bf16_t> kf;
             load_row<D>(kf, Ks, 16 * wave + li, 32 * m, g);
+            if constexpr (NCW == 1) {  // (as in finish: all Q fragments of the chunk first)
+                Frag<bf16_t> qfs[NQT];
 #pragma unroll
-            for (int b = 0; b < NQT; ++b) {
-                Frag<bf16_t> qf;
-                load_row<D>(qf, Qs, 16 * b + li, 32 * m, g);
+                for (int b = 0; b < NQT; ++b) load_row<D>(qfs[b], Qs, 16 * b + li, 32 * m, g);
 #pragma unroll
-                for (int c = 0; c < NCW; ++c) mma(oacc[b][c], kvf[c], qf);
-                mma(sacc[b], kf, qf);
+                for (int b = 0; b < NQT; ++b) {
+                    mma(oacc[b][0], kvf[0], qfs[b]);
+                    mma(sacc[b], kf, qfs[b]);
+                }
+            } else {
+#pragma unroll
+                for (int b = 0; b < NQT; ++b) {
+                    Frag<bf16_t> qf;
+                    load_row<D>(qf, Qs, 16 * b + li, 32 * m, g);
+#pragma unroll
+                    for (int c = 0; c < NCW; ++c) mma(oacc[b][c], kvf[c], qf);
+                    mma(sacc[b], kf, qf);
+                }
             }
         }
         issue_tile(cf, Slot<FILL>{}, Slot<2>{});
