@@ -47,10 +47,15 @@ DECODE_SOURCES = ["la_decode_kernels.h", "la_device.h"]
 
 
 def sources_sha(names) -> str:
+    """Hash of the kernel sources' code (// comments and blank lines left
+    out, so that a comment edit does not orphan the counter summaries)."""
     h = hashlib.sha256()
     for n in names:
-        with open(os.path.join(ROOT, "causal_linear_attention_la_amd", "csrc", n), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "causal_linear_attention_la_amd", "csrc", n), encoding="utf-8") as f:
+            for line in f:
+                code = line.split("//", 1)[0].rstrip()
+                if code:
+                    h.update(code.encode() + b"\n")
     return h.hexdigest()[:16]
 
 

@@ -4,10 +4,11 @@
 // Same work decomposition and results contract as la_prefill_kernels.h; the
 // block loop is organised for gfx950:
 //  * Q, K, V tiles go from HBM straight into LDS with buffer loads in LDS-DMA
-//    mode (no staging registers), double buffered: the loads of block j+1
-//    are issued when block j starts, so one iteration hides each load.  Rows
-//    past the end of a partial block lie outside the buffer range and arrive
-//    as zeros.
+//    mode (no staging registers), into two or three tile slots: the loads of
+//    block j+1 (or j+2) are issued during iteration j, so each load has one
+//    (or two) iterations to arrive.  Rows past the end of a partial block
+//    lie outside the buffer range and arrive as zeros.  In reverse mode (the
+//    backward's passes) the same loads mirror the rows of each block.
 //  * Tiles are row-major with 128- or 256-byte rows and no padding; the
 //    8-byte units of row r are permuted by XOR with an even mask, so 16-byte
 //    DMA slots stay whole.  The masks make every read pattern conflict free
@@ -34,6 +35,9 @@
 //    iteration j+1 between its two barriers, where no tile buffer is being
 //    written; its output rows are stored with buffer stores (rows past a
 //    partial block are dropped by the range check).
+//  * With one 16-column tile per wave (64-column slices) the loop has the
+//    registers to issue a group's fragment reads before the products that use
+//    them, paying one LDS latency per group; the full-width loop has not.
 #pragma once
 #include "la_prefill_kernels.h"
 
