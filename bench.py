@@ -17,8 +17,9 @@ a forward + backward pair sharing the forward's workspace under
 
 Prints one JSON line.  `roofline` is for the block-loop kernel: algorithmic
 bytes (q, k, v read + o written, 8 d bytes per token-head) per launch over its
-average duration, measured with HIP events recorded on the launch stream
-around every launch inside the timed region.  `cpu_baseline` times the fp64
+average duration, measured with HIP events stamped on the launch stream
+around every 8th launch inside the timed region (--event-stride; stamping
+every launch costs several microseconds per step).  `cpu_baseline` times the fp64
 oracle (the recurrent form) on the host cores for the same workload.
 """
 from __future__ import annotations
@@ -214,15 +215,23 @@ def bench_prefill(args, la, torch, hip):
     torch.cuda.synchronize()
 
     K = args.steps
-    evs = [(hip.event(), hip.event()) for _ in range(K)]
+    # The block-loop kernel of every event_stride-th step in the timed region
+    # is launched with start/end events (hipExtLaunchKernel); stamping every
+    # launch would itself cost several microseconds per step.
+    # (short timed regions -- long steps -- stamp every launch: there the cost is noise)
+    stride = max(1, args.event_stride) if args.event_stride else (8 if args.steps >= 128 else 1)
+    evs = {i: (hip.event(), hip.event()) for i in range(0, K, stride)}
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K):
-        step(i, evs[i][0], evs[i][1])
+        if i in evs:
+            step(i, evs[i][0], evs[i][1])
+        else:
+            step(i)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    kernel_ms = [hip.elapsed_ms(a, b) for a, b in evs]
-    for a, b in evs:
+    kernel_ms = [hip.elapsed_ms(a, b) for a, b in evs.values()]
+    for a, b in evs.values():
         hip.destroy(a)
         hip.destroy(b)
 
@@ -273,7 +282,7 @@ def bench_prefill(args, la, torch, hip):
         "config": {"workload": name, "documents": num_seqs, "heads": H, "tokens": T, "head_dim": d, "block": block,
                    "seg_len": plan["seg_len"], "value_slices": plan["value_slices"],
                    "segments": plan["num_segments"], "scan": plan["scan"], "slots": plan["slots"],
-                   "workgroups": plan["units"],
+                   "workgroups": plan["units"], "event_stride": stride,
                    "input_sets": nsets},
         "roofline": {"bound": "hbm", "kernel": kname, "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
@@ -487,6 +496,9 @@ def main():
     ap.add_argument("--force-scan", action="store_true")
     ap.add_argument("--slots", type=int, default=0, help="tile slots of the block loop: 0 automatic, 2 or 3")
     ap.add_argument("--rotate", type=int, default=8, help="input sets cycled through the timed steps")
+    ap.add_argument("--event-stride", type=int, default=0,
+                    help="stamp the block-loop kernel of every n-th timed step with events "
+                         "(0: every 8th with 128 or more steps, else every one)")
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
