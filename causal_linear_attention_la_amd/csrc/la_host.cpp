@@ -17,8 +17,10 @@ constexpr int kMaxLookback = 16;  // a unit sums at most this many segment state
 // The transpose-read loop takes three tile slots (loads two blocks ahead) on
 // segments of at least this many blocks; shorter ones start faster with two.
 constexpr int kThreeSlotMinBlocks = 16;
-constexpr int kShortSegmentBlocks = 4;
-constexpr int64_t kMaxLookbackWide = 4;  // the same on the full-width transpose-read loop
+constexpr int kShortSegmentBlocks = 6;
+// The full-width transpose-read loop sums at most this many on segments of
+// more than kThreeSlotMinBlocks blocks.
+constexpr int kMaxLookbackWideLong = 8;
 
 bool is_pow2_in(int32_t x, int32_t lo, int32_t hi) {
     if (x < lo || x > hi) return false;
@@ -83,22 +85,23 @@ la_status make_plan(int64_t T, int32_t num_seqs, int32_t H, int32_t d, int32_t b
     if (variant == 2 && !v2_ok(p.S)) return LA_ERR_UNSUPPORTED;
     p.variant = (variant == 0 ? v2_ok(p.S) : variant == 2) ? 2 : 1;  // the loop that will run
 
-    // Look-back or scan for segments of length L with slices of width W.
-    // Without the scan a unit that starts inside a document sums the states of
-    // that document's earlier segments in its prologue, on its own critical
-    // path.  Measured against the scan's extra launch: the look-back wins for
-    // up to kMaxLookback predecessors on the transpose-read loop with
-    // 64-column slices, but for only a few on the full-width loop, whose
-    // registers leave no room to keep those loads in flight (3 predecessors:
-    // look-back 7-10 % faster; 7 or more: 4-10 % slower).  The longest
-    // document is estimated from the mean length.
+    // Look-back or scan for segments of length L.  Without the scan a unit
+    // that starts inside a document sums the states of that document's
+    // earlier segments in its prologue, on its own critical path; the
+    // segments of one head run on one XCD, so after the first unit those
+    // states come from that XCD's L2.  Measured against the scan's extra
+    // launch: the look-back wins up to 15 predecessors on both block loops
+    // (3-16 %) and loses slightly (1-4 %) at 31; on the full-width loop with
+    // long segments it still wins at 7 (5 %) but not at 15 (16 x 65536
+    // tokens: 2.5 % slower).  The longest document is estimated from the
+    // mean length.
     auto needs_scan = [&](int64_t L, int32_t W) {
         const int64_t ns = T == 0 ? 1 : (T + L - 1) / L;
         if (ns <= 1) return false;
         const int64_t mean_len = (T + num_seqs - 1) / num_seqs;
         const int64_t span = std::min<int64_t>(ns, num_seqs == 1 ? ns : (mean_len + L - 1) / L + 1);
-        const int64_t max_preds = (p.variant == 2 && W >= 128) ? kMaxLookbackWide : kMaxLookback;
-        return ns - 1 > kMaxLookback || span - 1 > max_preds;
+        const bool wide_long = p.variant == 2 && W >= 128 && L / block > kThreeSlotMinBlocks;
+        return ns - 1 > kMaxLookback || span - 1 > (wide_long ? kMaxLookbackWideLong : kMaxLookback);
     };
 
     if (opts && opts->seg_len != 0) {
@@ -112,16 +115,16 @@ la_status make_plan(int64_t T, int32_t num_seqs, int32_t H, int32_t d, int32_t b
         if (L < floor_len) L = floor_len;
         if (L < block) L = block;
         if (L > INT32_MAX / 2) L = (INT32_MAX / 2 / block) * block;
-        // Segments of at most kShortSegmentBlocks blocks whose documents would
-        // need the scan: two value slices with twice the segment length keep
-        // the unit count, halve the segments per document and, at half width,
-        // can sum their predecessors without the scan, which is faster while
-        // segments are this short (8192 tokens x 8 heads: 52.7 -> 48.2 us per
-        // call; 2048 x 32: 37.9 -> 34.8 us); longer ones do better unsplit.
+        // Segments of at most kShortSegmentBlocks blocks: two value slices with
+        // twice the segment length keep the unit count and halve the segments
+        // per document, which is faster while segments are this short (its
+        // block loop streams longer segments, and it needs no scan where the
+        // full width would): 8192 tokens x 8 heads 45.7 -> 37.2 us per call,
+        // 2048 x 32 37.4 -> 33.7, 12288 x 8 52.2 -> 48.4; at 8 blocks it ties
+        // or loses (8192 x 16: 57.4 -> 61.5).
         const bool auto_s = !(opts && opts->value_slices != 0);
         if (auto_s && !(opts && opts->force_scan) && p.variant == 2 && L / block <= kShortSegmentBlocks &&
-            needs_scan(L, p.W) && slice_ok(2 * p.S) && v2_ok(2 * p.S) && 2 * L <= INT32_MAX / 2 &&
-            !needs_scan(2 * L, d / (2 * p.S))) {
+            slice_ok(2 * p.S) && v2_ok(2 * p.S) && 2 * L <= INT32_MAX / 2 && !needs_scan(2 * L, d / (2 * p.S))) {
             p.S *= 2;
             p.W = d / p.S;
             L *= 2;

@@ -90,17 +90,18 @@ __device__ __forceinline__ int doc_lower(const CuView& cu, int n, int t) {
     return lo;
 }
 
-// Workgroup -> unit.  Consecutive unit indices x = (u*H + h)*S + s go to the
-// same XCD (workgroup ids are dealt round-robin over the 8 XCDs), so the S
+// Workgroup -> unit.  Consecutive unit indices x = (h*nseg + u)*S + s go to
+// the same XCD (workgroup ids are dealt round-robin over the 8 XCDs), so the S
 // slices of one (segment, head) -- which read the same Q and K rows -- share
-// that XCD's L2.
+// that XCD's L2, and so do the segments of one head, whose block loops read
+// the same earlier segment states when they sum their prefix.
 __device__ __forceinline__ bool unit_of(const PrefillParams& p, int& u, int& h, int& s) {
     const int64_t g = blockIdx.x;
     const int64_t x = (g & 7) * p.per_xcd + (g >> 3);
     if (x >= p.units) return false;
     s = (int)(x % p.S);
-    h = (int)((x / p.S) % p.H);
-    u = (int)(x / ((int64_t)p.S * p.H));
+    u = (int)((x / p.S) % p.nseg);
+    h = (int)(x / ((int64_t)p.S * p.nseg));
     return true;
 }
 

@@ -53,18 +53,30 @@ int main() {
     EXPECT(make_plan(8192, 1, 8, 128, 64, LA_BF16, &o1, &p) == LA_ERR_UNSUPPORTED);
     o1.value_slices = 8;
     EXPECT(make_plan(8192, 1, 8, 128, 64, LA_BF16, &o1, &p) == LA_ERR_UNSUPPORTED);
-    // short segments that would need the scan go to two slices of twice the length
+    // segments of up to 6 blocks go to two slices of twice the length
     EXPECT(make_plan(8192, 1, 8, 128, 64, LA_BF16, nullptr, &p) == LA_OK && p.S == 2 && p.L == 512 && p.nseg == 16 &&
            p.scan == 0 && p.units == 256);
     EXPECT(make_plan(16384, 1, 8, 128, 64, LA_BF16, nullptr, &p) == LA_OK && p.S == 1 && p.L == 512 && p.scan == 1);
     EXPECT(make_plan(4096, 1, 8, 128, 64, LA_BF16, nullptr, &p) == LA_OK && p.S == 2 && p.L == 256 && p.scan == 0);
-    // look-back or scan: few predecessors on the full-width loop, up to 16 on 64-column slices
-    EXPECT(make_plan(4096, 1, 32, 128, 64, LA_BF16, nullptr, &p) == LA_OK && p.W == 128 && p.nseg == 8 && p.scan == 1);
+    EXPECT(make_plan(12288, 1, 8, 128, 64, LA_BF16, nullptr, &p) == LA_OK && p.S == 2 && p.L == 768 && p.scan == 0);
+    // look-back up to 16 predecessors (8 on the full-width loop with long segments), the scan beyond
+    EXPECT(make_plan(4096, 1, 32, 128, 64, LA_BF16, nullptr, &p) == LA_OK && p.W == 128 && p.nseg == 8 && p.scan == 0);
+    EXPECT(make_plan(8192, 1, 16, 128, 64, LA_BF16, nullptr, &p) == LA_OK && p.W == 128 && p.nseg == 16 && p.scan == 0);
+    la_prefill_opts o5{};
+    o5.seg_len = 512;
+    o5.value_slices = 1;
+    EXPECT(make_plan(8704, 1, 16, 128, 64, LA_BF16, &o5, &p) == LA_OK && p.W == 128 && p.nseg == 17 && p.scan == 0);
+    EXPECT(make_plan(9216, 1, 16, 128, 64, LA_BF16, &o5, &p) == LA_OK && p.W == 128 && p.nseg == 18 && p.scan == 1);
+    o5.value_slices = 2;
+    EXPECT(make_plan(8704, 1, 16, 128, 64, LA_BF16, &o5, &p) == LA_OK && p.W == 64 && p.nseg == 17 && p.scan == 0);
+    EXPECT(make_plan(9216, 1, 16, 128, 64, LA_BF16, &o5, &p) == LA_OK && p.W == 64 && p.nseg == 18 && p.scan == 1);
     EXPECT(make_plan(2048, 1, 32, 128, 64, LA_BF16, nullptr, &p) == LA_OK && p.S == 2 && p.L == 512 && p.scan == 0);
     EXPECT(make_plan(4096, 1, 16, 128, 64, LA_BF16, nullptr, &p) == LA_OK && p.S == 2 && p.L == 512 && p.scan == 0);
     EXPECT(make_plan(4096, 1, 64, 128, 64, LA_BF16, nullptr, &p) == LA_OK && p.W == 128 && p.nseg == 4 && p.scan == 0);
     EXPECT(make_plan(65536, 64, 16, 128, 64, LA_BF16, nullptr, &p) == LA_OK && p.nseg == 16 && p.scan == 0);
     EXPECT(make_plan(65536, 1, 16, 128, 64, LA_BF16, nullptr, &p) == LA_OK && p.nseg == 16 && p.scan == 1);
+    EXPECT(make_plan(16384, 1, 16, 128, 64, LA_BF16, nullptr, &p) == LA_OK && p.L == 1024 && p.scan == 0);
+    EXPECT(make_plan(16384, 1, 32, 128, 64, LA_BF16, nullptr, &p) == LA_OK && p.L == 2048 && p.nseg == 8 && p.scan == 0);
     la_prefill_opts o4{};
     o4.force_scan = 1;
     EXPECT(make_plan(8192, 1, 8, 128, 64, LA_BF16, &o4, &p) == LA_OK && p.S == 1 && p.L == 256 && p.scan == 1);
