@@ -62,7 +62,14 @@ struct CuView {
     int n;
     int T;
     int rev;
-    __device__ __forceinline__ int operator[](int k) const { return rev ? T - cu[n - k] : cu[k]; }
+    // The first and last boundaries are 0 and T by the interface contract,
+    // so they are never read from memory (a one-document call reads none):
+    // at kernel start that saves a memory round trip before the first load.
+    __device__ __forceinline__ int operator[](int k) const {
+        if (k <= 0) return 0;
+        if (k >= n) return T;
+        return rev ? T - cu[n - k] : cu[k];
+    }
 };
 __device__ __forceinline__ CuView cu_view(const PrefillParams& p) { return CuView{p.cu, p.num_seqs, p.T, p.rev}; }
 // Physical document and token of a logical one.
