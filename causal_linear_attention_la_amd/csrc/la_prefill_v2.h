@@ -407,15 +407,24 @@ __global__ __launch_bounds__(kThreads) void la_ws_transpose_v2(float* __restrict
         i0 = state_row(a, lane >> 4, 0);
         j = s * W + w * (W / 4) + state_col<NCW>(c, lane & 15);
     };
-    for (int e = threadIdx.x; e < D * D / 4; e += kThreads) {
-        int i0, j;
-        place(e, i0, j);
-        const f32x4_t x = base[e];
+    // every load of the entry is issued before the first LDS write, so the
+    // workgroup waits for memory once rather than once per 16-byte run
+    constexpr int PER_T = D * D / 4 / kThreads;
+    static_assert(PER_T * kThreads == D * D / 4, "whole runs per thread");
+    f32x4_t x[PER_T];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) M[(i0 + r) * PITCH + j] = x[r];
+    for (int k = 0; k < PER_T; ++k) x[k] = base[threadIdx.x + k * kThreads];
+#pragma unroll
+    for (int k = 0; k < PER_T; ++k) {
+        int i0, j;
+        place(threadIdx.x + k * kThreads, i0, j);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) M[(i0 + r) * PITCH + j] = x[k][r];
     }
     __syncthreads();
-    for (int e = threadIdx.x; e < D * D / 4; e += kThreads) {
+#pragma unroll
+    for (int k = 0; k < PER_T; ++k) {
+        const int e = threadIdx.x + k * kThreads;
         int i0, j;
         place(e, i0, j);
         base[e] = *reinterpret_cast<const f32x4_t*>(M + j * PITCH + i0);  // (X^T)[i0 + r][j] = X[j][i0 + r]
