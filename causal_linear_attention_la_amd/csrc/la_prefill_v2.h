@@ -34,12 +34,11 @@
 //  * The intra product of block j (it needs the scores P of block j) runs in
 //    iteration j+1 between its two barriers, where no tile buffer is being
 //    written; its output rows are stored with buffer stores (rows past a
-//    partial block are dropped by the range check).  Where LDS allows (all
-//    but the full-width loop with three slots) the output tile is staged in
-//    LDS and each wave stores whole rows of its own 16-row band with 16-byte
-//    stores, issued after the iteration's tile loads: the next iteration's
-//    wait for those loads then leaves the stores in flight (stores interleaved
-//    with the loads held every iteration up for the write latency).
+//    partial block are dropped by the range check).  Except on the full-width
+//    loop with three slots, the rows are packed into registers and stored
+//    after the iteration's tile loads: the next iteration's wait for those
+//    loads then leaves the stores in flight (stores issued between the loads
+//    held every iteration up for their write latency).
 //  * With one 16-column tile per wave (64-column slices) the loop has the
 //    registers to issue a group's fragment reads before the products that use
 //    them, paying one LDS latency per group; the full-width loop has not.
@@ -453,12 +452,13 @@ __global__ __launch_bounds__(kThreads, 1) void la_prefill_main_v2(PrefillParams 
     __shared__ __align__(16) bf16_t K0[QN], K1[QN], K2[X3 ? QN : 8];
     __shared__ __align__(16) bf16_t V0[VN], V1[VN], V2[X3 ? VN : 8];
     __shared__ __align__(16) bf16_t Ps[B * PP];
-    // Output staging, where LDS allows (the full-width loop with three slots
-    // already uses 152 KiB): wave w stores rows 16w..16w+15 of the tile, W/32
-    // stores of 16 bytes per lane.
-    constexpr bool OST = NCW == 1 || NS == 2;
-    __shared__ __align__(16) bf16_t Os[OST ? B * W : 8];
-    constexpr int NST = OST ? W / 32 : G::STORES;  // VMEM stores per wave and block
+    // Late output stores: the intra product packs block j-1's rows into
+    // registers and they are stored after block j+1's tile loads, so that the
+    // next iteration's wait for those loads leaves them in flight.  (The
+    // full-width loop with three slots has no registers to spare; it stores
+    // at once and its wait covers one iteration's loads and stores anyway.)
+    constexpr bool LATE = NCW == 1 || NS == 2;
+    constexpr int NST = G::STORES;  // VMEM stores per wave and block
     auto qbuf = [&](auto slot) -> bf16_t* {
         constexpr int X = decltype(slot)::value;
         if constexpr (X == 0) return Q0;
@@ -510,6 +510,7 @@ __global__ __launch_bounds__(kThreads, 1) void la_prefill_main_v2(PrefillParams 
 #pragma unroll
         for (int c = 0; c < NCW; ++c) oacc[b][c] = zero4();
     Frag<bf16_t> vfr[NCW][B / 32];
+    u32x4_t opk[NQT];  // packed output rows of the previous block (late stores: lanes as oacc)
 
     // A cursor past the end (nb = 0) still issues its loads, with an empty
     // buffer range: nothing is read, zeros land in the unused slot, and every
@@ -560,19 +561,14 @@ __global__ __launch_bounds__(kThreads, 1) void la_prefill_main_v2(PrefillParams 
                 }
             }
         }
-        if constexpr (OST) {
+        if constexpr (LATE) {
 #pragma unroll
             for (int b = 0; b < NQT; ++b) {
+                opk[b].x = pack2(oacc[b][0][0], oacc[b][0][1]);
+                opk[b].y = pack2(oacc[b][0][2], oacc[b][0][3]);
                 if constexpr (NCW == 2) {
-                    u32x4_t v;
-                    v.x = pack2(oacc[b][0][0], oacc[b][0][1]);
-                    v.y = pack2(oacc[b][0][2], oacc[b][0][3]);
-                    v.z = pack2(oacc[b][1][0], oacc[b][1][1]);
-                    v.w = pack2(oacc[b][1][2], oacc[b][1][3]);
-                    *reinterpret_cast<u32x4_t*>(Os + soff<W>(16 * b + li, col0 + 8 * g)) = v;
-                } else {
-                    *reinterpret_cast<uint2*>(Os + soff<W>(16 * b + li, col0 + 4 * g)) =
-                        make_uint2(pack2(oacc[b][0][0], oacc[b][0][1]), pack2(oacc[b][0][2], oacc[b][0][3]));
+                    opk[b].z = pack2(oacc[b][1][0], oacc[b][1][1]);
+                    opk[b].w = pack2(oacc[b][1][2], oacc[b][1][3]);
                 }
 #pragma unroll
                 for (int c = 0; c < NCW; ++c) oacc[b][c] = zero4();
@@ -611,15 +607,19 @@ __global__ __launch_bounds__(kThreads, 1) void la_prefill_main_v2(PrefillParams 
     };
 
     auto finish_store = [&](int pb0, int pnb) {
-        constexpr int CPR = W * 2 / 16, RPI = 64 / CPR, NI = 16 / RPI;
         const __amdgpu_buffer_rsrc_t ro =
-            make_rsrc(og + ((int64_t)phys_block(p, pb0, pnb) * p.H + h) * D + s * W, (uint32_t)pnb * row_bytes);
+            make_rsrc(og + ((int64_t)phys_block(p, pb0, pnb) * p.H + h) * D + s * W + col0, (uint32_t)pnb * row_bytes);
 #pragma unroll
-        for (int i = 0; i < NI; ++i) {
-            const int r = 16 * wave + RPI * i + lane / CPR, ch = lane % CPR;
-            const u32x4_t v = *reinterpret_cast<const u32x4_t*>(Os + soff<W>(r, 8 * ch));
-            const int pr = p.rev ? pnb - 1 - r : r;
-            __builtin_amdgcn_raw_buffer_store_b128(v, ro, (uint32_t)pr * row_bytes + (uint32_t)ch * 16u, 0, 0);
+        for (int b = 0; b < NQT; ++b) {
+            const int r = 16 * b + li;
+            const uint32_t off = (uint32_t)(p.rev ? pnb - 1 - r : r) * row_bytes;
+            if constexpr (NCW == 2) __builtin_amdgcn_raw_buffer_store_b128(opk[b], ro, off + (8 * g) * 2, 0, 0);
+            else {
+                u32x2_t v;
+                v.x = opk[b].x;
+                v.y = opk[b].y;
+                __builtin_amdgcn_raw_buffer_store_b64(v, ro, off + (4 * g) * 2, 0, 0);
+            }
         }
     };
 
@@ -660,13 +660,14 @@ __global__ __launch_bounds__(kThreads, 1) void la_prefill_main_v2(PrefillParams 
         // Loads of block j are done.  Vector-memory operations retire in
         // issue order, so the wait lets exactly what was issued after them
         // stay in flight: with two slots, the previous iteration's output
-        // stores (issued after its loads when the rows are staged); with
-        // three, the previous iteration's loads and stores.  The first
-        // iteration follows the prologue instead, which issues no stores:
-        // there only block 1's loads (three slots) may still be in flight.
+        // stores (issued after its loads); with three, the previous
+        // iteration's loads and stores.  The first iteration follows the
+        // prologue instead, which issues no stores: there only block 1's
+        // loads (three slots) may still be in flight.
+        static_assert(NS == 3 || LATE, "two slots always store late");
         if constexpr (NS == 2) {
             if (j == 0) vm_wait<0>();
-            else vm_wait<OST ? NST : 0>();
+            else vm_wait<NST>();
         } else {
             if (j == 0) vm_wait<G::LOADS>();
             else vm_wait<G::LOADS + NST>();
@@ -720,9 +721,9 @@ __global__ __launch_bounds__(kThreads, 1) void la_prefill_main_v2(PrefillParams 
             }
         }
         issue_tile(cf, Slot<FILL>{}, Slot<2>{});
-        // block j-1's rows leave after this step's loads: the next step's wait
-        // for those loads lets these stores stay in flight
-        if constexpr (OST) finish_store(pb0, pnb);
+        // block j-1's rows leave after this iteration's loads: the next
+        // iteration's wait for those loads lets these stores stay in flight
+        if constexpr (LATE) finish_store(pb0, pnb);
         // state: KV += K^T V (after the inter product read it)
         state_update<D, B, W>(kv, vfr, Ks, Vs, col0, lane);
 
@@ -774,10 +775,7 @@ __global__ __launch_bounds__(kThreads, 1) void la_prefill_main_v2(PrefillParams 
     if (j > 0) {
         lds_barrier();  // scores of the last block visible
         finish(pb0, pnb);
-        if constexpr (OST) {
-            lds_barrier();
-            finish_store(pb0, pnb);
-        }
+        if constexpr (LATE) finish_store(pb0, pnb);
     }
 
     if (p.kv_out) empty_doc_states<D, W>(p, u, h, s, t0, t1, tid);
