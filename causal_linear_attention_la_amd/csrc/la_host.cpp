@@ -17,7 +17,7 @@ constexpr int kMaxLookback = 16;  // a unit sums at most this many segment state
 // The transpose-read loop takes three tile slots (loads two blocks ahead) on
 // segments of at least this many blocks; shorter ones start faster with two.
 constexpr int kThreeSlotMinBlocks = 16;
-constexpr int kShortSegmentBlocks = 6;
+constexpr int kShortSegmentBlocks = 12;
 // The full-width transpose-read loop sums at most this many on segments of
 // more than kThreeSlotMinBlocks blocks.
 constexpr int kMaxLookbackWideLong = 8;
@@ -117,11 +117,12 @@ la_status make_plan(int64_t T, int32_t num_seqs, int32_t H, int32_t d, int32_t b
         if (L > INT32_MAX / 2) L = (INT32_MAX / 2 / block) * block;
         // Segments of at most kShortSegmentBlocks blocks: two value slices with
         // twice the segment length keep the unit count and halve the segments
-        // per document, which is faster while segments are this short (its
-        // block loop streams longer segments, and it needs no scan where the
-        // full width would): 8192 tokens x 8 heads 45.7 -> 37.2 us per call,
-        // 2048 x 32 37.4 -> 33.7, 12288 x 8 52.2 -> 48.4; at 8 blocks it ties
-        // or loses (8192 x 16: 57.4 -> 61.5).
+        // per document, which is faster while segments are this short (the
+        // 64-column loop is the quicker one per block, and it needs no scan
+        // where the full width would): 8192 tokens x 8 heads 44.9 -> 34.6 us
+        // per call, 2048 x 32 36.6 -> 31.1, 16384 x 8 62.3 -> 56.7, 24576 x 8
+        // (12 blocks) 80.9 -> 75.8; at 16 blocks it loses (32768 x 8: 101.8
+        // -> 103.2).
         const bool auto_s = !(opts && opts->value_slices != 0);
         if (auto_s && !(opts && opts->force_scan) && p.variant == 2 && L / block <= kShortSegmentBlocks &&
             slice_ok(2 * p.S) && v2_ok(2 * p.S) && 2 * L <= INT32_MAX / 2 && !needs_scan(2 * L, d / (2 * p.S))) {

@@ -53,15 +53,18 @@ int main() {
     EXPECT(make_plan(8192, 1, 8, 128, 64, LA_BF16, &o1, &p) == LA_ERR_UNSUPPORTED);
     o1.value_slices = 8;
     EXPECT(make_plan(8192, 1, 8, 128, 64, LA_BF16, &o1, &p) == LA_ERR_UNSUPPORTED);
-    // segments of up to 6 blocks go to two slices of twice the length
+    // segments of up to 12 blocks go to two slices of twice the length
     EXPECT(make_plan(8192, 1, 8, 128, 64, LA_BF16, nullptr, &p) == LA_OK && p.S == 2 && p.L == 512 && p.nseg == 16 &&
            p.scan == 0 && p.units == 256);
-    EXPECT(make_plan(16384, 1, 8, 128, 64, LA_BF16, nullptr, &p) == LA_OK && p.S == 1 && p.L == 512 && p.scan == 1);
+    EXPECT(make_plan(16384, 1, 8, 128, 64, LA_BF16, nullptr, &p) == LA_OK && p.S == 2 && p.L == 1024 && p.scan == 0);
+    EXPECT(make_plan(24576, 1, 8, 128, 64, LA_BF16, nullptr, &p) == LA_OK && p.S == 2 && p.L == 1536 && p.scan == 0);
+    EXPECT(make_plan(32768, 1, 8, 128, 64, LA_BF16, nullptr, &p) == LA_OK && p.S == 1 && p.L == 1024 && p.scan == 1);
     EXPECT(make_plan(4096, 1, 8, 128, 64, LA_BF16, nullptr, &p) == LA_OK && p.S == 2 && p.L == 256 && p.scan == 0);
     EXPECT(make_plan(12288, 1, 8, 128, 64, LA_BF16, nullptr, &p) == LA_OK && p.S == 2 && p.L == 768 && p.scan == 0);
     // look-back up to 16 predecessors (8 on the full-width loop with long segments), the scan beyond
-    EXPECT(make_plan(4096, 1, 32, 128, 64, LA_BF16, nullptr, &p) == LA_OK && p.W == 128 && p.nseg == 8 && p.scan == 0);
-    EXPECT(make_plan(8192, 1, 16, 128, 64, LA_BF16, nullptr, &p) == LA_OK && p.W == 128 && p.nseg == 16 && p.scan == 0);
+    EXPECT(make_plan(4096, 1, 32, 128, 64, LA_BF16, nullptr, &p) == LA_OK && p.W == 64 && p.nseg == 4 && p.scan == 0);
+    EXPECT(make_plan(8192, 1, 16, 128, 64, LA_BF16, nullptr, &p) == LA_OK && p.W == 64 && p.nseg == 8 && p.scan == 0);
+    EXPECT(make_plan(8192, 1, 32, 128, 64, LA_BF16, nullptr, &p) == LA_OK && p.W == 128 && p.nseg == 8 && p.scan == 0);
     la_prefill_opts o5{};
     o5.seg_len = 512;
     o5.value_slices = 1;
