@@ -56,6 +56,11 @@ def load():
         return _lib
     if not os.path.exists(LIB_PATH):
         raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m causal_linear_attention_la_amd._build`")
+    # torch first: the library then binds to the HIP runtime torch has already
+    # loaded (same soname).  Loaded before torch, it would bring in the system
+    # HIP runtime beside torch's bundled one, and torch's tensors and streams
+    # would be handed to a second runtime (its launches then fail).
+    import torch  # noqa: F401
     lib = ctypes.CDLL(LIB_PATH)
     vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
     lib.la_prefill.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, vp, i32, i64, ctypes.c_int, vp, sz, vp]

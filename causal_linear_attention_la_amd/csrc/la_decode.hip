@@ -7,13 +7,12 @@ template <typename T>
 hipError_t run_decode(const DecodeParams& p, int D, hipStream_t st) {
     const dim3 grid((unsigned)p.pairs), block(kThreads);
     switch (D) {
-        case 16: la_decode_kernel<T, 16><<<grid, block, 0, st>>>(p); break;
-        case 32: la_decode_kernel<T, 32><<<grid, block, 0, st>>>(p); break;
-        case 64: la_decode_kernel<T, 64><<<grid, block, 0, st>>>(p); break;
-        case 128: la_decode_kernel<T, 128><<<grid, block, 0, st>>>(p); break;
+        case 16: return launch_kernel(la_decode_kernel<T, 16>, grid, block, st, p);
+        case 32: return launch_kernel(la_decode_kernel<T, 32>, grid, block, st, p);
+        case 64: return launch_kernel(la_decode_kernel<T, 64>, grid, block, st, p);
+        case 128: return launch_kernel(la_decode_kernel<T, 128>, grid, block, st, p);
         default: return hipErrorInvalidValue;
     }
-    return hipGetLastError();
 }
 }  // namespace
 

@@ -9,6 +9,22 @@
 
 namespace la {
 
+template <class T>
+struct nodeduce {
+    using type = T;
+};
+
+// Launches `kernel` and returns the status of this launch alone.  (After a
+// `<<<...>>>` launch the only check is hipGetLastError, which also reports
+// errors that earlier calls on the thread left behind -- another library's
+// failed query, say -- and would make a good launch look failed.)
+template <typename... KArgs>
+inline hipError_t launch_kernel(void (*kernel)(KArgs...), dim3 grid, dim3 block, hipStream_t st,
+                                typename nodeduce<KArgs>::type... args) {
+    void* ptrs[] = {static_cast<void*>(&args)..., nullptr};
+    return hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, ptrs, 0, st);
+}
+
 // Enqueues the prefill kernels for one plan: segment states (nseg > 1), prefix
 // scan (scan != 0), then the block loop bracketed by the optional events.
 // variant: 0 = automatic, 1 = reference block loop, 2 = transpose-read block

@@ -20,11 +20,10 @@ template __global__ void v2::la_ws_transpose_v2<64, 64>(float*, int64_t);
 hipError_t launch_ws_transpose(float* ws, int64_t states, int D, int W, hipStream_t st) {
     if (states <= 0) return hipSuccess;
     const dim3 grid((unsigned)states), block(kThreads);
-    if (D == 128 && W == 128) v2::la_ws_transpose_v2<128, 128><<<grid, block, 0, st>>>(ws, states);
-    else if (D == 128 && W == 64) v2::la_ws_transpose_v2<128, 64><<<grid, block, 0, st>>>(ws, states);
-    else if (D == 64 && W == 64) v2::la_ws_transpose_v2<64, 64><<<grid, block, 0, st>>>(ws, states);
-    else return hipErrorInvalidValue;
-    return hipGetLastError();
+    if (D == 128 && W == 128) return launch_kernel(v2::la_ws_transpose_v2<128, 128>, grid, block, st, ws, states);
+    if (D == 128 && W == 64) return launch_kernel(v2::la_ws_transpose_v2<128, 64>, grid, block, st, ws, states);
+    if (D == 64 && W == 64) return launch_kernel(v2::la_ws_transpose_v2<64, 64>, grid, block, st, ws, states);
+    return hipErrorInvalidValue;
 }
 
 hipError_t launch_prefill_bf16(const PrefillParams& p, int D, int B, int W, int variant, hipStream_t st, hipEvent_t e0,

@@ -15,10 +15,7 @@ constexpr bool has_v2() {
 // that they timestamp the kernel's own start and end.
 inline hipError_t launch_main(void (*kernel)(PrefillParams), dim3 grid, dim3 block, const PrefillParams& p,
                               hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
-    if (!e0 && !e1) {
-        kernel<<<grid, block, 0, st>>>(p);
-        return hipSuccess;
-    }
+    if (!e0 && !e1) return launch_kernel(kernel, grid, block, st, p);
     PrefillParams arg = p;
     void* args[] = {&arg};
     return hipExtLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, args, 0, st, e0, e1, 0);
@@ -35,18 +32,19 @@ hipError_t run_prefill(const PrefillParams& p, int variant, hipStream_t st, hipE
         if constexpr (has_v2<T, D, B, W>()) use_v2 = (variant != 1);
         if (variant == 2 && !use_v2) return hipErrorInvalidValue;
         if (p.nseg > 1 && !p.skip_prefix) {
+            void (*seg_kernel)(PrefillParams) = la_segment_state_kernel<T, D, B, W>;
             if constexpr (has_v2<T, D, B, W>()) {
-                if (use_v2) v2::la_segment_state_v2<D, B, W><<<grid, block, 0, st>>>(p);
-                else la_segment_state_kernel<T, D, B, W><<<grid, block, 0, st>>>(p);
-            } else {
-                la_segment_state_kernel<T, D, B, W><<<grid, block, 0, st>>>(p);
+                if (use_v2) seg_kernel = v2::la_segment_state_v2<D, B, W>;
             }
+            hipError_t e = launch_kernel(seg_kernel, grid, block, st, p);
+            if (e != hipSuccess) return e;
             if (p.scan) {
                 const int64_t entries = (int64_t)p.H * D * D;  // a multiple of 4
                 const int64_t threads = entries / 4;
                 constexpr int NT = 128;
-                la_segment_scan_kernel<32, NT><<<dim3((unsigned)((threads + NT - 1) / NT)), dim3(NT), 0, st>>>(
-                    p.ws, p.flags, p.nseg, entries);
+                e = launch_kernel(la_segment_scan_kernel<32, NT>, dim3((unsigned)((threads + NT - 1) / NT)), dim3(NT),
+                                  st, p.ws, (const int32_t*)p.flags, (int)p.nseg, entries);
+                if (e != hipSuccess) return e;
             }
         }
         void (*main_kernel)(PrefillParams) = la_prefill_main_kernel<T, D, B, W>;
@@ -60,9 +58,7 @@ hipError_t run_prefill(const PrefillParams& p, int variant, hipStream_t st, hipE
                 }
             }
         }
-        hipError_t e = launch_main(main_kernel, grid, block, p, st, e0, e1);
-        if (e != hipSuccess) return e;
-        return hipGetLastError();
+        return launch_main(main_kernel, grid, block, p, st, e0, e1);
     }
 }
 

@@ -29,7 +29,10 @@
  * Errors
  *   Arguments are validated on the host before anything is enqueued; a rejected
  *   call returns a status and enqueues nothing.  A failed kernel launch returns
- *   LA_ERR_HIP.  Asynchronous device faults surface on the stream as usual.
+ *   LA_ERR_HIP (kernels enqueued before it in the same call stay enqueued).
+ *   Only the call's own launches are checked: an error that earlier HIP calls
+ *   left in the thread's last-error slot is neither reported nor cleared.
+ *   Asynchronous device faults surface on the stream as usual.
  */
 #ifndef LA_H
 #define LA_H

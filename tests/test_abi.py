@@ -1,6 +1,7 @@
 """C-ABI checks that need no GPU: the library loads, exports every entry point
 include/la.h declares, and rejects bad arguments on the host before anything
 is enqueued (only invalid calls are made here)."""
+import ast
 import ctypes
 import os
 import re
@@ -137,3 +138,20 @@ def test_no_undefined_library_symbols(lib):
     out = subprocess.run(["nm", "-D", "--undefined-only", la.LIB_PATH], capture_output=True, text=True).stdout
     missing = [l for l in out.splitlines() if "_ZN2la" in l]
     assert not missing, missing
+
+
+def test_one_hip_runtime_in_the_process():
+    """Loading the library first, then torch, leaves one HIP runtime in the
+    process: torch's bundled one, to which the library binds (the binding
+    imports torch before it loads the library).  Two runtimes would each see
+    the other's tensors and streams as foreign."""
+    code = (
+        "import sys; sys.path.insert(0, %r)\n"
+        "import causal_linear_attention_la_amd as la\n"
+        "la.load()\n"
+        "import torch\n"
+        "print(sorted({l.split()[-1] for l in open('/proc/self/maps') if 'libamdhip64' in l}))\n" % ROOT
+    )
+    out = subprocess.run(["python3", "-c", code], capture_output=True, text=True, check=True).stdout.strip()
+    paths = ast.literal_eval(out)
+    assert len(paths) == 1, paths

@@ -221,6 +221,49 @@ def test_run_to_run_bitwise_determinism():
         assert np.array_equal(first[0], again[0]) and np.array_equal(first[1], again[1])
 
 
+def test_stale_hip_error_not_reported():
+    """An error an earlier HIP call left in the thread's last-error slot (here
+    a host-side query of a device index that does not exist) is neither
+    reported by the library's calls nor cleared by them.  Every buffer is
+    allocated before the error is planted (torch's allocator would report it)."""
+    import torch
+
+    hip = ctypes.CDLL("libamdhip64.so")
+    for f in ("hipGetLastError", "hipPeekAtLastError", "hipDeviceGetAttribute", "hipDeviceSynchronize"):
+        getattr(hip, f).restype = ctypes.c_int
+    T, H, d = 1000, 2, 128
+    q, k, v = rand_inputs(56, T, H, d, "bf16")
+    cu = np.array([0, 400, 1000], dtype=np.int32)
+    qd, kd, vd, cud = to_dev(q), to_dev(k), to_dev(v), to_dev(cu)
+    o = torch.empty_like(qd)
+    kv = torch.empty((2, H, d, d), dtype=torch.float32, device="cuda")
+    plan = la.la_prefill_plan(T, 2, H, d, 64, la.LA_BF16, la.make_opts(seg_len=256))
+    assert plan["num_segments"] > 1  # segment states, look-back and block loop all launch
+    ws = torch.empty(plan["workspace_bytes"], dtype=torch.uint8, device="cuda")
+    s0 = la_inputs.normal(56, 9, (2, H, d, d), "fp32", 0.01)
+    sd = to_dev(s0)
+    q2, k2, v2 = to_dev(q[:2]), to_dev(k[:2]), to_dev(v[:2])
+    o2 = torch.empty_like(q2)
+    torch.cuda.synchronize()
+    hip.hipGetLastError()  # start from a clean slot
+    value = ctypes.c_int(0)
+    assert hip.hipDeviceGetAttribute(ctypes.byref(value), 0, 1 << 20) != 0  # no such device
+    stale = hip.hipPeekAtLastError()
+    assert stale != 0
+    try:
+        la.prefill(qd, kd, vd, cud, block=64, out=o, kv_state_out=kv, workspace=ws, seg_len=256)
+        la.decode(q2, k2, v2, sd, out=o2)
+        assert hip.hipDeviceSynchronize() == 0
+        assert hip.hipPeekAtLastError() == stale
+    finally:
+        hip.hipGetLastError()
+    check_against_oracle(q, k, v, cu, to_host(o), to_host(kv), False, "after a stale HIP error")
+    s_ref = s0.astype(np.float64).reshape(-1, d, d)
+    o_ref = oracle.decode_step(q[:2].reshape(-1, d), k[:2].reshape(-1, d), v[:2].reshape(-1, d), s_ref)
+    ErrAcc().add(to_host(o2).reshape(-1, d), o_ref).check(False, "decode o after a stale HIP error")
+    ErrAcc().add(to_host(sd).reshape(-1, d, d), s_ref).check(True, "decode state after a stale HIP error")
+
+
 def test_guard_bands():
     """Outputs are written exactly inside their bounds."""
     import torch
