@@ -53,7 +53,7 @@ def draw(seed):
                 backward=r.random() < 0.35)
 
 
-SEEDS = list(range(1000, 1240))
+SEEDS = list(range(1000, 2000))
 
 
 @pytest.mark.parametrize("seed", SEEDS)
