@@ -453,8 +453,8 @@ __global__ __launch_bounds__(kThreads, 1) void la_prefill_main_v2(PrefillParams 
     __shared__ __align__(16) bf16_t V0[VN], V1[VN], V2[X3 ? VN : 8];
     __shared__ __align__(16) bf16_t Ps[B * PP];
     // Late output stores: the intra product packs block j-1's rows into
-    // registers and they are stored after block j+1's tile loads, so that the
-    // next iteration's wait for those loads leaves them in flight.  (The
+    // registers and they are stored after the iteration's tile loads, so that
+    // the next iteration's wait for its tiles leaves them in flight.  (The
     // full-width loop with three slots has no registers to spare; it stores
     // at once and its wait covers one iteration's loads and stores anyway.)
     constexpr bool LATE = NCW == 1 || NS == 2;
