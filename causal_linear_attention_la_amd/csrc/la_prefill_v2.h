@@ -674,8 +674,9 @@ __global__ __launch_bounds__(kThreads, 1) void la_prefill_main_v2(PrefillParams 
         }
         lds_barrier();  // (A) block j visible; block j-1's tiles no longer read
         issue_tile(cf, Slot<FILL>{}, Slot<0>{});
-        // block j-1's output; in the first iteration pnb = 0 and the stores
-        // (of whatever the accumulators hold) fall outside the buffer range
+        // block j-1's intra product (and its rows, unless they are stored
+        // late); in the first iteration pnb = 0 and the stores (of whatever
+        // the accumulators hold) fall outside the buffer range
         finish(pb0, pnb);
         issue_tile(cf, Slot<FILL>{}, Slot<1>{});
         lds_barrier();  // (B) scores of block j-1 consumed
