@@ -1,10 +1,11 @@
-"""Prefill and decode captured in a HIP graph (torch.cuda.CUDAGraph) and
+"""Prefill, decode and backward captured in a HIP graph (torch.cuda.CUDAGraph) and
 replayed: every replay must give, bit for bit, what the same call gives
 eagerly (the kernels are deterministic), with eager work and
 synchronisations between the replays.  Cases: a multi-segment plan with the
 look-back, the same with the separate prefix-scan kernel, packed documents
-with an empty one, and a decode step whose state is reset eagerly before
-each replay.  The eager result itself is checked against the fp64 oracle."""
+with an empty one, a decode step whose state is reset eagerly before
+each replay, and the backward.  The eager prefill and decode results are
+checked against the fp64 oracle."""
 import numpy as np
 import pytest
 
@@ -117,3 +118,39 @@ def test_decode_graph_replays_match_eager():
         log(f"    decode replay {r}")
         assert torch.equal(o, o_ref), f"replay {r}: o differs from the eager step"
         assert torch.equal(S, S_ref), f"replay {r}: state differs from the eager step"
+
+
+def test_backward_graph_replays_match_eager():
+    """The backward's passes (with the in-place transposes of segment states)
+    captured together; every replay matches the eager call bit for bit (the
+    eager gradients themselves are checked against the oracle elsewhere)."""
+    import torch
+
+    T, H, d = 2000, 2, 128
+    cu = np.array([0, 900, T], np.int32)
+    opts = dict(seg_len=256)
+    q, k, v, dout = (la_inputs.normal(75, i, (T, H, d), "bf16", 1 / np.sqrt(d)) for i in range(4))
+    qd, kd, vd, dod, cud = to_dev(q), to_dev(k), to_dev(v), to_dev(dout), to_dev(cu)
+    dko = to_dev(la_inputs.normal(75, 9, (2, H, d, d), "fp32", 0.01))
+    outs = (torch.empty_like(qd), torch.empty_like(qd), torch.empty_like(qd),
+            torch.empty((2, H, d, d), dtype=torch.float32, device="cuda"))
+    need = la.la_prefill_workspace_size_ex(T, 2, H, d, 64, la.LA_BF16, la.make_opts(**opts))
+    assert need > 0
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+
+    def call():
+        la.backward(qd, kd, vd, dod, cud, block=64, dkv_state_out=dko, workspace=ws, out=outs, **opts)
+
+    call()
+    torch.cuda.synchronize()
+    refs = [t.clone() for t in outs]
+    g = _capture(call)
+    for r in range(REPLAYS):
+        for t in outs:
+            t.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        log(f"    backward replay {r}")
+        for name, t, ref in zip(("dq", "dk", "dv", "dkv_in"), outs, refs):
+            assert torch.equal(t, ref), f"replay {r}: {name} differs from the eager call"
