@@ -1,26 +1,33 @@
 #!/usr/bin/env python3
 """Benchmark: causal linear attention (Lightning-style) on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload prefill_8k]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload long_1m]
 
 A step is one pass of the hot path over one batch of synthetic input: one
-la_prefill call over the workload (segment states, prefix scan when needed,
-block loop).  The default workload is the 8-head x 8192-token bf16 prefill
-(d = 128, block 64).  Inputs are generated on the host from fixed seeds,
-copied to HBM before timing, and rotated over several input sets so that the
-timed steps read HBM rather than the 256 MB last-level cache.  The decode
-workload (256 sequences x 64 heads, fp32 state, 1000 steps) is timed in the
-same run and reported under "decode", and the prefill's backward
-(la_prefill_backward: dq, dk, dv) over the same workload under "backward", with
-a forward + backward pair sharing the forward's workspace under
-"backward"/"train_step".
+la_prefill call over the whole workload (segment states, prefix scan when the
+plan needs one, block loop).  The headline workload is the 8-head x
+1,048,576-token bf16 prefill (d = 128, block 64), the largest of the
+single-GPU prefill workloads.  Inputs are generated on the host from fixed
+seeds and copied to HBM before timing; small workloads rotate over several
+input sets so that the timed steps read HBM rather than the 256 MB last-level
+cache.
 
-Prints one JSON line.  `roofline` is for the block-loop kernel: algorithmic
-bytes (q, k, v read + o written, 8 d bytes per token-head) per launch over its
-average duration, measured with HIP events stamped on the launch stream
-around every 8th launch inside the timed region (--event-stride; stamping
-every launch costs several microseconds per step).  `cpu_baseline` times the fp64
-oracle (the recurrent form) on the host cores for the same workload.
+`value` comes from a timed loop of K steps with nothing but the calls in it
+(synchronised before and after).  A second loop over the same steps launches
+the block-loop kernel through hipExtLaunchKernel with start/end events on the
+launch stream: `roofline` is that kernel's algorithmic bytes (q, k, v read + o
+written, 8 d bytes per token-head) over its average duration.  `whole_call`
+is the same bytes over the whole step (every kernel of the call), the figure
+the 60 % target is stated for.  Both are also given against `ceilings`:
+contiguous HBM streams written here (include/la_bench.h) timed in the same
+run, 3 reads + 1 write for prefill and 1 read + 1 write for decode.
+
+Reported beside the headline, in the same line: the packed-document and 8k
+prefill workloads (`workloads`), the prefill's backward and a forward +
+backward training step on the headline workload (`backward`), the decode
+workload (256 sequences x 64 heads, fp32 state, 1000 steps, `decode`), and
+`cpu_baseline`: the fp64 oracle (recurrent form) on the host cores over a
+bounded sample of the headline workload.
 """
 from __future__ import annotations
 
@@ -39,12 +46,13 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, GB/s
 DECODE_SAMPLE = {}  # host copy of a few decode states for the oracle's timing
-MFMA_BF16_PEAK_TFLOPS = 2500.0
 
 KERNEL_SOURCES = ["la_prefill_kernels.h", "la_prefill_v2.h", "la_device.h", "la_tiles.h", "la_prefill_launch.inl",
                   "la_prefill_bf16.hip", "la_host.cpp"]
 MAIN_KERNEL = {1: "la_prefill_main_kernel", 2: "la_prefill_main_v2"}  # by the plan's block-loop variant
-DECODE_SOURCES = ["la_decode_kernels.h", "la_device.h"]
+DECODE_SOURCES = ["la_decode_kernels.h", "la_device.h", "la_decode.hip"]
+METRIC = "prefill tokens·heads/s (bf16, d=128) + % roofline; decode steps/s"
+GIB = 1 << 30
 
 
 def sources_sha(names) -> str:
@@ -93,6 +101,24 @@ class Hip:
         self.lib.hipEventDestroy(e)
 
 
+def gpu_time(torch, hip, fn, reps: int) -> float:
+    """Seconds per call of fn() over reps calls, by one event pair on the
+    current stream around all of them (after one untimed call)."""
+    stream = torch.cuda.current_stream().cuda_stream
+    fn()
+    torch.cuda.synchronize()
+    e0, e1 = hip.event(), hip.event()
+    hip.record(e0, stream)
+    for _ in range(reps):
+        fn()
+    hip.record(e1, stream)
+    torch.cuda.synchronize()
+    s = hip.elapsed_ms(e0, e1) / 1e3 / reps
+    hip.destroy(e0)
+    hip.destroy(e1)
+    return s
+
+
 def load_traffic(kernel: str, workload: str, sha: str):
     """HBM bytes per launch from a committed rocprofv3 counter summary, if it
     was taken on the current kernel sources."""
@@ -106,36 +132,6 @@ def load_traffic(kernel: str, workload: str, sha: str):
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(w, target_cpu_s: float = 10.0) -> dict:
-    """The fp64 oracle as it stands, over the whole workload, repeated until
-    about target_cpu_s seconds of CPU time have been spent."""
-    import oracle
-
-    oracle.build()
-    reps, wall = 0, 0.0
-    while True:
-        t0 = time.perf_counter()
-        o_ref, kv_ref = oracle.recurrent(w["q"], w["k"], w["v"], w["cu"], want_o=True, want_state=True)
-        wall += time.perf_counter() - t0
-        if reps == 0 and "gpu_o" in w:
-            w["error_vs_oracle"] = error_vs_oracle(w, o_ref, kv_ref)
-        del o_ref, kv_ref
-        reps += 1
-        threads = oracle.last_threads()
-        if wall * threads >= target_cpu_s or reps >= 50:
-            break
-    th = w["T"] * w["H"] * reps / wall
-    # one thread on a quarter of the heads, for a per-core figure
-    hq = max(1, w["H"] // 4)
-    t0 = time.perf_counter()
-    oracle.recurrent(w["q"], w["k"], w["v"], w["cu"], want_o=True, want_state=True, heads=(0, hq), nthreads=1)
-    one = w["T"] * hq / (time.perf_counter() - t0)
-    return {"value": th, "unit": "token·heads/s", "cores": threads, "kind": "oracle",
-            "sample": f"whole {w['name']} workload ({w['T']} tokens x {w['H']} heads, d={w['d']}), "
-                      f"fp64 recurrent form, {reps} repetitions, {wall:.2f} s wall",
-            "single_thread_value": one, "cpu_model": cpu_model()}
-
-
 def cpu_model() -> str:
     try:
         with open("/proc/cpuinfo") as f:
@@ -147,33 +143,62 @@ def cpu_model() -> str:
     return "unknown"
 
 
-def copy_bandwidth(torch, hip, nbytes: int = 1 << 30, reps: int = 20) -> float:
-    """Measured device copy bandwidth (GB/s, read + write bytes) of a 1 GiB
-    device-to-device copy: a second, practical roofline beside the datasheet's."""
-    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
-    dst = torch.empty_like(src)
-    for _ in range(3):
-        dst.copy_(src)
-    stream = torch.cuda.current_stream().cuda_stream
-    e0, e1 = hip.event(), hip.event()
-    torch.cuda.synchronize()
-    hip.record(e0, stream)
-    for _ in range(reps):
-        dst.copy_(src)
-    hip.record(e1, stream)
-    torch.cuda.synchronize()
-    s = hip.elapsed_ms(e0, e1) / 1e3
-    hip.destroy(e0)
-    hip.destroy(e1)
-    del src, dst
-    return 2 * nbytes * reps / s / 1e9
+# ------------------------------------------------------------------ ceilings
+
+def stream_ceilings(la, torch, hip) -> dict:
+    """Bandwidth (GB/s of bytes read + written) of the contiguous streams in
+    la_bench_stream over 1 GiB per source: the best of 256 and 512
+    workgroups, plain and non-temporal accesses."""
+    lib = la.load()
+    bufs = [torch.empty(GIB, dtype=torch.uint8, device="cuda").fill_(i + 1) for i in range(4)]
+    P = lambda t: ctypes.c_void_p(t.data_ptr())
+    sp = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    out = {}
+    for mode, name, nbytes in ((0, "copy_1r1w", 2 * GIB), (1, "stream_3r1w", 4 * GIB)):
+        best, how = 0.0, None
+        for wgs in (256, 512):
+            for nt in (0, 1):
+                def fn():
+                    st = lib.la_bench_stream(mode, P(bufs[0]), P(bufs[1]), P(bufs[2]), P(bufs[3]), GIB, wgs, nt, sp)
+                    if st != 0:
+                        raise RuntimeError(f"la_bench_stream: {st}")
+                gbs = nbytes / gpu_time(torch, hip, fn, 10) / 1e9
+                if gbs > best:
+                    best, how = gbs, f"{wgs} workgroups, {'non-temporal' if nt else 'plain'} accesses"
+        out[name] = {"GBs": best, "config": how}
+    del bufs
+    torch.cuda.empty_cache()
+    return out
 
 
-def bench_prefill(args, la, torch, hip):
+# ------------------------------------------------------------------- prefill
+
+def device_sets(torch, w, rotate: int):
+    """Input set 0 is the seeded workload; the others are copies shifted by
+    one token per set (same statistics, different bytes in HBM)."""
+    T, H, d = w["T"], w["H"], w["d"]
+
+    def dev(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(a).cuda()
+
+    per_set = 4 * T * H * d * (2 if w["dtype"] == "bf16" else 4)
+    nsets = max(1, min(rotate, int((8 * GIB) // max(per_set, 1))))
+    q0, k0, v0 = dev(w["q"]), dev(w["k"]), dev(w["v"])
+    sets = []
+    for i in range(nsets):
+        sh = i % max(T, 1)
+        q, k, v = (torch.roll(x, sh, 0).contiguous() if sh else x for x in (q0, k0, v0))
+        sets.append((q, k, v, torch.empty_like(q)))
+    return sets
+
+
+def bench_prefill(name, args, la, torch, hip, steps: int, warmup: int, graph: bool, keep_sets: bool = False):
+    """One prefill workload: clean timed loop (value), event-stamped loop
+    (block-loop kernel duration), optionally HIP-graph replay."""
     import la_inputs
 
-    name = args.workload
-    cfg = la_inputs.WORKLOADS[name]
     w = la_inputs.prefill_inputs(name)
     w["name"] = name
     T, H, d, block = w["T"], w["H"], w["d"], args.block or w["block"]
@@ -181,27 +206,11 @@ def bench_prefill(args, la, torch, hip):
     num_seqs = len(w["cu"]) - 1
     opts = dict(seg_len=args.seg_len, value_slices=args.slices, force_scan=args.force_scan, slots=args.slots)
     plan = la.la_prefill_plan(T, num_seqs, H, d, block, dt, la.make_opts(**opts))
-
-    def dev(a):
-        if a.dtype == np.uint16:
-            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
-        return torch.from_numpy(a).cuda()
-
-    # input sets: set 0 is the seeded workload, the others are copies shifted
-    # by one token per set (same statistics, different bytes in HBM)
-    per_set = 4 * T * H * d * (2 if w["dtype"] == "bf16" else 4)
-    nsets = max(1, min(args.rotate, int((8 << 30) // max(per_set, 1))))
-    q0, k0, v0 = dev(w["q"]), dev(w["k"]), dev(w["v"])
-    sets = []
-    for i in range(nsets):
-        sh = i % max(T, 1)
-        q, k, v = (torch.roll(x, sh, 0).contiguous() if sh else x for x in (q0, k0, v0))
-        sets.append((q, k, v, torch.empty_like(q)))
-    w["dev_sets"] = sets
+    sets = device_sets(torch, w, args.rotate)
+    nsets = len(sets)
     cu = torch.from_numpy(w["cu"]).cuda()
     kv = torch.empty((num_seqs, H, d, d), dtype=torch.float32, device="cuda")
-    ws_bytes = plan["workspace_bytes"]
-    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(max(plan["workspace_bytes"], 256), dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream()
     sp = stream.cuda_stream
 
@@ -210,34 +219,37 @@ def bench_prefill(args, la, torch, hip):
         la.prefill(q, k, v, cu, block=block, out=o, kv_state_out=kv, workspace=ws, begin_event=ev0, end_event=ev1,
                    **opts)
 
-    for i in range(args.warmup):
+    for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
 
-    K = args.steps
-    # The block-loop kernel of every event_stride-th step in the timed region
-    # is launched with start/end events (hipExtLaunchKernel); stamping every
-    # launch would itself cost several microseconds per step.
-    # (short timed regions -- long steps -- stamp every launch: there the cost is noise)
-    stride = max(1, args.event_stride) if args.event_stride else (8 if args.steps >= 128 else 1)
-    evs = {i: (hip.event(), hip.event()) for i in range(0, K, stride)}
+    # the timed loop: the calls and nothing else
+    e0, e1 = hip.event(), hip.event()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(K):
-        if i in evs:
-            step(i, evs[i][0], evs[i][1])
-        else:
-            step(i)
+    hip.record(e0, sp)
+    for i in range(steps):
+        step(i)
+    hip.record(e1, sp)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    kernel_ms = [hip.elapsed_ms(a, b) for a, b in evs.values()]
-    for a, b in evs.values():
+    gpu_s = hip.elapsed_ms(e0, e1) / 1e3
+    hip.destroy(e0)
+    hip.destroy(e1)
+
+    # the same steps again, the block-loop kernel of each launched with events
+    evs = [(hip.event(), hip.event()) for _ in range(steps)]
+    torch.cuda.synchronize()
+    for i in range(steps):
+        step(i, evs[i][0], evs[i][1])
+    torch.cuda.synchronize()
+    kernel_ms = [hip.elapsed_ms(a, b) for a, b in evs]
+    for a, b in evs:
         hip.destroy(a)
         hip.destroy(b)
 
-    # the same steps replayed from a HIP graph (launch overhead removed)
     graph_value = None
-    if not args.no_graph:
+    if graph:
         g = torch.cuda.CUDAGraph()
         s = torch.cuda.Stream()
         s.wait_stream(stream)
@@ -248,71 +260,121 @@ def bench_prefill(args, la, torch, hip):
                 for i in range(nsets):
                     step(i)
         torch.cuda.synchronize()
-        reps = max(1, K // nsets)
+        reps = max(1, steps // nsets)
         g.replay()
         torch.cuda.synchronize()
         t1 = time.perf_counter()
         for _ in range(reps):
             g.replay()
         torch.cuda.synchronize()
-        graph_elapsed = time.perf_counter() - t1
-        graph_value = T * H * nsets * reps / graph_elapsed
+        graph_value = T * H * nsets * reps / (time.perf_counter() - t1)
+        del g
 
+    esz = 2 if w["dtype"] == "bf16" else 4
+    algo_bytes = T * H * 4 * d * esz  # q, k, v read + o written
     avg_kernel_s = float(np.mean(kernel_ms)) / 1e3
-    algo_bytes = T * H * 8 * d * (1 if w["dtype"] == "bf16" else 2)
     achieved = algo_bytes / avg_kernel_s / 1e9
     sha = sources_sha(KERNEL_SOURCES)
     kname = MAIN_KERNEL[plan["variant"]]
-    traffic = load_traffic(kname, name, sha)
-    value = T * H * K / elapsed
-    roof_th = HBM_PEAK_GBS * 1e9 / (algo_bytes / (T * H))  # whole step at HBM peak
+    roof_th = HBM_PEAK_GBS * 1e9 / (algo_bytes / (T * H))  # token-heads/s with every byte at HBM peak
+    value = T * H * steps / elapsed
     rec = {
-        "metric": "prefill tokens·heads/s (bf16, d=128) + % roofline; decode steps/s",
-        "value": value,
-        "unit": "token·heads/s",
-        "n_gpus": 1,
-        "steps": K,
-        "warmup": args.warmup,
-        "ms_per_step": elapsed / K * 1e3,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": w["dtype"],
-        "data": "synthetic",
+        "workload": name, "value": value, "unit": "token·heads/s", "steps": steps, "warmup": warmup,
+        "ms_per_step": elapsed / steps * 1e3, "gpu_ms_per_step": gpu_s / steps * 1e3,
         "config": {"workload": name, "documents": num_seqs, "heads": H, "tokens": T, "head_dim": d, "block": block,
-                   "seg_len": plan["seg_len"], "value_slices": plan["value_slices"],
+                   "dtype": w["dtype"], "seg_len": plan["seg_len"], "value_slices": plan["value_slices"],
                    "segments": plan["num_segments"], "scan": plan["scan"], "slots": plan["slots"],
-                   "workgroups": plan["units"], "event_stride": stride,
-                   "input_sets": nsets},
-        "roofline": {"bound": "hbm", "kernel": kname, "achieved": achieved,
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": traffic, "kernel_ms": avg_kernel_s * 1e3,
+                   "workgroups": plan["units"], "input_sets": nsets},
+        "roofline": {"bound": "hbm", "kernel": kname, "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": load_traffic(kname, name, sha),
+                     "kernel_ms": avg_kernel_s * 1e3, "kernel_launches_timed": steps,
                      "algorithmic_bytes": algo_bytes, "kernel_sources_sha": sha},
-        "path_roofline": {"token_heads_per_s": roof_th, "frac": value / roof_th},
+        "whole_call": {"achieved": algo_bytes * steps / elapsed / 1e9, "unit": "GB/s",
+                       "roofline_token_heads_per_s": roof_th, "frac": value / roof_th},
         "graph_replay_value": graph_value,
     }
-    if not args.no_cpu_baseline:
-        # outputs of the seeded input set, for the error against the oracle
-        step(0)
-        torch.cuda.synchronize()
-        o0 = sets[0][3]
-        w["gpu_o"] = (o0.float() if o0.dtype == torch.bfloat16 else o0).cpu().numpy()
-        w["gpu_kv"] = kv.cpu().numpy()
+    rec["roofline"]["whole_call_frac"] = rec["whole_call"]["frac"]
+    # outputs of the seeded input set, for the error against the oracle
+    step(0)
+    torch.cuda.synchronize()
+    o0 = sets[0][3]
+    w["gpu_o"] = o0
+    w["gpu_kv"] = kv
+    if keep_sets:
+        w["dev_sets"] = sets
     return rec, w
 
 
-def error_vs_oracle(w, o_ref, kv_ref) -> dict:
-    """rel-L2 and max-abs error (relative to max |ref|) of the GPU outputs
-    of the seeded input set against the fp64 oracle."""
-    def errs(g, r):
-        g = np.asarray(g, dtype=np.float64).ravel()
-        r = np.asarray(r, dtype=np.float64).ravel()
-        den = max(float(np.linalg.norm(r)), 1e-300)
-        return float(np.linalg.norm(g - r) / den), float(np.max(np.abs(g - r)) / max(float(np.max(np.abs(r))), 1e-300))
-    o_l2, o_max = errs(w["gpu_o"], o_ref)
-    kv_l2, kv_max = errs(w["gpu_kv"], kv_ref)
-    return {"o_rel_l2": o_l2, "o_max_abs_rel": o_max, "kv_state_rel_l2": kv_l2, "kv_state_max_abs_rel": kv_max}
+def with_ceiling(roof: dict, ceiling_gbs: float):
+    roof["measured_ceiling_GBs"] = ceiling_gbs
+    roof["frac_of_measured_ceiling"] = roof["achieved"] / ceiling_gbs
 
+
+# ------------------------------------------------------------------ backward
+
+def bench_backward(args, la, torch, hip, w, dev_sets, steps: int):
+    """la_prefill_backward over the same workload: dq, dk, dv from dO with no
+    incoming state and no final-state gradient.  Algorithmic bytes per call:
+    q, k, v, dO read and dq, dk, dv written once, 14 d bytes per token-head
+    in bf16.  Timed with one event pair on the launch stream around all calls.
+    Then a training step's attention work: the forward, and the backward handed
+    the forward's workspace."""
+    import la_inputs
+
+    T, H, d = w["T"], w["H"], w["d"]
+    esz = 2 if w["dtype"] == "bf16" else 4
+    block = args.block or w["block"]
+    opts = dict(seg_len=args.seg_len, value_slices=args.slices, force_scan=args.force_scan, slots=args.slots)
+    cu = torch.from_numpy(w["cu"]).cuda()
+    d0 = la_inputs.normal(la_inputs.WORKLOADS[w["name"]]["seed"], 8, (T, H, d), w["dtype"], 1.0)
+    dout0 = torch.from_numpy(d0.view(np.int16)).view(torch.bfloat16).cuda() if d0.dtype == np.uint16 \
+        else torch.from_numpy(d0).cuda()
+    del d0
+    sets = []
+    for i, (q, k, v, _) in enumerate(dev_sets):
+        dout = torch.roll(dout0, i, 0).contiguous() if i else dout0
+        sets.append((q, k, v, dout))
+    outs = (torch.empty_like(dout0), torch.empty_like(dout0), torch.empty_like(dout0), None)
+    num_seqs = len(w["cu"]) - 1
+    dt = la.LA_BF16 if w["dtype"] == "bf16" else la.LA_FP32
+    need = la.la_prefill_workspace_size_ex(T, num_seqs, H, d, block, dt, la.make_opts(**opts))
+    ws = torch.empty(max(need, 256), dtype=torch.uint8, device="cuda")
+    it = [0]
+
+    def call():
+        q, k, v, dout = sets[it[0] % len(sets)]
+        it[0] += 1
+        la.backward(q, k, v, dout, cu, block=block, want_dkv_in=False, workspace=ws, out=outs, **opts)
+
+    s = gpu_time(torch, hip, call, steps)
+    algo = T * H * 7 * d * esz
+    achieved = algo / s / 1e9
+    rec = {"workload": w["name"], "value": T * H / s, "unit": "token·heads/s", "steps": steps,
+           "gpu_ms_per_step": s * 1e3,
+           "roofline": {"bound": "hbm", "kernel": "la_prefill_backward (whole call)", "achieved": achieved,
+                        "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                        "algorithmic_bytes": algo}}
+    fo = torch.empty_like(dout0)
+    fkv = torch.empty((num_seqs, H, d, d), dtype=torch.float32, device="cuda")
+
+    def train():
+        q, k, v, dout = sets[it[0] % len(sets)]
+        it[0] += 1
+        la.prefill(q, k, v, cu, block=block, out=fo, kv_state_out=fkv, workspace=ws, **opts)
+        la.backward(q, k, v, dout, cu, block=block, want_dkv_in=False, out=outs, forward_workspace=ws, **opts)
+
+    s = gpu_time(torch, hip, train, steps)
+    talgo = T * H * 11 * d * esz  # forward 8d + backward 14d bytes per token-head (bf16)
+    tach = talgo / s / 1e9
+    rec["train_step"] = {"value": T * H / s, "unit": "token·heads/s", "gpu_ms_per_step": s * 1e3,
+                         "roofline": {"bound": "hbm", "achieved": tach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                      "frac": tach / HBM_PEAK_GBS, "algorithmic_bytes": talgo}}
+    del sets, outs, ws, fo, dout0
+    torch.cuda.empty_cache()
+    return rec
+
+
+# -------------------------------------------------------------------- decode
 
 def bench_decode(args, la, torch, hip):
     import la_inputs
@@ -331,14 +393,14 @@ def bench_decode(args, la, torch, hip):
     for i in range(10):
         la.decode(*sets[i % pool], S, out=o)
     torch.cuda.synchronize()
-    stream = torch.cuda.current_stream().cuda_stream
+    sp = torch.cuda.current_stream().cuda_stream
     e0, e1 = hip.event(), hip.event()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    hip.record(e0, stream)
+    hip.record(e0, sp)
     for i in range(steps):
         la.decode(*sets[i % pool], S, out=o)
-    hip.record(e1, stream)
+    hip.record(e1, sp)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     gpu_s = hip.elapsed_ms(e0, e1) / 1e3
@@ -346,6 +408,8 @@ def bench_decode(args, la, torch, hip):
     hip.destroy(e1)
     bytes_step = ns * H * (2 * d * d * 4 + 4 * d * 2)
     achieved = bytes_step * steps / gpu_s / 1e9
+    del S, sets, o
+    torch.cuda.empty_cache()
     return {"workload": "decode_256x64", "value": steps / wall, "unit": "steps/s", "steps": steps,
             "ms_per_step": wall / steps * 1e3, "gpu_ms_per_step": gpu_s / steps * 1e3,
             "roofline": {"bound": "hbm", "kernel": "la_decode_kernel", "achieved": achieved, "peak": HBM_PEAK_GBS,
@@ -353,88 +417,59 @@ def bench_decode(args, la, torch, hip):
                          "kernel_sources_sha": sources_sha(DECODE_SOURCES)}}
 
 
-def bench_backward(args, la, torch, hip, w, dev_sets):
-    """la_prefill_backward over the same workload: dq, dk, dv from dO with no
-    incoming state and no final-state gradient.  Algorithmic bytes per call:
-    q, k, v, dO read and dq, dk, dv written once, 14 d bytes per token-head
-    in bf16.  Timed with HIP events on the launch stream around all calls."""
-    import la_inputs
+# -------------------------------------------------------------- CPU baseline
 
-    T, H, d = w["T"], w["H"], w["d"]
-    esz = 2 if w["dtype"] == "bf16" else 4
-    block = args.block or w["block"]
-    opts = dict(seg_len=args.seg_len, value_slices=args.slices, force_scan=args.force_scan, slots=args.slots)
-    cu = torch.from_numpy(w["cu"]).cuda()
-    d0 = la_inputs.normal(la_inputs.WORKLOADS[w["name"]]["seed"], 8, (T, H, d), w["dtype"], 1.0)
-    dout0 = torch.from_numpy(d0.view(np.int16)).view(torch.bfloat16).cuda() if d0.dtype == np.uint16 \
-        else torch.from_numpy(d0).cuda()
-    sets = []
-    for i, (q, k, v, _) in enumerate(dev_sets):
-        dout = torch.roll(dout0, i, 0).contiguous() if i else dout0
-        sets.append((q, k, v, dout))
-    outs = (torch.empty_like(dout0), torch.empty_like(dout0), torch.empty_like(dout0), None)
-    num_seqs = len(w["cu"]) - 1
-    dt = la.LA_BF16 if w["dtype"] == "bf16" else la.LA_FP32
-    need = la.la_prefill_workspace_size_ex(T, num_seqs, H, d, block, dt, la.make_opts(**opts))
-    ws = torch.empty(max(need, 256), dtype=torch.uint8, device="cuda")
+def error_vs_oracle(gpu, ref) -> tuple:
+    g = np.asarray(gpu, dtype=np.float64).ravel()
+    r = np.asarray(ref, dtype=np.float64).ravel()
+    den = max(float(np.linalg.norm(r)), 1e-300)
+    return float(np.linalg.norm(g - r) / den), float(np.max(np.abs(g - r)) / max(float(np.max(np.abs(r))), 1e-300))
 
-    def call(i):
-        q, k, v, dout = sets[i % len(sets)]
-        la.backward(q, k, v, dout, cu, block=block, want_dkv_in=False, workspace=ws, out=outs, **opts)
 
-    for i in range(max(1, args.warmup // 4)):
-        call(i)
-    torch.cuda.synchronize()
-    K = max(1, args.steps // 4)
-    stream = torch.cuda.current_stream().cuda_stream
-    e0, e1 = hip.event(), hip.event()
-    torch.cuda.synchronize()
+def cpu_baseline(w, target_cpu_s: float = 12.0) -> dict:
+    """The fp64 oracle as it stands (recurrent form, all host threads) on a
+    bounded sample of the workload: its first Ts tokens of every head (for a
+    one-document workload, exactly the first Ts outputs of the full call),
+    repeated until about target_cpu_s seconds of CPU time are spent.  The GPU
+    outputs of those tokens are compared with the oracle's."""
+    import oracle
+
+    oracle.build()
+    T, H = w["T"], w["H"]
+    one_doc = len(w["cu"]) == 2
+    Ts = min(T, 131072) if one_doc else T
+    cu = np.array([0, Ts], dtype=np.int32) if one_doc else w["cu"]
+    q, k, v = (np.ascontiguousarray(w[x][:Ts]) for x in ("q", "k", "v"))
+    reps, wall, err = 0, 0.0, None
+    while True:
+        t0 = time.perf_counter()
+        o_ref, kv_ref = oracle.recurrent(q, k, v, cu, want_o=True, want_state=not one_doc or Ts == T)
+        wall += time.perf_counter() - t0
+        if err is None:
+            g = w["gpu_o"][:Ts]
+            g = (g.float() if g.dtype.is_floating_point and g.element_size() == 2 else g).cpu().numpy()
+            e_o = error_vs_oracle(g, o_ref)
+            err = {"o_rel_l2": e_o[0], "o_max_abs_rel": e_o[1], "compared": f"o of tokens [0, {Ts}), all heads"}
+            if kv_ref is not None:
+                e_kv = error_vs_oracle(w["gpu_kv"].cpu().numpy(), kv_ref)
+                err.update(kv_state_rel_l2=e_kv[0], kv_state_max_abs_rel=e_kv[1])
+        del o_ref, kv_ref
+        reps += 1
+        threads = oracle.last_threads()
+        if wall * threads >= target_cpu_s or reps >= 50:
+            break
+    th = Ts * H * reps / wall
+    hq = max(1, H // 4)
+    Ts1 = min(Ts, 32768)
+    cu1 = np.array([0, Ts1], dtype=np.int32) if one_doc else cu
     t0 = time.perf_counter()
-    hip.record(e0, stream)
-    for i in range(K):
-        call(i)
-    hip.record(e1, stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    gpu_s = hip.elapsed_ms(e0, e1) / 1e3
-    hip.destroy(e0)
-    hip.destroy(e1)
-    algo = T * H * 14 * d * esz // 2
-    achieved = algo * K / gpu_s / 1e9
-    rec = {"workload": w["name"], "value": T * H * K / wall, "unit": "token·heads/s", "steps": K,
-           "ms_per_step": wall / K * 1e3, "gpu_ms_per_step": gpu_s / K * 1e3,
-           "roofline": {"bound": "hbm", "kernel": "la_prefill_backward (3 prefill passes)", "achieved": achieved,
-                        "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                        "algorithmic_bytes": algo}}
-
-    # One training step's attention work: the forward, then the backward handed
-    # the forward's workspace (its dq pass reuses the forward's segment states).
-    fo = torch.empty_like(dout0)
-    fkv = torch.empty((num_seqs, H, d, d), dtype=torch.float32, device="cuda")
-
-    def train(i):
-        q, k, v, dout = sets[i % len(sets)]
-        la.prefill(q, k, v, cu, block=block, out=fo, kv_state_out=fkv, workspace=ws, **opts)
-        la.backward(q, k, v, dout, cu, block=block, want_dkv_in=False, out=outs, forward_workspace=ws, **opts)
-
-    for i in range(max(1, args.warmup // 4)):
-        train(i)
-    e0, e1 = hip.event(), hip.event()
-    torch.cuda.synchronize()
-    hip.record(e0, stream)
-    for i in range(K):
-        train(i)
-    hip.record(e1, stream)
-    torch.cuda.synchronize()
-    tr_s = hip.elapsed_ms(e0, e1) / 1e3
-    hip.destroy(e0)
-    hip.destroy(e1)
-    talgo = T * H * 22 * d * esz // 2  # forward 8d + backward 14d bytes per token-head
-    tach = talgo * K / tr_s / 1e9
-    rec["train_step"] = {"value": T * H * K / tr_s, "unit": "token·heads/s", "gpu_ms_per_step": tr_s / K * 1e3,
-                         "roofline": {"bound": "hbm", "achieved": tach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                                      "frac": tach / HBM_PEAK_GBS, "algorithmic_bytes": talgo}}
-    return rec
+    oracle.recurrent(q[:Ts1] if one_doc else q, k[:Ts1] if one_doc else k, v[:Ts1] if one_doc else v, cu1,
+                     want_o=True, want_state=True, heads=(0, hq), nthreads=1)
+    one = (Ts1 if one_doc else Ts) * hq / (time.perf_counter() - t0)
+    return {"value": th, "unit": "token·heads/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {Ts} tokens x {H} heads of {w['name']} (d={w['d']}), fp64 recurrent form, "
+                      f"{reps} repetition(s), {wall:.2f} s wall on {threads} threads",
+            "single_thread_value": one, "cpu_model": cpu_model(), "error_vs_oracle": err}
 
 
 def decode_cpu_baseline(S_sample, steps: int = 200) -> dict:
@@ -459,15 +494,22 @@ def decode_cpu_baseline(S_sample, steps: int = 200) -> dict:
                                         f"{wall:.2f} s wall, scaled to the whole batch"}
 
 
+# ------------------------------------------------------------ profile passes
+
 def profile_pass(args, la, torch):
-    """Short run for rocprofv3 counter passes: a 256 MiB device copy (the
-    calibration kernel) then a few prefill steps of the workload."""
+    """Short run for rocprofv3 counter passes: a 256 MiB 1-read + 1-write
+    stream (la_bench_stream, the calibration kernel: 268,435,456 bytes read
+    and written), then a few calls of the workload."""
     import la_inputs
 
+    lib = la.load()
     src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda").fill_(1)
     dst = torch.empty_like(src)
-    dst.copy_(src)
+    st = lib.la_bench_stream(0, ctypes.c_void_p(src.data_ptr()), None, None, ctypes.c_void_p(dst.data_ptr()),
+                             256 << 20, 256, 0, ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    assert st == 0, st
     torch.cuda.synchronize()
+    del src, dst
     w = la_inputs.prefill_inputs(args.workload)
     dev = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
     q, k, v = dev(w["q"]), dev(w["k"]), dev(w["v"])
@@ -486,20 +528,18 @@ def profile_pass(args, la, torch):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=2000)
-    ap.add_argument("--warmup", type=int, default=100)
-    ap.add_argument("--workload", default="prefill_8k",
-                    choices=["prefill_8k", "varlen_128k", "long_1m", "tiny_fp32"])
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="long_1m", choices=["long_1m", "varlen_128k", "prefill_8k", "tiny_fp32"])
     ap.add_argument("--block", type=int, default=0)
     ap.add_argument("--seg-len", type=int, default=0)
     ap.add_argument("--slices", type=int, default=0)
     ap.add_argument("--force-scan", action="store_true")
     ap.add_argument("--slots", type=int, default=0, help="tile slots of the block loop: 0 automatic, 2 or 3")
-    ap.add_argument("--rotate", type=int, default=8, help="input sets cycled through the timed steps")
-    ap.add_argument("--event-stride", type=int, default=0,
-                    help="stamp the block-loop kernel of every n-th timed step with events "
-                         "(0: every 8th with 128 or more steps, else every one)")
+    ap.add_argument("--rotate", type=int, default=8, help="input sets cycled through the timed steps (at most 8 GiB)")
+    ap.add_argument("--small-steps", type=int, default=2000, help="timed steps of the 8k workload")
     ap.add_argument("--decode-steps", type=int, default=1000)
+    ap.add_argument("--no-extra", action="store_true", help="headline workload only")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -509,7 +549,8 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py runs on one GPU only: the library has no multi-GPU path (use --gpus 1)", file=sys.stderr)
+        print("bench.py measures one GPU: the library has no multi-GPU path, so only --gpus 1 is valid",
+              file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -524,25 +565,63 @@ def main():
         profile_pass(args, la, torch)
         return
     hip = Hip()
-    rec, w = bench_prefill(args, la, torch, hip)
+    ceil = stream_ceilings(la, torch, hip)
+    prefill_ceiling = ceil["stream_3r1w"]["GBs"]
+
+    small = args.workload in ("prefill_8k", "tiny_fp32")
+    steps = args.small_steps if small and args.steps == 20 else args.steps
+    head, w = bench_prefill(args.workload, args, la, torch, hip, steps, args.warmup,
+                            graph=small and not args.no_graph, keep_sets=not args.no_backward)
+    with_ceiling(head["roofline"], prefill_ceiling)
+    head["whole_call"]["frac_of_measured_ceiling"] = head["whole_call"]["achieved"] / prefill_ceiling
+    rec = {
+        "metric": METRIC,
+        "value": head["value"],
+        "unit": head["unit"],
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": args.warmup,
+        "ms_per_step": head["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w["dtype"],
+        "data": "synthetic",
+        "config": head["config"],
+        "roofline": head["roofline"],
+        "whole_call": head["whole_call"],
+        "gpu_ms_per_step": head["gpu_ms_per_step"],
+        "ceilings": ceil,
+    }
     if not args.no_backward:
-        rec["backward"] = bench_backward(args, la, torch, hip, w, w.pop("dev_sets"))
-    else:
-        w.pop("dev_sets")
-    if not args.no_decode:
-        rec["decode"] = bench_decode(args, la, torch, hip)
-    copy = copy_bandwidth(torch, hip)
-    for part in (rec, rec.get("backward"), rec.get("decode")):
-        if part:
-            part["roofline"]["measured_copy_GBs"] = copy
-            part["roofline"]["frac_of_measured_copy"] = part["roofline"]["achieved"] / copy
+        rec["backward"] = bench_backward(args, la, torch, hip, w, w.pop("dev_sets"), max(2, args.steps // 4))
+        with_ceiling(rec["backward"]["roofline"], prefill_ceiling)
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w)
-        rec["error_vs_oracle"] = w.get("error_vs_oracle")
-        if "decode" in rec:
-            rec["decode"]["cpu_baseline"] = decode_cpu_baseline(DECODE_SAMPLE["S"])
     else:
         rec["cpu_baseline"] = None
+    del w
+    torch.cuda.empty_cache()
+
+    if not args.no_extra:
+        extras = {}
+        for name in ("varlen_128k", "long_1m", "prefill_8k"):
+            if name == args.workload:
+                continue
+            sm = name == "prefill_8k"
+            r, wx = bench_prefill(name, args, la, torch, hip, args.small_steps if sm else args.steps, args.warmup,
+                                  graph=sm and not args.no_graph)
+            with_ceiling(r["roofline"], prefill_ceiling)
+            r["whole_call"]["frac_of_measured_ceiling"] = r["whole_call"]["achieved"] / prefill_ceiling
+            extras[name] = r
+            del wx
+            torch.cuda.empty_cache()
+        rec["workloads"] = extras
+    if not args.no_decode:
+        rec["decode"] = bench_decode(args, la, torch, hip)
+        with_ceiling(rec["decode"]["roofline"], ceil["copy_1r1w"]["GBs"])
+        if not args.no_cpu_baseline:
+            rec["decode"]["cpu_baseline"] = decode_cpu_baseline(DECODE_SAMPLE["S"])
     print(json.dumps(rec))
 
 

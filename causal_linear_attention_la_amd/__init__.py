@@ -20,7 +20,8 @@ LA_OK, LA_ERR_INVALID_ARG, LA_ERR_UNSUPPORTED, LA_ERR_WORKSPACE, LA_ERR_HIP = ra
 LA_BF16, LA_FP32 = 0, 1
 
 EXPORTED = ("la_prefill", "la_decode", "la_prefill_workspace_size", "la_status_string", "la_prefill_plan",
-            "la_prefill_workspace_size_ex", "la_prefill_ex", "la_prefill_resume", "la_prefill_backward")
+            "la_prefill_workspace_size_ex", "la_prefill_ex", "la_prefill_resume", "la_prefill_backward",
+            "la_bench_stream")
 
 
 class LAError(RuntimeError):
@@ -85,6 +86,8 @@ def load():
     lib.la_prefill_plan.restype = ctypes.c_int
     lib.la_status_string.argtypes = [ctypes.c_int]
     lib.la_status_string.restype = ctypes.c_char_p
+    lib.la_bench_stream.argtypes = [i32, vp, vp, vp, vp, sz, i32, i32, vp]
+    lib.la_bench_stream.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -124,6 +127,10 @@ def la_prefill_backward(q, k, v, dout, cu_seqlens, H, d, block, kv_state_in, dkv
 
 def la_decode(q, k, v, kv_state_inout, o, num_seqs, H, d, dtype, stream) -> int:
     return load().la_decode(q, k, v, kv_state_inout, o, num_seqs, H, d, dtype, stream)
+
+
+def la_bench_stream(mode, a, b, c, dst, nbytes, workgroups, nontemporal, stream) -> int:
+    return load().la_bench_stream(mode, a, b, c, dst, nbytes, workgroups, nontemporal, stream)
 
 
 def la_prefill_workspace_size(total_tokens, num_seqs, H, d, block, dtype) -> int:
@@ -185,6 +192,51 @@ def _ptr(t):
     return ctypes.c_void_p(t.data_ptr()) if t is not None else None
 
 
+def _check(cond: bool, exc, msg: str):
+    if not cond:
+        raise exc(msg)
+
+
+def _check_tensors(ref, named, where: str):
+    """Every tensor in `named` ({name: (tensor or None, dtype or None for
+    ref's dtype, shape)}) has that dtype and shape, is contiguous and sits on
+    ref's device, which is a GPU.  Checked in that order, before any pointer
+    reaches the C ABI: a host pointer, a wrong dtype or a short buffer would
+    otherwise be read or written by the kernels."""
+    import torch
+
+    for name, (t, dtype, shape) in named.items():
+        if t is None:
+            continue
+        _check(isinstance(t, torch.Tensor), TypeError, f"{where}: {name} must be a torch.Tensor")
+        want = ref.dtype if dtype is None else dtype
+        _check(t.dtype == want, TypeError, f"{where}: {name} has dtype {t.dtype}, expected {want}")
+        _check(tuple(t.shape) == tuple(shape), ValueError,
+               f"{where}: {name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+        _check(t.is_contiguous(), ValueError, f"{where}: {name} must be contiguous")
+        _check(t.device == ref.device, ValueError, f"{where}: {name} is on {t.device}, q is on {ref.device}")
+    _check(ref.is_cuda, ValueError, f"{where}: tensors must be on a GPU (q is on {ref.device})")
+
+
+def _check_cu(cu_seqlens, where: str):
+    import torch
+
+    _check(isinstance(cu_seqlens, torch.Tensor), TypeError, f"{where}: cu_seqlens must be a torch.Tensor")
+    _check(cu_seqlens.dim() == 1 and cu_seqlens.numel() >= 2, ValueError,
+           f"{where}: cu_seqlens must be 1-D with num_seqs + 1 >= 2 entries")
+    _check(cu_seqlens.dtype == torch.int32, TypeError, f"{where}: cu_seqlens must be int32, got {cu_seqlens.dtype}")
+
+
+def _check_ws(ws, ref, where: str):
+    import torch
+
+    if ws is None:
+        return
+    _check(isinstance(ws, torch.Tensor), TypeError, f"{where}: workspace must be a torch.Tensor")
+    _check(ws.is_contiguous(), ValueError, f"{where}: workspace must be contiguous")
+    _check(ws.device == ref.device, ValueError, f"{where}: workspace is on {ws.device}, q is on {ref.device}")
+
+
 def prefill(q, k, v, cu_seqlens, block: int = 64, want_state: bool = True, out=None, kv_state_out=None,
             workspace=None, seg_len: int = 0, value_slices: int = 0, force_scan: bool = False, stream=None,
             begin_event=None, end_event=None, variant: int = 0, kv_state_in=None, slots: int = 0):
@@ -198,9 +250,18 @@ def prefill(q, k, v, cu_seqlens, block: int = 64, want_state: bool = True, out=N
     """
     import torch
 
+    _check(q.dim() == 3, ValueError, f"prefill: q must be [T, H, d], got shape {tuple(q.shape)}")
     T, H, d = q.shape
     dt = _dtype_code(q)
+    _check_cu(cu_seqlens, "prefill")
     num_seqs = cu_seqlens.numel() - 1
+    st_shape = (num_seqs, H, d, d)
+    _check_tensors(q, {"k": (k, None, q.shape), "v": (v, None, q.shape), "out": (out, None, q.shape),
+                       "kv_state_out": (kv_state_out, torch.float32, st_shape),
+                       "kv_state_in": (kv_state_in, torch.float32, st_shape),
+                       "cu_seqlens": (cu_seqlens, torch.int32, (num_seqs + 1,)), "q": (q, None, q.shape)},
+                   "prefill")
+    _check_ws(workspace, q, "prefill")
     o = out if out is not None else torch.empty_like(q)
     kv = kv_state_out
     if kv is None and want_state:
@@ -232,9 +293,23 @@ def backward(q, k, v, dout, cu_seqlens, block: int = 64, kv_state_in=None, dkv_s
     Returns (dq, dk, dv, dkv_state_in or None)."""
     import torch
 
+    _check(q.dim() == 3, ValueError, f"backward: q must be [T, H, d], got shape {tuple(q.shape)}")
     T, H, d = q.shape
     dt = _dtype_code(q)
+    _check_cu(cu_seqlens, "backward")
     num_seqs = cu_seqlens.numel() - 1
+    st_shape = (num_seqs, H, d, d)
+    named = {"k": (k, None, q.shape), "v": (v, None, q.shape), "dout": (dout, None, q.shape),
+             "kv_state_in": (kv_state_in, torch.float32, st_shape),
+             "dkv_state_out": (dkv_state_out, torch.float32, st_shape),
+             "cu_seqlens": (cu_seqlens, torch.int32, (num_seqs + 1,)), "q": (q, None, q.shape)}
+    if out is not None:
+        _check(len(out) == 4, ValueError, "backward: out must be (dq, dk, dv, dkv_in)")
+        named.update({"dq": (out[0], None, q.shape), "dk": (out[1], None, q.shape), "dv": (out[2], None, q.shape),
+                      "dkv_in": (out[3], torch.float32, st_shape)})
+    _check_tensors(q, named, "backward")
+    _check_ws(workspace, q, "backward")
+    _check_ws(forward_workspace, q, "backward")
     if out is not None:
         dq, dk, dv, dkv_in = out
     else:
@@ -261,7 +336,13 @@ def decode(q, k, v, kv_state, out=None, stream=None):
     q, k, v: [num_seqs, H, d].  Returns o."""
     import torch
 
+    _check(q.dim() == 3, ValueError, f"decode: q must be [num_seqs, H, d], got shape {tuple(q.shape)}")
     num_seqs, H, d = q.shape
+    _dtype_code(q)
+    _check(kv_state is not None, ValueError, "decode: kv_state is required")
+    _check_tensors(q, {"k": (k, None, q.shape), "v": (v, None, q.shape), "out": (out, None, q.shape),
+                       "kv_state": (kv_state, torch.float32, (num_seqs, H, d, d)), "q": (q, None, q.shape)},
+                   "decode")
     o = out if out is not None else torch.empty_like(q)
     st = la_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(kv_state), _ptr(o), num_seqs, H, d, _dtype_code(q),
                    _stream_ptr(stream))

@@ -184,7 +184,6 @@ la_status la_decode(const void* q, const void* k, const void* v, float* kv_state
     p.S = kv_state_inout;
     p.o = o;
     p.pairs = (int64_t)num_seqs * H;
-    if (p.pairs > INT32_MAX) return LA_ERR_UNSUPPORTED;
     hipError_t e = la::launch_decode(p, d, (int)dtype, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? LA_OK : LA_ERR_HIP;
 }

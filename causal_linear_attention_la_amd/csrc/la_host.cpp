@@ -11,6 +11,14 @@ namespace la {
 namespace {
 
 constexpr int kNumCUs = 256;      // MI355X compute units
+// A dispatch's grid is at most 2^32 - 1 work-items per dimension; the block
+// loop and the segment-state kernel launch 8 * ceil(units / 8) workgroups of
+// 256 lanes, so a plan may hold at most this many units.
+constexpr int64_t kMaxUnits = 8 * (((int64_t)1 << 32) - 1) / (8 * 256);
+// The transpose-read kernels address a 64-token block of one head through a
+// buffer descriptor: row offsets up to 64 rows of H * d * 2 bytes must fit the
+// descriptor's 32-bit range.
+constexpr int64_t kMaxBlockBytes = ((int64_t)1 << 32) - 1;
 constexpr int kUnitsTarget = 256; // block-loop workgroups to aim for (one per CU)
 constexpr int kMinSegment = 256;  // shorter segments spend more on state traffic than they gain
 constexpr int kMaxLookback = 16;  // a unit sums at most this many segment states
@@ -59,8 +67,12 @@ la_status make_plan(int64_t T, int32_t num_seqs, int32_t H, int32_t d, int32_t b
         if (S < 1 || d % S != 0) return false;
         return main_fits((int)es, d, block, d / S);
     };
-    // the transpose-read block loop: bf16, d >= 64, 64-token blocks, slices >= 64 columns
-    auto v2_ok = [&](int32_t S) { return dtype == LA_BF16 && d >= 64 && block == 64 && d / S >= 64; };
+    // the transpose-read block loop: bf16, d >= 64, 64-token blocks, slices >= 64 columns, and a
+    // block of rows (64 rows of H * d bf16) addressable with 32-bit offsets
+    auto v2_ok = [&](int32_t S) {
+        return dtype == LA_BF16 && d >= 64 && block == 64 && d / S >= 64 &&
+               (int64_t)H * d * 2 * block <= kMaxBlockBytes;
+    };
     const int32_t variant = opts ? opts->variant : 0;
     if (variant < 0 || variant > 2) return LA_ERR_UNSUPPORTED;
 
@@ -136,8 +148,10 @@ la_status make_plan(int64_t T, int32_t num_seqs, int32_t H, int32_t d, int32_t b
     if (nseg > INT32_MAX) return LA_ERR_UNSUPPORTED;
     p.nseg = (int32_t)nseg;
     p.units = nseg * (int64_t)H * p.S;
-    if (p.units > (int64_t)INT32_MAX * 8) return LA_ERR_UNSUPPORTED;
+    if (p.units > kMaxUnits) return LA_ERR_UNSUPPORTED;
     p.scan = p.nseg > 1 && ((opts && opts->force_scan) || needs_scan(p.L, p.W)) ? 1 : 0;
+    // the scan kernel runs one lane per 4 state entries of a segment (H * d * d entries)
+    if (p.scan && (int64_t)H * d * d / 4 > (((int64_t)1 << 32) - 1)) return LA_ERR_UNSUPPORTED;
     const int32_t slots = opts ? opts->slots : 0;
     if (!(slots == 0 || slots == 2 || slots == 3)) return LA_ERR_UNSUPPORTED;
     const bool three_ok = p.variant == 2 && d == 128;
@@ -227,6 +241,8 @@ la_status validate_decode(const void* q, const void* k, const void* v, const flo
     int64_t pairs, n, ns;
     if (!mul_ok(num_seqs, H, pairs) || !mul_ok(pairs, (int64_t)d * es, n) || !mul_ok(pairs, (int64_t)d * d * 4, ns))
         return LA_ERR_INVALID_ARG;
+    // one 256-lane workgroup per (sequence, head): the grid's work-items must fit 32 bits
+    if (pairs * 256 > (((int64_t)1 << 32) - 1)) return LA_ERR_UNSUPPORTED;
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(S, 16) || !aligned(o, 16))
         return LA_ERR_INVALID_ARG;
     const size_t tn = (size_t)n, sn = (size_t)ns;

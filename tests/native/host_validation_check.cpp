@@ -3,6 +3,7 @@
 #include <cstdint>
 #include <cstdio>
 #include <cstdlib>
+#include <climits>
 #include <initializer_list>
 
 #include "../../causal_linear_attention_la_amd/csrc/la_host.h"
@@ -113,6 +114,24 @@ int main() {
     EXPECT(make_plan(10, 1, 8, 128, 64, 7, nullptr, &p) == LA_ERR_UNSUPPORTED);
     EXPECT(make_plan((int64_t)1 << 33, 1, 8, 128, 64, LA_BF16, nullptr, &p) == LA_ERR_INVALID_ARG);
 
+    // dispatch limits: a plan whose grid would not fit one dispatch is refused
+    // before anything is enqueued (at most 2^32 - 1 work-items: 16,777,208 units)
+    la_prefill_opts o6{};
+    o6.seg_len = 64;
+    o6.value_slices = 1;
+    o6.variant = 1;
+    EXPECT(make_plan((int64_t)64 * 262143, 1, 64, 16, 64, LA_BF16, &o6, &p) == LA_OK && p.units == 16777152);
+    EXPECT(make_plan((int64_t)64 * 262144, 1, 64, 16, 64, LA_BF16, &o6, &p) == LA_ERR_UNSUPPORTED);
+    EXPECT(make_plan(INT32_MAX, 1, 8, 128, 64, LA_BF16, &o6, &p) == LA_ERR_UNSUPPORTED);
+    // the transpose-read loop needs 64 rows of H * d bf16 within 32-bit offsets
+    EXPECT(make_plan(1024, 1, 262143, 128, 64, LA_BF16, nullptr, &p) == LA_OK && p.variant == 2);
+    EXPECT(make_plan(1024, 1, 262144, 128, 64, LA_BF16, nullptr, &p) == LA_OK && p.variant == 1);
+    la_prefill_opts o7{};
+    o7.variant = 2;
+    EXPECT(make_plan(1024, 1, 262144, 128, 64, LA_BF16, &o7, &p) == LA_ERR_UNSUPPORTED);
+    EXPECT(make_plan(1024, 1, 524287, 64, 64, LA_BF16, &o7, &p) == LA_OK && p.variant == 2);
+    EXPECT(make_plan(1024, 1, 524288, 64, 64, LA_BF16, &o7, &p) == LA_ERR_UNSUPPORTED);
+
     // pointer errors
     const int64_t T = 8192;
     EXPECT(make_plan(T, 1, 8, 128, 64, LA_BF16, nullptr, &p) == LA_OK);
@@ -147,6 +166,9 @@ int main() {
     EXPECT(validate_decode(q, k, v, static_cast<float*>(P(G + 16)), o, 256, 64, 128, LA_BF16) == LA_ERR_INVALID_ARG);
     EXPECT(validate_decode(q, k, v, static_cast<float*>(P(6 * G + 4)), o, 256, 64, 128, LA_BF16) == LA_ERR_INVALID_ARG);
     EXPECT(validate_decode(q, k, v, kv, o, 256, 64, 128, 5) == LA_ERR_UNSUPPORTED);
+    // one workgroup of 256 lanes per pair: at most 16,777,215 pairs in a grid
+    EXPECT(validate_decode(q, k, v, kv, o, 65535, 256, 16, LA_BF16) == LA_OK);
+    EXPECT(validate_decode(q, k, v, kv, o, 65536, 256, 16, LA_BF16) == LA_ERR_UNSUPPORTED);
 
     if (failures) {
         std::fprintf(stderr, "%d check(s) failed\n", failures);

@@ -1,7 +1,8 @@
 """C-ABI checks that need no GPU: the library loads, exports every entry point
-include/la.h declares, and rejects bad arguments on the host before anything
-is enqueued (only invalid calls are made here)."""
+the headers in include/ declare, and rejects bad arguments on the host before
+anything is enqueued (only invalid calls are made here)."""
 import ast
+import glob
 import ctypes
 import os
 import re
@@ -12,7 +13,7 @@ import pytest
 import causal_linear_attention_la_amd as la
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "la.h")
+HEADERS = sorted(glob.glob(os.path.join(ROOT, "include", "*.h")))
 
 
 @pytest.fixture(scope="module")
@@ -23,15 +24,17 @@ def lib():
 
 
 def declared_functions():
-    text = open(HEADER, encoding="utf-8").read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    names = re.findall(r"\b(?:la_status|size_t|const char\s*\*)\s+(la_\w+)\s*\(", text)
-    return sorted(set(names))
+    names = set()
+    for h in HEADERS:
+        text = open(h, encoding="utf-8").read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names |= set(re.findall(r"\b(?:la_status|size_t|const char\s*\*)\s+(la_\w+)\s*\(", text))
+    return sorted(names)
 
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert set(la.EXPORTED) <= set(names)
+    assert set(la.EXPORTED) == set(names)
     out = subprocess.run(["nm", "-D", "--defined-only", la.LIB_PATH], capture_output=True, text=True).stdout
     exported = set(re.findall(r"\bT (la_\w+)", out))
     missing = [n for n in names if n not in exported]
@@ -98,6 +101,21 @@ def test_decode_rejects(lib, kw, status):
     vp = lambda x: ctypes.c_void_p(x) if x else None
     assert la.la_decode(vp(a["q"]), vp(a["k"]), vp(a["v"]), vp(a["S"]), vp(a["o"]), a["num_seqs"], a["H"], a["d"],
                         a["dtype"], None) == status
+
+
+@pytest.mark.parametrize("args", [
+    (3, G, 0, 0, 4 * G, 1 << 20, 256, 0),       # unknown mode
+    (0, 0, 0, 0, 4 * G, 1 << 20, 256, 0),       # no source
+    (1, G, 0, 3 * G, 4 * G, 1 << 20, 256, 0),   # three-source mode with a missing source
+    (0, G, 0, 0, 0, 1 << 20, 256, 0),           # no destination
+    (0, G + 8, 0, 0, 4 * G, 1 << 20, 256, 0),   # misaligned source
+    (0, G, 0, 0, 4 * G, 100, 256, 0),           # size not a multiple of 16
+    (0, G, 0, 0, 4 * G, 1 << 20, 0, 0),         # no workgroups
+])
+def test_bench_stream_rejects(lib, args):
+    mode, a, b, c, dst, n, wgs, nt = args
+    vp = lambda x: ctypes.c_void_p(x) if x else None
+    assert la.la_bench_stream(mode, vp(a), vp(b), vp(c), vp(dst), n, wgs, nt, None) == la.LA_ERR_INVALID_ARG
 
 
 def test_plans(lib):
