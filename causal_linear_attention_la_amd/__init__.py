@@ -21,7 +21,7 @@ LA_BF16, LA_FP32 = 0, 1
 
 EXPORTED = ("la_prefill", "la_decode", "la_prefill_workspace_size", "la_status_string", "la_prefill_plan",
             "la_prefill_workspace_size_ex", "la_prefill_ex", "la_prefill_resume", "la_prefill_backward",
-            "la_bench_stream")
+            "la_bench_stream", "la_prefill_noalloc")
 
 
 class LAError(RuntimeError):
@@ -86,6 +86,8 @@ def load():
     lib.la_prefill_plan.restype = ctypes.c_int
     lib.la_status_string.argtypes = [ctypes.c_int]
     lib.la_status_string.restype = ctypes.c_char_p
+    lib.la_prefill_noalloc.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, vp, i32, i64, ctypes.c_int, vp]
+    lib.la_prefill_noalloc.restype = ctypes.c_int
     lib.la_bench_stream.argtypes = [i32, vp, vp, vp, vp, sz, i32, i32, vp]
     lib.la_bench_stream.restype = ctypes.c_int
     _lib = lib
@@ -127,6 +129,12 @@ def la_prefill_backward(q, k, v, dout, cu_seqlens, H, d, block, kv_state_in, dkv
 
 def la_decode(q, k, v, kv_state_inout, o, num_seqs, H, d, dtype, stream) -> int:
     return load().la_decode(q, k, v, kv_state_inout, o, num_seqs, H, d, dtype, stream)
+
+
+def la_prefill_noalloc(q, k, v, o, cu_seqlens, H, d, block, kv_state_out, num_seqs, total_tokens, dtype,
+                       stream) -> int:
+    return load().la_prefill_noalloc(q, k, v, o, cu_seqlens, H, d, block, kv_state_out, num_seqs, total_tokens,
+                                     dtype, stream)
 
 
 def la_bench_stream(mode, a, b, c, dst, nbytes, workgroups, nontemporal, stream) -> int:

@@ -1,13 +1,43 @@
 // C ABI (include/la.h): validate on the host, plan, enqueue.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "../../include/la.h"
 #include "la_host.h"
 #include "la_launch.h"
 
 using la::Plan;
 
+// Workspace of la_prefill_noalloc: one copy per GPU, in device memory for as
+// long as the process runs.  On the host this name is only a handle for
+// hipGetSymbolAddress, never an address a kernel may use.
+static __device__ __align__(256) unsigned char scratch[LA_NOALLOC_SCRATCH_BYTES];
+
 namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// Device address of `scratch` on the current device: looked up once per
+// device (with that device current) and kept.
+la_status scratch_on_current_device(void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return LA_ERR_HIP;
+    void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+        if (!p) {
+            if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return LA_ERR_HIP;
+            g_scratch_ptr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return LA_OK;
+}
 
 // Fills the launch parameters of one validated prefill pass and enqueues it.
 la_status enqueue_prefill(const Plan& plan, const void* q, const void* k, const void* v, void* o, const int32_t* cu,
@@ -171,6 +201,26 @@ la_status la_prefill(const void* q, const void* k, const void* v, void* o, const
                      la_dtype dtype, void* workspace, size_t workspace_bytes, void* stream) {
     return la_prefill_ex(q, k, v, o, cu_seqlens, H, d, block, kv_state_out, num_seqs, total_tokens, dtype, workspace,
                          workspace_bytes, stream, nullptr);
+}
+
+la_status la_prefill_noalloc(const void* q, const void* k, const void* v, void* o, const int32_t* cu_seqlens,
+                             int32_t H, int32_t d, int32_t block, float* kv_state_out, int32_t num_seqs,
+                             int64_t total_tokens, la_dtype dtype, void* stream) {
+    // the plan alone gives the workspace size: reject before touching the device
+    Plan plan;
+    la_status st = la::make_plan(total_tokens, num_seqs, H, d, block, (int)dtype, nullptr, &plan);
+    if (st != LA_OK) return st;
+    if (plan.ws_bytes > (size_t)LA_NOALLOC_SCRATCH_BYTES) return LA_ERR_WORKSPACE;
+    void* ws = nullptr;
+    if (plan.ws_bytes > 0) {
+        st = scratch_on_current_device(&ws);
+        if (st != LA_OK) return st;
+    }
+    st = la::validate_prefill(q, k, v, o, cu_seqlens, H, d, block, nullptr, kv_state_out, num_seqs, total_tokens,
+                              (int)dtype, ws, plan.ws_bytes, nullptr, &plan);
+    if (st != LA_OK) return st;
+    return enqueue_prefill(plan, q, k, v, o, cu_seqlens, H, d, block, nullptr, 0, kv_state_out, 0, num_seqs,
+                           total_tokens, dtype, ws, stream, nullptr, nullptr);
 }
 
 la_status la_decode(const void* q, const void* k, const void* v, float* kv_state_inout, void* o, int32_t num_seqs,

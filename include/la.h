@@ -22,7 +22,8 @@
  *
  * Ownership and execution
  *   Every pointer is caller-owned device memory.  The library allocates, frees
- *   and synchronises nothing and keeps no mutable global state, so calls are
+ *   and synchronises nothing and, apart from la_prefill_noalloc's static
+ *   device array (see there), keeps no mutable global state, so calls are
  *   reentrant and thread-safe.  Work is enqueued on `stream` (a hipStream_t;
  *   NULL = the null stream) and the call returns after enqueueing.
  *
@@ -106,6 +107,29 @@ la_status la_prefill(const void* q, const void* k, const void* v, void* o, const
  */
 la_status la_decode(const void* q, const void* k, const void* v, float* kv_state_inout, void* o, int32_t num_seqs,
                     int32_t H, int32_t d, la_dtype dtype, void* stream);
+
+/* Prefill that allocates nothing and takes no workspace argument: the same
+ * operation, arguments and results as la_prefill (the same kernels and plan,
+ * so bit-identical outputs), for callers that cannot allocate device memory
+ * around a call -- code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation.  The segment states that la_prefill keeps in the
+ * caller's workspace go instead to a static device array inside the library,
+ * LA_NOALLOC_SCRATCH_BYTES (32 MiB) per GPU, held by each GPU the library runs
+ * on until the process ends.  Its address is looked up once per device, on the
+ * first call with that device current.
+ *
+ *   Returns LA_ERR_WORKSPACE, with nothing enqueued, when the call's plan needs
+ *   more than LA_NOALLOC_SCRATCH_BYTES of workspace (la_prefill_workspace_size()
+ *   gives that figure); shapes of up to 256 x 64 KiB segment states fit.
+ *   Every call on one GPU shares that GPU's array: calls that overlap in time
+ *   on one GPU (two streams, two threads) race and give wrong results; calls
+ *   ordered on one stream are safe.  No content needs clearing between calls.
+ *   Other arguments, errors and ownership as in la_prefill.
+ */
+#define LA_NOALLOC_SCRATCH_BYTES (32u << 20)
+la_status la_prefill_noalloc(const void* q, const void* k, const void* v, void* o, const int32_t* cu_seqlens,
+                             int32_t H, int32_t d, int32_t block, float* kv_state_out, int32_t num_seqs,
+                             int64_t total_tokens, la_dtype dtype, void* stream);
 
 /* Human-readable status name (static string). */
 const char* la_status_string(la_status s);

@@ -118,6 +118,20 @@ def test_bench_stream_rejects(lib, args):
     assert la.la_bench_stream(mode, vp(a), vp(b), vp(c), vp(dst), n, wgs, nt, None) == la.LA_ERR_INVALID_ARG
 
 
+def test_noalloc_refuses_plans_beyond_its_array(lib):
+    """la_prefill_noalloc refuses, on the host and before any device call, a
+    plan whose workspace exceeds the library's static 32 MiB array."""
+    T, H, d, B = 353, 274, 128, 32  # two segments of 352 tokens x 274 heads of 64 KiB states
+    assert la.la_prefill_plan(T, 1, H, d, B, la.LA_BF16)["workspace_bytes"] > 32 << 20
+    vp = ctypes.c_void_p
+    st = la.la_prefill_noalloc(vp(G), vp(2 * G), vp(3 * G), vp(4 * G), vp(5 * G), H, d, B, vp(6 * G), 1, T,
+                               la.LA_BF16, None)
+    assert st == la.LA_ERR_WORKSPACE
+    # shape errors come first, as in la_prefill
+    assert la.la_prefill_noalloc(vp(G), vp(2 * G), vp(3 * G), vp(4 * G), vp(5 * G), 8, 48, 64, None, 1, 8192,
+                                 la.LA_BF16, None) == la.LA_ERR_UNSUPPORTED
+
+
 def test_plans(lib):
     p = la.la_prefill_plan(8192, 1, 8, 128, 64, la.LA_BF16)
     assert p["units"] == p["num_segments"] * 8 * p["value_slices"] and p["seg_len"] % 64 == 0
