@@ -34,13 +34,13 @@ class la_prefill_opts(ctypes.Structure):
     _fields_ = [("seg_len", ctypes.c_int32), ("value_slices", ctypes.c_int32), ("force_scan", ctypes.c_int32),
                 ("variant", ctypes.c_int32), ("main_begin_event", ctypes.c_void_p),
                 ("main_end_event", ctypes.c_void_p), ("slots", ctypes.c_int32),
-                ("forward_states", ctypes.c_int32)]
+                ("forward_states", ctypes.c_int32), ("work_list", ctypes.c_int32)]
 
 
 class la_prefill_plan_info(ctypes.Structure):
     _fields_ = [("seg_len", ctypes.c_int32), ("value_slices", ctypes.c_int32), ("num_segments", ctypes.c_int32),
                 ("scan", ctypes.c_int32), ("units", ctypes.c_int64), ("workspace_bytes", ctypes.c_size_t),
-                ("variant", ctypes.c_int32), ("slots", ctypes.c_int32)]
+                ("variant", ctypes.c_int32), ("slots", ctypes.c_int32), ("packed", ctypes.c_int32)]
 
 
 _lib = None
@@ -146,9 +146,11 @@ def la_prefill_workspace_size(total_tokens, num_seqs, H, d, block, dtype) -> int
 
 
 def make_opts(seg_len: int = 0, value_slices: int = 0, force_scan: bool = False, begin_event=None,
-              end_event=None, variant: int = 0, slots: int = 0, forward_states: bool = False) -> la_prefill_opts:
+              end_event=None, variant: int = 0, slots: int = 0, forward_states: bool = False,
+              work_list: int = 0) -> la_prefill_opts:
     return la_prefill_opts(int(seg_len), int(value_slices), 1 if force_scan else 0, int(variant),
-                           _event_ptr(begin_event), _event_ptr(end_event), int(slots), 1 if forward_states else 0)
+                           _event_ptr(begin_event), _event_ptr(end_event), int(slots), 1 if forward_states else 0,
+                           int(work_list))
 
 
 def la_prefill_workspace_size_ex(total_tokens, num_seqs, H, d, block, dtype, opts=None) -> int:
@@ -164,7 +166,7 @@ def la_prefill_plan(total_tokens, num_seqs, H, d, block, dtype, opts=None) -> di
         raise LAError(st, "la_prefill_plan")
     return dict(seg_len=info.seg_len, value_slices=info.value_slices, num_segments=info.num_segments,
                 scan=info.scan, units=info.units, workspace_bytes=info.workspace_bytes, variant=info.variant,
-                slots=info.slots)
+                slots=info.slots, packed=info.packed)
 
 
 # ------------------------------------------------------------ torch layer
@@ -247,7 +249,8 @@ def _check_ws(ws, ref, where: str):
 
 def prefill(q, k, v, cu_seqlens, block: int = 64, want_state: bool = True, out=None, kv_state_out=None,
             workspace=None, seg_len: int = 0, value_slices: int = 0, force_scan: bool = False, stream=None,
-            begin_event=None, end_event=None, variant: int = 0, kv_state_in=None, slots: int = 0):
+            begin_event=None, end_event=None, variant: int = 0, kv_state_in=None, slots: int = 0,
+            work_list: int = 0):
     """Lightning-style causal linear attention over packed documents.
 
     q, k, v: [T, H, d] bf16/fp32 CUDA tensors; cu_seqlens: int32 [num_seqs + 1]
@@ -274,7 +277,8 @@ def prefill(q, k, v, cu_seqlens, block: int = 64, want_state: bool = True, out=N
     kv = kv_state_out
     if kv is None and want_state:
         kv = torch.empty((num_seqs, H, d, d), dtype=torch.float32, device=q.device)
-    opts = make_opts(seg_len, value_slices, force_scan, begin_event, end_event, variant, slots)
+    opts = make_opts(seg_len, value_slices, force_scan, begin_event, end_event, variant, slots,
+                     work_list=work_list)
     need = la_prefill_workspace_size_ex(T, num_seqs, H, d, block, dt, opts)
     ws = workspace
     if need and (ws is None or ws.numel() * ws.element_size() < need):
@@ -291,7 +295,7 @@ def prefill(q, k, v, cu_seqlens, block: int = 64, want_state: bool = True, out=N
 def backward(q, k, v, dout, cu_seqlens, block: int = 64, kv_state_in=None, dkv_state_out=None,
              want_dkv_in: bool = True, workspace=None, seg_len: int = 0, value_slices: int = 0,
              force_scan: bool = False, stream=None, variant: int = 0, out=None, slots: int = 0,
-             forward_workspace=None):
+             forward_workspace=None, work_list: int = 0):
     """Gradients of the prefill (la_prefill_backward).  dout is dL/do
     ([T, H, d], same dtype as q); dkv_state_out (fp32 [num_seqs, H, d, d] or
     None) is dL/dkv_state_out.  out = (dq, dk, dv, dkv_in) preallocated
@@ -323,7 +327,8 @@ def backward(q, k, v, dout, cu_seqlens, block: int = 64, kv_state_in=None, dkv_s
     else:
         dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
         dkv_in = torch.empty((num_seqs, H, d, d), dtype=torch.float32, device=q.device) if want_dkv_in else None
-    opts = make_opts(seg_len, value_slices, force_scan, None, None, variant, slots, forward_workspace is not None)
+    opts = make_opts(seg_len, value_slices, force_scan, None, None, variant, slots, forward_workspace is not None,
+                     work_list)
     need = la_prefill_workspace_size_ex(T, num_seqs, H, d, block, dt, opts)
     ws = forward_workspace if forward_workspace is not None else workspace
     if need and (ws is None or ws.numel() * ws.element_size() < need):

@@ -54,6 +54,11 @@ la_status enqueue_prefill(const Plan& plan, const void* q, const void* k, const 
     p.kv_out = kv_out;
     p.ws = plan.ws_bytes ? reinterpret_cast<float*>(static_cast<char*>(workspace) + plan.ws_states_off) : nullptr;
     p.flags = plan.ws_bytes ? reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + plan.ws_flags_off) : nullptr;
+    p.packed = plan.packed;
+    p.max_pieces = plan.max_pieces;
+    p.state_slots = plan.state_slots;
+    p.pieces = plan.packed ? reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + plan.ws_pieces_off) : nullptr;
+    p.slot_tab = plan.packed ? reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + plan.ws_slots_off) : nullptr;
     p.T = (int32_t)T;
     p.num_seqs = num_seqs;
     p.H = H;
@@ -102,6 +107,7 @@ la_status la_prefill_plan(int64_t total_tokens, int32_t num_seqs, int32_t H, int
         out->workspace_bytes = p.ws_bytes;
         out->variant = p.variant;
         out->slots = p.slots;
+        out->packed = p.packed;
     }
     return LA_OK;
 }
@@ -157,10 +163,9 @@ la_status la_prefill_backward(const void* q, const void* k, const void* v, const
     // (sums of k^T v): when the caller hands back the forward's workspace, they
     // are transposed in place instead of computed again.
     int reuse_fwd = 0;
-    if (opts && opts->forward_states && p1.variant == 2 && p1.nseg > 1) {
+    if (opts && opts->forward_states && p1.variant == 2 && p1.states() > 0) {
         float* ws = reinterpret_cast<float*>(static_cast<char*>(workspace) + p1.ws_states_off);
-        if (la::launch_ws_transpose(ws, (int64_t)(p1.nseg - 1) * H, d, p1.W, static_cast<hipStream_t>(stream)) !=
-            hipSuccess)
+        if (la::launch_ws_transpose(ws, p1.states() * H, d, p1.W, static_cast<hipStream_t>(stream)) != hipSuccess)
             return LA_ERR_HIP;
         reuse_fwd = 1;
     }
@@ -177,10 +182,10 @@ la_status la_prefill_backward(const void* q, const void* k, const void* v, const
     // (sums of q^T dO) over the same segments: on the transpose-read loop they
     // are transposed in place rather than computed again from Q and dO.
     int reuse = 0;
-    if (p2.variant == 2 && p2.nseg > 1 && p2.L == p3.L && p2.S == p3.S && p2.nseg == p3.nseg && p2.scan == p3.scan) {
+    if (p2.variant == 2 && p2.states() > 0 && p2.L == p3.L && p2.S == p3.S && p2.nseg == p3.nseg &&
+        p2.scan == p3.scan && p2.packed == p3.packed) {
         float* ws = reinterpret_cast<float*>(static_cast<char*>(workspace) + p3.ws_states_off);
-        if (la::launch_ws_transpose(ws, (int64_t)(p3.nseg - 1) * H, d, p3.W, static_cast<hipStream_t>(stream)) !=
-            hipSuccess)
+        if (la::launch_ws_transpose(ws, p3.states() * H, d, p3.W, static_cast<hipStream_t>(stream)) != hipSuccess)
             return LA_ERR_HIP;
         reuse = 1;
     }

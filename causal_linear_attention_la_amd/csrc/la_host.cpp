@@ -29,6 +29,12 @@ constexpr int kShortSegmentBlocks = 12;
 // The full-width transpose-read loop sums at most this many on segments of
 // more than kThreeSlotMinBlocks blocks.
 constexpr int kMaxLookbackWideLong = 8;
+// Document pieces are chosen when there are at least as many documents as
+// segments per head (the mean document fits one segment, so most documents
+// need no segment state), the units stay within a few per CU (each unit pays
+// a pipeline start), and no document can need more than kMaxLookback states.
+constexpr int kMaxPackedUnitsPerCU = 8;
+constexpr int kMaxPackedDocs = 4096;  // the planning kernel: 1024 lanes x 4 documents
 
 bool is_pow2_in(int32_t x, int32_t lo, int32_t hi) {
     if (x < lo || x > hi) return false;
@@ -148,8 +154,23 @@ la_status make_plan(int64_t T, int32_t num_seqs, int32_t H, int32_t d, int32_t b
     if (nseg > INT32_MAX) return LA_ERR_UNSUPPORTED;
     p.nseg = (int32_t)nseg;
     p.units = nseg * (int64_t)H * p.S;
+    const int32_t work_list = opts ? opts->work_list : 0;
+    if (work_list < 0 || work_list > 2) return LA_ERR_UNSUPPORTED;
+    {
+        const int64_t pieces = (int64_t)num_seqs + T / p.L;
+        const bool fits = T > 0 && num_seqs <= kMaxPackedDocs && nseg - 1 <= kMaxLookback &&
+                          pieces * H * p.S <= kMaxUnits && !(opts && opts->force_scan);
+        const bool want = num_seqs > 1 && num_seqs >= nseg && pieces * H * p.S <= (int64_t)kMaxPackedUnitsPerCU * kNumCUs;
+        if (work_list == 2 && !fits) return LA_ERR_UNSUPPORTED;
+        if (fits && (work_list == 2 || (work_list == 0 && want))) {
+            p.packed = 1;
+            p.max_pieces = (int32_t)pieces;
+            p.state_slots = (int32_t)(T / p.L);
+            p.units = pieces * H * p.S;
+        }
+    }
     if (p.units > kMaxUnits) return LA_ERR_UNSUPPORTED;
-    p.scan = p.nseg > 1 && ((opts && opts->force_scan) || needs_scan(p.L, p.W)) ? 1 : 0;
+    p.scan = !p.packed && p.nseg > 1 && ((opts && opts->force_scan) || needs_scan(p.L, p.W)) ? 1 : 0;
     // the scan kernel runs one lane per 4 state entries of a segment (H * d * d entries)
     if (p.scan && (int64_t)H * d * d / 4 > (((int64_t)1 << 32) - 1)) return LA_ERR_UNSUPPORTED;
     const int32_t slots = opts ? opts->slots : 0;
@@ -160,12 +181,22 @@ la_status make_plan(int64_t T, int32_t num_seqs, int32_t H, int32_t d, int32_t b
     else p.slots = three_ok && p.L / block >= kThreeSlotMinBlocks ? 3 : 2;
     if (p.variant != 2) p.slots = 2;  // (the generic loop has no slot choice)
 
-    if (p.nseg > 1) {
+    auto round256 = [](size_t x) { return (x + 255) & ~(size_t)255; };
+    if (p.packed) {
+        int64_t states;
+        if (!mul_ok(std::max<int64_t>(p.state_slots, 1), (int64_t)H * d * d, states) || !mul_ok(states, 4, states))
+            return LA_ERR_UNSUPPORTED;
+        p.ws_states_off = 0;
+        p.ws_flags_off = round256((size_t)states);
+        p.ws_pieces_off = p.ws_flags_off + 256;
+        p.ws_slots_off = p.ws_pieces_off + round256((size_t)p.max_pieces * 16);
+        p.ws_bytes = p.ws_slots_off + round256((size_t)std::max(p.state_slots, 1) * 8);
+    } else if (p.nseg > 1) {
         int64_t states;
         if (!mul_ok(nseg, (int64_t)H * d * d, states) || !mul_ok(states, 4, states)) return LA_ERR_UNSUPPORTED;
         p.ws_states_off = 0;
-        p.ws_flags_off = ((size_t)states + 255) & ~(size_t)255;
-        p.ws_bytes = p.ws_flags_off + (((size_t)nseg * 4 + 255) & ~(size_t)255);
+        p.ws_flags_off = round256((size_t)states);
+        p.ws_bytes = p.ws_flags_off + round256((size_t)nseg * 4);
     }
     (void)kNumCUs;
     *out = p;

@@ -17,10 +17,21 @@ struct Plan {
     int32_t scan = 0;   // run the prefix-scan kernel
     int32_t variant = 1;  // block loop: 1 generic, 2 transpose-read
     int32_t slots = 2;    // tile slots of the transpose-read loop
-    int64_t units = 0;  // nseg * H * S
+    int64_t units = 0;  // block-loop workgroups: nseg * H * S, or max_pieces * H * S (packed)
+    // Document pieces instead of fixed segments: every document is cut into
+    // pieces of at most L tokens, laid out longest first by a planning kernel
+    // (the host cannot see the document lengths), one workgroup per (piece,
+    // head, slice).  Only documents longer than L need segment states.
+    int32_t packed = 0;
+    int32_t max_pieces = 0;   // bound on the pieces: num_seqs + floor(T / L)
+    int32_t state_slots = 0;  // bound on the segment states of the pieces: floor(T / L)
     size_t ws_bytes = 0;
     size_t ws_states_off = 0;
     size_t ws_flags_off = 0;
+    size_t ws_pieces_off = 0;  // packed: piece table, 4 int32 per piece
+    size_t ws_slots_off = 0;   // packed: state-slot table, 2 int32 per slot
+    // segment states per head held in the workspace
+    int64_t states() const { return packed ? state_slots : nseg - 1; }
 };
 
 // Element size of a dtype (0 if unknown).

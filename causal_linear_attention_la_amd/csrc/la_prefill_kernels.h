@@ -47,8 +47,13 @@ struct PrefillParams {
     int32_t kv_in_t; // 1: kv_in holds transposed states ([value][key])
     int32_t slots;   // tile slots of the transpose-read block loop (2 or 3)
     int32_t skip_prefix;  // 1: ws already holds this pass's states; run only the block loop
-    int32_t pad_;
-    int64_t units;   // nseg * H * S
+    int32_t packed;       // 1: the work list is document pieces (pieces / slot_tab, written on the device)
+    int32_t max_pieces;   // packed: entries of pieces
+    int32_t state_slots;  // packed: entries of slot_tab
+    int32_t* pieces;      // packed: [max_pieces][4] first token, length (-1: unused), document,
+                          //         the document's first state slot (-1: none); longest first
+    int32_t* slot_tab;    // packed: [state_slots][2] first token, length (0: unused)
+    int64_t units;   // block-loop workgroups
     int64_t per_xcd; // ceil(units / 8)
 };
 
@@ -110,6 +115,160 @@ __device__ __forceinline__ bool unit_of(const PrefillParams& p, int& u, int& h, 
     u = (int)((x / p.S) % p.nseg);
     h = (int)(x / ((int64_t)p.S * p.nseg));
     return true;
+}
+
+// Packed work list: workgroup g takes entry g / (H S) of the piece table,
+// which the planning kernel wrote longest first, so that workgroups are
+// dispatched longest first; head (g / S) mod H, slice g mod S.  The entry is
+// the same for the whole workgroup (readfirstlane keeps it in scalar
+// registers).
+struct Piece {
+    int t0, len, doc, base;
+};
+__device__ __forceinline__ bool piece_of(const PrefillParams& p, Piece& pc, int& h, int& s) {
+    const int64_t g = blockIdx.x;
+    const int64_t r = g / ((int64_t)p.H * p.S);
+    if (r >= p.max_pieces) return false;
+    const int4 e = reinterpret_cast<const int4*>(p.pieces)[r];
+    pc.t0 = __builtin_amdgcn_readfirstlane(e.x);
+    pc.len = __builtin_amdgcn_readfirstlane(e.y);
+    pc.doc = __builtin_amdgcn_readfirstlane(e.z);
+    pc.base = __builtin_amdgcn_readfirstlane(e.w);
+    if (pc.len < 0) return false;
+    h = (int)((g / p.S) % p.H);
+    s = (int)(g % p.S);
+    return true;
+}
+// Packed work list, segment-state kernels: workgroup g takes state slot
+// g / (H S) (a piece that is not its document's last), head and slice as above.
+__device__ __forceinline__ bool slot_of(const PrefillParams& p, int& j, int& t0, int& len, int& h, int& s) {
+    const int64_t g = blockIdx.x;
+    const int64_t r = g / ((int64_t)p.H * p.S);
+    if (r >= p.state_slots) return false;
+    const int2 e = reinterpret_cast<const int2*>(p.slot_tab)[r];
+    t0 = __builtin_amdgcn_readfirstlane(e.x);
+    len = __builtin_amdgcn_readfirstlane(e.y);
+    if (len <= 0) return false;
+    j = (int)r;
+    h = (int)((g / p.S) % p.H);
+    s = (int)(g % p.S);
+    return true;
+}
+
+// ---------------------------------------------------------------------------
+// The packed work list, built on the device (the document boundaries live in
+// device memory).  Document n_d tokens long is cut into max(1, ceil(n_d / L))
+// pieces: the first ones exactly L tokens from the document start, the last
+// one the rest (length 0 for an empty document, whose unit only writes its
+// final state).  Every piece but the last of its document owns a state slot
+// (K^T V over the piece); a document's slots are consecutive, in document
+// order.  Pieces go to the table longest first -- a counting sort over
+// kPlanThreads length buckets, ties in any order -- so that the workgroups
+// the hardware dispatches first are the longest (longest-processing-time
+// list scheduling over the CUs).  Which workgroup runs a piece does not change
+// any result.  One workgroup; at most kPlanThreads * 4 documents.
+constexpr int kPlanThreads = 1024;
+constexpr int kPlanDocsPerThread = 4;  // so at most 4096 documents
+
+// Inclusive scan of one int per lane over the workgroup: a shuffle scan in
+// each wave, then the wave totals scanned by the first wave (two barriers).
+__device__ __forceinline__ int block_scan_incl(int x, int* wave_tot, int tid) {
+    constexpr int NW = kPlanThreads / 64;
+    const int lane = tid & 63, wave = tid >> 6;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(x, off, 64);
+        if (lane >= off) x += y;
+    }
+    if (lane == 63) wave_tot[wave] = x;
+    __syncthreads();
+    if (wave == 0) {
+        int t = lane < NW ? wave_tot[lane] : 0;
+#pragma unroll
+        for (int off = 1; off < NW; off <<= 1) {
+            const int y = __shfl_up(t, off, 64);
+            if (lane >= off) t += y;
+        }
+        if (lane < NW) wave_tot[lane] = t;
+    }
+    __syncthreads();
+    const int before = wave > 0 ? wave_tot[wave - 1] : 0;
+    const int total = wave_tot[NW - 1];
+    __syncthreads();  // wave_tot may be reused by the next scan
+    wave_tot[NW] = total;
+    return x + before;
+}
+
+template <int NT>
+__global__ __launch_bounds__(NT) void la_plan_pieces_kernel(PrefillParams p) {
+    static_assert(NT == kPlanThreads, "one lane per length bucket");
+    __shared__ int wave_tot[kPlanThreads / 64 + 1];
+    __shared__ int cnt[kPlanThreads];  // pieces per length bucket, then each bucket's next table position
+    const int tid = threadIdx.x;
+    const CuView cu = cu_view(p);
+    const int n = p.num_seqs, L = p.L;
+    // this lane's documents: a contiguous run, boundaries read once
+    const int per = (n + kPlanThreads - 1) / kPlanThreads;
+    const int d0 = min(n, tid * per), nd = min(n, d0 + per) - d0;
+    int start[kPlanDocsPerThread], len[kPlanDocsPerThread], np[kPlanDocsPerThread];
+    int nslots = 0, npieces = 0;
+#pragma unroll
+    for (int i = 0; i < kPlanDocsPerThread; ++i) {
+        start[i] = i < nd ? cu[d0 + i] : 0;
+        len[i] = i < nd ? cu[d0 + i + 1] - start[i] : 0;
+        np[i] = i < nd ? (len[i] == 0 ? 1 : (len[i] + L - 1) / L) : 0;
+        nslots += i < nd ? np[i] - 1 : 0;
+        npieces += np[i];
+    }
+    // bucket of a piece length in [0, L]: longer pieces, higher buckets
+    auto bucket = [&](int plen) { return (int)((int64_t)plen * (kPlanThreads - 1) / L); };
+    cnt[tid] = 0;
+    int slot = block_scan_incl(nslots, wave_tot, tid) - nslots;  // first state slot of this lane's documents
+    const int total_slots = wave_tot[kPlanThreads / 64];
+    const int total_pieces = (block_scan_incl(npieces, wave_tot, tid), wave_tot[kPlanThreads / 64]);
+#pragma unroll
+    for (int i = 0; i < kPlanDocsPerThread; ++i) {
+        if (i < nd) {
+            if (np[i] > 1) atomicAdd(&cnt[bucket(L)], np[i] - 1);
+            atomicAdd(&cnt[bucket(len[i] - (np[i] - 1) * L)], 1);
+        }
+    }
+    __syncthreads();
+    // descending order of buckets: lane t holds bucket kPlanThreads - 1 - t
+    const int mine = cnt[kPlanThreads - 1 - tid];
+    const int first = block_scan_incl(mine, wave_tot, tid) - mine;
+    cnt[kPlanThreads - 1 - tid] = first;  // first table position of that bucket
+    __syncthreads();
+    int4* tab = reinterpret_cast<int4*>(p.pieces);
+    int2* stab = reinterpret_cast<int2*>(p.slot_tab);
+#pragma unroll
+    for (int i = 0; i < kPlanDocsPerThread; ++i) {
+        if (i < nd) {
+            const int base = np[i] > 1 ? slot : -1;
+            for (int k = 0; k < np[i]; ++k) {
+                const int plen = k < np[i] - 1 ? L : len[i] - (np[i] - 1) * L;
+                const int pos = atomicAdd(&cnt[bucket(plen)], 1);
+                tab[pos] = make_int4(start[i] + k * L, plen, d0 + i, base);
+                if (k < np[i] - 1) stab[slot + k] = make_int2(start[i] + k * L, L);
+            }
+            slot += np[i] - 1;
+        }
+    }
+    for (int r = total_pieces + tid; r < p.max_pieces; r += kPlanThreads) tab[r] = make_int4(0, -1, 0, -1);
+    for (int r = total_slots + tid; r < p.state_slots; r += kPlanThreads) stab[r] = make_int2(0, 0);
+}
+
+// Final state of one empty document (the packed work list gives each its own
+// unit): the incoming state, or zero.
+template <int D, int W>
+__device__ __forceinline__ void one_empty_doc_state(const PrefillParams& p, int doc, int h, int s, int tid) {
+    const int64_t base = (((int64_t)phys_doc(p, doc) * p.H + h) * D) * D;
+    float* dst = p.kv_out + base;
+    const float* src = p.kv_in ? p.kv_in + base : nullptr;
+    for (int i = tid; i < D * W; i += kThreads) {
+        const int r = i / W, c = s * W + i % W;  // key row, value column
+        dst[(int64_t)r * D + c] = src ? (p.kv_in_t ? src[(int64_t)c * D + r] : src[(int64_t)r * D + c]) : 0.f;
+    }
 }
 
 // Walks the blocks of one segment [t0, t1): blocks start at the segment start
@@ -245,19 +404,27 @@ __global__ __launch_bounds__(kThreads, 2) void la_segment_state_kernel(PrefillPa
     TIn* Kt = smem;
     TIn* Vt = smem + al8(kt_elems(D, B));
 
-    int u, h, s;
-    if (!unit_of(p, u, h, s)) return;
-    if (u >= p.nseg - 1) return;  // nothing after the last segment
+    int u, h, s, b0, t_end;
     const int tid = threadIdx.x, lane = tid & 63, li = lane & 15, g = lane >> 4;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int t_beg = u * p.L, t_end = (u + 1) * p.L;  // t_end < T here
-    const CuView cu = cu_view(p);
-    const int de = doc_at(cu, p.num_seqs, t_end - 1);
-    const int dstart = cu[de];
-    const bool needs = cu[de + 1] > t_end;
-    const bool chain = dstart < t_beg;
-    if (h == 0 && s == 0 && tid == 0) p.flags[u] = (needs ? 1 : 0) | (chain ? 2 : 0);
-    if (!needs) return;
+    if (p.packed) {  // state slot u: a whole piece [b0, t_end) of one document
+        int len;
+        if (!slot_of(p, u, b0, len, h, s)) return;
+        t_end = b0 + len;
+    } else {
+        if (!unit_of(p, u, h, s)) return;
+        if (u >= p.nseg - 1) return;  // nothing after the last segment
+        const int t_beg = u * p.L;
+        t_end = (u + 1) * p.L;  // t_end < T here
+        const CuView cu = cu_view(p);
+        const int de = doc_at(cu, p.num_seqs, t_end - 1);
+        const int dstart = cu[de];
+        const bool needs = cu[de + 1] > t_end;
+        const bool chain = dstart < t_beg;
+        if (h == 0 && s == 0 && tid == 0) p.flags[u] = (needs ? 1 : 0) | (chain ? 2 : 0);
+        if (!needs) return;
+        b0 = max(t_beg, dstart);
+    }
 
     const TIn* kg = static_cast<const TIn*>(p.k);
     const TIn* vg = static_cast<const TIn*>(p.v);
@@ -268,7 +435,6 @@ __global__ __launch_bounds__(kThreads, 2) void la_segment_state_kernel(PrefillPa
 
     TileRegs<TIn, B, D> lk;
     TileRegs<TIn, B, W> lv;
-    int b0 = max(t_beg, dstart);
     int nb = min(B, t_end - b0);
     lk.load(kg + ((int64_t)phys_tok(p, b0) * p.H + h) * D, ld, nb, tid);
     lv.load(vg + ((int64_t)phys_tok(p, b0) * p.H + h) * D + s * W, ld, nb, tid);
@@ -380,11 +546,26 @@ __global__ __launch_bounds__(kThreads, 1) void la_prefill_main_kernel(PrefillPar
     TIn* Ps = smem + OPS;
     TIn* KVt = smem + OKV;
 
-    int u, h, s;
-    if (!unit_of(p, u, h, s)) return;
+    int u = 0, h, s, t0, t1;
+    int lb0 = 0, lb1 = 0;  // packed: state slots of the document's earlier pieces
     const int tid = threadIdx.x, lane = tid & 63, li = lane & 15, g = lane >> 4;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int t0 = u * p.L, t1 = min(p.T, t0 + p.L);
+    if (p.packed) {
+        Piece pc;
+        if (!piece_of(p, pc, h, s)) return;
+        if (pc.len == 0) {  // an empty document: only its final state
+            if (p.kv_out) one_empty_doc_state<D, W>(p, pc.doc, h, s, tid);
+            return;
+        }
+        t0 = pc.t0;
+        t1 = pc.t0 + pc.len;
+        lb0 = pc.base;
+        lb1 = pc.base + (t0 - cu_view(p)[pc.doc]) / p.L;
+    } else {
+        if (!unit_of(p, u, h, s)) return;
+        t0 = u * p.L;
+        t1 = min(p.T, t0 + p.L);
+    }
     const TIn* qg = static_cast<const TIn*>(p.q);
     const TIn* kg = static_cast<const TIn*>(p.k);
     const TIn* vg = static_cast<const TIn*>(p.v);
@@ -407,8 +588,9 @@ __global__ __launch_bounds__(kThreads, 1) void la_prefill_main_kernel(PrefillPar
 #pragma unroll
     for (int j = 0; j < KVPW; ++j) kv[j] = zero4();
     if (cur.nb > 0 && !cur.first_of_doc) {
-        const int u_first = p.scan ? u - 1 : cuv[cur.doc] / p.L;
-        for (int uu = u_first; uu < u; ++uu) {
+        const int u_first = p.packed ? lb0 : p.scan ? u - 1 : cuv[cur.doc] / p.L;
+        const int u_end = p.packed ? lb1 : u;
+        for (int uu = u_first; uu < u_end; ++uu) {
             const float* src = p.ws + (((int64_t)uu * p.H + h) * D) * D + s * W;
 #pragma unroll
             for (int j = 0; j < KVPW; ++j) {
@@ -577,8 +759,8 @@ __global__ __launch_bounds__(kThreads, 1) void la_prefill_main_kernel(PrefillPar
     }
 
     // Empty documents placed in this segment keep their incoming state (zero
-    // when none is given).
-    if (p.kv_out) empty_doc_states<D, W>(p, u, h, s, t0, t1, tid);
+    // when none is given); the packed work list gives them units of their own.
+    if (p.kv_out && !p.packed) empty_doc_states<D, W>(p, u, h, s, t0, t1, tid);
 }
 
 }  // namespace la

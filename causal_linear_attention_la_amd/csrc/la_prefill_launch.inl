@@ -27,11 +27,24 @@ hipError_t run_prefill(const PrefillParams& p, int variant, hipStream_t st, hipE
         return hipErrorInvalidValue;
     } else {
         const dim3 block(kThreads);
-        const dim3 grid((unsigned)(8 * p.per_xcd));
+        // segments: 8 * ceil(units / 8) workgroups (units numbered per XCD);
+        // pieces: one per table entry (head, slice), in table order
+        const dim3 grid((unsigned)(p.packed ? p.units : 8 * p.per_xcd));
         bool use_v2 = false;
         if constexpr (has_v2<T, D, B, W>()) use_v2 = (variant != 1);
         if (variant == 2 && !use_v2) return hipErrorInvalidValue;
-        if (p.nseg > 1 && !p.skip_prefix) {
+        if (p.packed) {
+            hipError_t e = launch_kernel(la_plan_pieces_kernel<kPlanThreads>, dim3(1), dim3(kPlanThreads), st, p);
+            if (e != hipSuccess) return e;
+            if (p.state_slots > 0 && !p.skip_prefix) {
+                void (*seg_kernel)(PrefillParams) = la_segment_state_kernel<T, D, B, W>;
+                if constexpr (has_v2<T, D, B, W>()) {
+                    if (use_v2) seg_kernel = v2::la_segment_state_v2<D, B, W>;
+                }
+                e = launch_kernel(seg_kernel, dim3((unsigned)((int64_t)p.state_slots * p.H * p.S)), block, st, p);
+                if (e != hipSuccess) return e;
+            }
+        } else if (p.nseg > 1 && !p.skip_prefix) {
             void (*seg_kernel)(PrefillParams) = la_segment_state_kernel<T, D, B, W>;
             if constexpr (has_v2<T, D, B, W>()) {
                 if (use_v2) seg_kernel = v2::la_segment_state_v2<D, B, W>;

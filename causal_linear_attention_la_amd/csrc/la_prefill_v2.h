@@ -301,22 +301,30 @@ __global__ __launch_bounds__(kThreads, 1) void la_segment_state_v2(PrefillParams
     __shared__ __align__(16) bf16_t Vb0[2 * B * W], Vb1[2 * B * W];
     auto kbuf = [&](auto slot) -> bf16_t* { if constexpr (decltype(slot)::value == 0) return Kb0; else return Kb1; };
     auto vbuf = [&](auto slot) -> bf16_t* { if constexpr (decltype(slot)::value == 0) return Vb0; else return Vb1; };
-    int u, h, s;
-    if (!unit_of(p, u, h, s)) return;
-    if (u >= p.nseg - 1) return;
+    int u, h, s, first, t_end;
     const int tid = threadIdx.x, lane = tid & 63, li = lane & 15, g = lane >> 4;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int t_beg = u * p.L, t_end = (u + 1) * p.L;
-    // values loaded from cu are the same in every lane: readfirstlane makes
-    // that visible to the compiler, which then keeps the buffer descriptors
-    // built from them in scalar registers (no per-lane waterfall loops)
-    const CuView cu = cu_view(p);
-    const int de = __builtin_amdgcn_readfirstlane(doc_at(cu, p.num_seqs, t_end - 1));
-    const int dstart = __builtin_amdgcn_readfirstlane(cu[de]);
-    const bool needs = __builtin_amdgcn_readfirstlane(cu[de + 1]) > t_end;
-    const bool chain = dstart < t_beg;
-    if (h == 0 && s == 0 && tid == 0) p.flags[u] = (needs ? 1 : 0) | (chain ? 2 : 0);
-    if (!needs) return;
+    if (p.packed) {  // state slot u: a whole piece [first, t_end) of one document
+        int len;
+        if (!slot_of(p, u, first, len, h, s)) return;
+        t_end = first + len;
+    } else {
+        if (!unit_of(p, u, h, s)) return;
+        if (u >= p.nseg - 1) return;
+        const int t_beg = u * p.L;
+        t_end = (u + 1) * p.L;
+        // values loaded from cu are the same in every lane: readfirstlane makes
+        // that visible to the compiler, which then keeps the buffer descriptors
+        // built from them in scalar registers (no per-lane waterfall loops)
+        const CuView cu = cu_view(p);
+        const int de = __builtin_amdgcn_readfirstlane(doc_at(cu, p.num_seqs, t_end - 1));
+        const int dstart = __builtin_amdgcn_readfirstlane(cu[de]);
+        const bool needs = __builtin_amdgcn_readfirstlane(cu[de + 1]) > t_end;
+        const bool chain = dstart < t_beg;
+        if (h == 0 && s == 0 && tid == 0) p.flags[u] = (needs ? 1 : 0) | (chain ? 2 : 0);
+        if (!needs) return;
+        first = max(t_beg, dstart);
+    }
 
     const bf16_t* kg = static_cast<const bf16_t*>(p.k);
     const bf16_t* vg = static_cast<const bf16_t*>(p.v);
@@ -333,7 +341,6 @@ __global__ __launch_bounds__(kThreads, 1) void la_segment_state_v2(PrefillParams
         for (int c = 0; c < G::NCW; ++c) kv[a][c] = zero4();
     Frag<bf16_t> vfr[G::NCW][B / 32];
 
-    const int first = max(t_beg, dstart);
     const int nblk = (t_end - first + B - 1) / B;
     // Pair jj = blocks 2jj and 2jj+1.  Blocks past the last one are issued
     // with an empty range: nothing is read, their rows arrive as zeros and
@@ -478,12 +485,27 @@ __global__ __launch_bounds__(kThreads, 1) void la_prefill_main_v2(PrefillParams 
         else return V2;
     };
 
-    int u, h, s;
-    if (!unit_of(p, u, h, s)) return;
+    int u = 0, h, s, t0, t1;
+    int lb0 = 0, lb1 = 0;  // packed: state slots of the document's earlier pieces
     const int tid = threadIdx.x, lane = tid & 63, li = lane & 15, g = lane >> 4;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: descriptors in SGPRs
+    if (p.packed) {
+        Piece pc;
+        if (!piece_of(p, pc, h, s)) return;
+        if (pc.len == 0) {  // an empty document: only its final state
+            if (p.kv_out) one_empty_doc_state<D, W>(p, pc.doc, h, s, tid);
+            return;
+        }
+        t0 = pc.t0;
+        t1 = pc.t0 + pc.len;
+        lb0 = pc.base;
+        lb1 = pc.base + (t0 - cu_view(p)[pc.doc]) / p.L;
+    } else {
+        if (!unit_of(p, u, h, s)) return;
+        t0 = u * p.L;
+        t1 = min(p.T, t0 + p.L);
+    }
     const int col0 = wave * G::CW;
-    const int t0 = u * p.L, t1 = min(p.T, t0 + p.L);
     const bf16_t* qg = static_cast<const bf16_t*>(p.q);
     const bf16_t* kg = static_cast<const bf16_t*>(p.k);
     const bf16_t* vg = static_cast<const bf16_t*>(p.v);
@@ -633,8 +655,9 @@ __global__ __launch_bounds__(kThreads, 1) void la_prefill_main_v2(PrefillParams 
         if constexpr (NS == 3) issue(c1, Slot<1>{});
     }
     if (c0.nb > 0 && !c0.first_of_doc) {
-        const int u_first = p.scan ? u - 1 : cuv[c0.doc] / p.L;
-        for (int uu = u_first; uu < u; ++uu)
+        const int u_first = p.packed ? lb0 : p.scan ? u - 1 : cuv[c0.doc] / p.L;
+        const int u_end = p.packed ? lb1 : u;
+        for (int uu = u_first; uu < u_end; ++uu)
             load_ws<D, B, W>(kv, p.ws + ws_offset<D, W>(p, uu, h, s, wave), lane);
     }
     // a caller-supplied state before the document's first token joins the prefix
@@ -779,7 +802,7 @@ __global__ __launch_bounds__(kThreads, 1) void la_prefill_main_v2(PrefillParams 
         if constexpr (LATE) finish_store(pb0, pnb);
     }
 
-    if (p.kv_out) empty_doc_states<D, W>(p, u, h, s, t0, t1, tid);
+    if (p.kv_out && !p.packed) empty_doc_states<D, W>(p, u, h, s, t0, t1, tid);
     vm_wait<0>();  // no tile load may still be writing into this workgroup's LDS when it ends
 }
 

@@ -170,6 +170,12 @@ typedef struct {
                                (transposed) instead of computing them again.  The
                                contents cannot be checked: with any other workspace
                                the gradients are wrong. */
+    int32_t work_list;      /* 0 = automatic, 1 = fixed segments of seg_len tokens,
+                               2 = document pieces: each document cut into pieces of
+                               at most seg_len tokens, ordered longest first on the
+                               device (LA_ERR_UNSUPPORTED where the plan cannot take
+                               them: more than 4096 documents, a document that could
+                               need more than 16 earlier pieces, or force_scan) */
 } la_prefill_opts;
 
 /* The decomposition a prefill call will use (for reports and tests). */
@@ -182,6 +188,8 @@ typedef struct {
     size_t workspace_bytes;
     int32_t variant;       /* the block-loop kernel that runs: 1 = generic, 2 = transpose-read */
     int32_t slots;         /* tile slots of the transpose-read loop (2 or 3) */
+    int32_t packed;        /* 1 if the work list is document pieces (units is then
+                              an upper bound: workgroups past the last piece exit) */
 } la_prefill_plan_info;
 
 la_status la_prefill_plan(int64_t total_tokens, int32_t num_seqs, int32_t H, int32_t d, int32_t block,

@@ -114,6 +114,28 @@ int main() {
     EXPECT(make_plan(10, 1, 8, 128, 64, 7, nullptr, &p) == LA_ERR_UNSUPPORTED);
     EXPECT(make_plan((int64_t)1 << 33, 1, 8, 128, 64, LA_BF16, nullptr, &p) == LA_ERR_INVALID_ARG);
 
+    // document pieces: chosen when the documents outnumber the segments per head and the units stay few
+    EXPECT(make_plan(131072, 20, 64, 128, 64, LA_BF16, nullptr, &p) == LA_OK && p.packed == 1 && p.max_pieces == 24 &&
+           p.state_slots == 4 && p.units == 24 * 64 && p.scan == 0 && p.ws_pieces_off >= p.ws_flags_off &&
+           p.ws_slots_off >= p.ws_pieces_off + 24 * 16 && p.ws_bytes >= p.ws_slots_off + 4 * 8 && p.states() == 4);
+    EXPECT(make_plan(131072, 300, 64, 128, 64, LA_BF16, nullptr, &p) == LA_OK && p.packed == 0);  // too many units
+    EXPECT(make_plan(8192, 2, 8, 128, 64, LA_BF16, nullptr, &p) == LA_OK && p.packed == 0);  // fewer documents than segments
+    la_prefill_opts o8{};
+    o8.work_list = 2;
+    EXPECT(make_plan(8192, 2, 8, 128, 64, LA_BF16, &o8, &p) == LA_OK && p.packed == 1 && p.max_pieces == 18);
+    o8.seg_len = 64;  // a document could need 127 earlier pieces
+    EXPECT(make_plan(8192, 2, 8, 128, 64, LA_BF16, &o8, &p) == LA_ERR_UNSUPPORTED);
+    o8.seg_len = 0;
+    o8.force_scan = 1;
+    EXPECT(make_plan(8192, 2, 8, 128, 64, LA_BF16, &o8, &p) == LA_ERR_UNSUPPORTED);
+    o8.force_scan = 0;
+    EXPECT(make_plan(100000, 5000, 8, 128, 64, LA_BF16, &o8, &p) == LA_ERR_UNSUPPORTED);  // over 4096 documents
+    EXPECT(make_plan(0, 3, 8, 128, 64, LA_BF16, &o8, &p) == LA_ERR_UNSUPPORTED);          // no tokens
+    o8.work_list = 1;
+    EXPECT(make_plan(131072, 20, 64, 128, 64, LA_BF16, &o8, &p) == LA_OK && p.packed == 0);
+    o8.work_list = 3;
+    EXPECT(make_plan(131072, 20, 64, 128, 64, LA_BF16, &o8, &p) == LA_ERR_UNSUPPORTED);
+
     // dispatch limits: a plan whose grid would not fit one dispatch is refused
     // before anything is enqueued (at most 2^32 - 1 work-items: 16,777,208 units)
     la_prefill_opts o6{};

@@ -146,6 +146,13 @@ def test_plans(lib):
     assert p["workspace_bytes"] >= 128 * 8 * 128 * 128 * 4
     with pytest.raises(la.LAError):
         la.la_prefill_plan(8192, 1, 8, 128, 64, la.LA_BF16, la.make_opts(seg_len=100))
+    # document pieces on the packed 131072-token workload (20 documents, 64 heads): at most 24 pieces
+    p = la.la_prefill_plan(131072, 20, 64, 128, 64, la.LA_BF16)
+    assert p["packed"] == 1 and p["units"] == 24 * 64 and p["scan"] == 0
+    assert la.la_prefill_plan(8192, 1, 8, 128, 64, la.LA_BF16)["packed"] == 0
+    assert la.la_prefill_plan(131072, 20, 64, 128, 64, la.LA_BF16, la.make_opts(work_list=1))["packed"] == 0
+    with pytest.raises(la.LAError):  # a document could need more than 16 earlier pieces
+        la.la_prefill_plan(8192, 2, 8, 128, 64, la.LA_BF16, la.make_opts(seg_len=64, work_list=2))
     # tile slots of the transpose-read loop: three on long segments, two on short ones
     assert la.la_prefill_plan(8192, 1, 8, 128, 64, la.LA_BF16)["slots"] == 2
     assert la.la_prefill_plan(1048576, 1, 8, 128, 64, la.LA_BF16)["slots"] == 3

@@ -5,7 +5,7 @@ Cases: ragged packed documents (empty ones included) with and without
 incoming states and final-state gradients, on both block loops (bf16 d = 128
 and 64 on the gfx950 loop, bf16 block 32 and fp32 on the generic loop), with
 segment splitting and the scan path (which in the reverse passes run over
-documents read back to front), the 8192-token x 8-head workload in full, and
+documents read back to front), the document-piece work list, the 8192-token x 8-head workload in full, and
 the 1M-token workload on the GPU in full, checked exactly on windows, and the
 131072-token packed workload in full, two heads compared against the oracle."""
 import numpy as np
@@ -61,7 +61,8 @@ def check(q, k, v, dout, cu, kv_in, dkv_out, got, fp32, what):
 
 CASES = [(d, block, dtype, opts, with_states)
          for d, block, dtype in ((128, 64, "bf16"), (64, 64, "bf16"), (128, 32, "bf16"), (32, 64, "fp32"))
-         for opts in (dict(), dict(seg_len=2 * block, value_slices=2), dict(seg_len=block, force_scan=True))
+         for opts in (dict(), dict(seg_len=2 * block, value_slices=2), dict(seg_len=block, force_scan=True),
+                      dict(seg_len=max(128, 2 * block), work_list=2))
          for with_states in (False, True)]
 
 

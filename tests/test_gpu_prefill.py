@@ -2,7 +2,8 @@
 
 Cases: the tiny fp32 and 8k-token bf16 workloads in full; every (d, block,
 dtype) the library supports on ragged lengths; forced segment splitting and
-value slicing (the LASP+-style prefix path); two and three tile slots in the
+value slicing (the LASP+-style prefix path); the document-piece work list
+(documents cut into pieces, longest first, on every block loop); two and three tile slots in the
 block loop; packed documents with empty and ragged ones; exact-integer
 inputs that must match bit for bit; run-to-run
 determinism; guard bands around the outputs; zero tokens; and the
@@ -102,6 +103,50 @@ def test_segment_splitting(opts):
     check_against_oracle(q, k, v, cu, o, kv, False, f"split {opts}")
 
 
+PIECE_CASES = [(d, block, dtype, opts)
+               for d, block, dtype in ((128, 64, "bf16"), (64, 64, "bf16"), (32, 64, "bf16"), (128, 128, "bf16"),
+                                       (128, 32, "fp32"), (16, 32, "fp32"))
+               for opts in (dict(seg_len=128), dict(seg_len=256, value_slices=2), dict(seg_len=640))]
+
+
+@pytest.mark.parametrize("d,block,dtype,opts", PIECE_CASES,
+                         ids=[f"d{c[0]}-b{c[1]}-{c[2]}-{c[3]}" for c in PIECE_CASES])
+def test_document_pieces(d, block, dtype, opts):
+    """The document-piece work list: documents longer than the piece length
+    are cut into several pieces (their earlier pieces' states summed in the
+    prologue), empty documents get units of their own, the planning kernel
+    orders the pieces longest first.  Against the oracle, with incoming states."""
+    import torch
+
+    if opts["seg_len"] % block:
+        pytest.skip("piece length not a multiple of the block")
+    lens = [0, 1500, 3, 0, 0, 200, 1, 777, 129, 0]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    T, H = int(cu[-1]), 3
+    dt = la.LA_BF16 if dtype == "bf16" else la.LA_FP32
+    S = opts.get("value_slices", 0)
+    try:
+        plan = la.la_prefill_plan(T, len(lens), H, d, block, dt, la.make_opts(work_list=2, **opts))
+    except la.LAError:
+        pytest.skip("this slicing does not fit LDS for this shape")
+    assert plan["packed"] == 1
+    log(f"  pieces d={d} b={block} {dtype} {opts} plan={plan}")
+    q, k, v = rand_inputs(171 + d + block, T, H, d, dtype)
+    kv_in = np.ascontiguousarray(la_inputs.normal(172, 7, (len(lens), H, d, d), "fp32", float(np.sqrt(2000)) / d),
+                                 dtype=np.float32)
+    o, kv = la.prefill(to_dev(q), to_dev(k), to_dev(v), to_dev(cu), block=block, work_list=2,
+                       kv_state_in=to_dev(kv_in), **opts)
+    torch.cuda.synchronize()
+    o_ref, kv_ref = oracle.recurrent(q, k, v, cu, kv_in=kv_in)
+    ErrAcc().add(to_host(o), o_ref).check(dtype == "fp32", f"pieces {opts} o")
+    ErrAcc().add(to_host(kv), kv_ref).check(dtype == "fp32", f"pieces {opts} kv_state")
+    # the empty documents' final states are their incoming states, exactly
+    kvh = to_host(kv)
+    for i, n in enumerate(lens):
+        if n == 0:
+            assert np.array_equal(kvh[i], kv_in[i])
+
+
 SLOT_CASES = [(S, opts) for S in (1, 2)
               for opts in (dict(), dict(seg_len=64), dict(seg_len=192, force_scan=True), dict(seg_len=1024))]
 
@@ -164,7 +209,7 @@ def test_varlen_tails_and_empty_docs():
     T, H, d = int(cu[-1]), 4, 64
     q, k, v = rand_inputs(41, T, H, d, "bf16")
     for block in (32, 64, 128):
-        for opts in (dict(), dict(seg_len=block, value_slices=2)):
+        for opts in (dict(), dict(seg_len=block, value_slices=2), dict(seg_len=max(64, block), work_list=2)):
             log(f"  tails block={block} {opts}")
             o, kv = run_gpu(q, k, v, cu, block, **opts)
             o_ref, kv_ref = check_against_oracle(q, k, v, cu, o, kv, False, f"tails b{block} {opts}")
@@ -198,7 +243,8 @@ def test_exact_integer_inputs_bitexact(dtype, d):
     assert np.all(o_ref == np.round(o_ref)) and np.max(np.abs(o_ref)) < 2 ** 24
     blocks = (32, 64, 128) if not (dtype == "fp32" and d >= 64) else (32, 64)
     for block in blocks:
-        for opts in (dict(), dict(seg_len=block, value_slices=1), dict(seg_len=block, value_slices=d // 32 or 1)):
+        for opts in (dict(), dict(seg_len=block, value_slices=1), dict(seg_len=block, value_slices=d // 32 or 1),
+                     dict(seg_len=block, work_list=2)):
             try:
                 la.la_prefill_plan(T, 2, H, d, block, la.LA_BF16 if dtype == "bf16" else la.LA_FP32,
                                    la.make_opts(**opts))
@@ -278,7 +324,7 @@ def test_guard_bands():
     kv_buf = torch.full((n_kv + 2 * guard,), -7.25, dtype=torch.float32, device="cuda")
     o_view = o_buf[guard:guard + n_o].view(T, H, d)
     kv_view = kv_buf[guard:guard + n_kv].view(2, H, d, d)
-    for opts in (dict(), dict(seg_len=64, value_slices=4)):
+    for opts in (dict(), dict(seg_len=64, value_slices=4), dict(seg_len=64, work_list=2)):
         la.prefill(to_dev(q), to_dev(k), to_dev(v), to_dev(cu), block=block, out=o_view, kv_state_out=kv_view,
                    **opts)
         torch.cuda.synchronize()

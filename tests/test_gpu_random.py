@@ -1,6 +1,6 @@
 """Randomised parity: seeded draws of shapes, packed-document layouts and
 every decomposition knob (segment length, value slices, scan, tile slots,
-block loop, incoming states), each prefill checked against the fp64 oracle,
+block loop, work list, incoming states), each prefill checked against the fp64 oracle,
 and a share of them through the backward as well.  Draws whose options the
 planner rejects must be rejected (LA_ERR_UNSUPPORTED) before anything runs."""
 import numpy as np
@@ -49,8 +49,11 @@ def draw(seed):
         opts["variant"] = int(r.choice([1, 2]))
     if r.random() < 0.3:
         opts["slots"] = int(r.choice([2, 3]))
-    return dict(d=d, dtype=dtype, block=block, H=H, lens=lens, opts=opts, kv_in=r.random() < 0.4,
-                backward=r.random() < 0.35)
+    kv_in = r.random() < 0.4
+    backward = r.random() < 0.35
+    if r.random() < 0.35:  # drawn last: the earlier knobs of every seed stay as they were
+        opts["work_list"] = int(r.choice([1, 2]))
+    return dict(d=d, dtype=dtype, block=block, H=H, lens=lens, opts=opts, kv_in=kv_in, backward=backward)
 
 
 SEEDS = list(range(1000, 2000))
