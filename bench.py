@@ -148,7 +148,7 @@ def cpu_model() -> str:
 def stream_ceilings(la, torch, hip) -> dict:
     """Bandwidth (GB/s of bytes read + written) of the contiguous streams in
     la_bench_stream over 1 GiB per source: the best of 256 and 512
-    workgroups, plain and non-temporal accesses."""
+    workgroups, plain and non-temporal accesses, two rounds of 20 passes."""
     lib = la.load()
     bufs = [torch.empty(GIB, dtype=torch.uint8, device="cuda").fill_(i + 1) for i in range(4)]
     P = lambda t: ctypes.c_void_p(t.data_ptr())
@@ -156,15 +156,17 @@ def stream_ceilings(la, torch, hip) -> dict:
     out = {}
     for mode, name, nbytes in ((0, "copy_1r1w", 2 * GIB), (1, "stream_3r1w", 4 * GIB)):
         best, how = 0.0, None
-        for wgs in (256, 512):
-            for nt in (0, 1):
-                def fn():
-                    st = lib.la_bench_stream(mode, P(bufs[0]), P(bufs[1]), P(bufs[2]), P(bufs[3]), GIB, wgs, nt, sp)
-                    if st != 0:
-                        raise RuntimeError(f"la_bench_stream: {st}")
-                gbs = nbytes / gpu_time(torch, hip, fn, 10) / 1e9
-                if gbs > best:
-                    best, how = gbs, f"{wgs} workgroups, {'non-temporal' if nt else 'plain'} accesses"
+        for _ in range(2):
+            for wgs in (256, 512):
+                for nt in (0, 1):
+                    def fn():
+                        st = lib.la_bench_stream(mode, P(bufs[0]), P(bufs[1]), P(bufs[2]), P(bufs[3]), GIB, wgs, nt,
+                                                 sp)
+                        if st != 0:
+                            raise RuntimeError(f"la_bench_stream: {st}")
+                    gbs = nbytes / gpu_time(torch, hip, fn, 20) / 1e9
+                    if gbs > best:
+                        best, how = gbs, f"{wgs} workgroups, {'non-temporal' if nt else 'plain'} accesses"
         out[name] = {"GBs": best, "config": how}
     del bufs
     torch.cuda.empty_cache()
@@ -303,6 +305,37 @@ def bench_prefill(name, args, la, torch, hip, steps: int, warmup: int, graph: bo
     if keep_sets:
         w["dev_sets"] = sets
     return rec, w
+
+
+def bench_block(la, torch, hip, w, block: int, steps: int) -> dict:
+    """The same workload and device inputs with another block size: whole-call
+    time and the block-loop kernel's duration (events), plan included."""
+    T, H, d = w["T"], w["H"], w["d"]
+    num_seqs = len(w["cu"]) - 1
+    dt = la.LA_BF16 if w["dtype"] == "bf16" else la.LA_FP32
+    plan = la.la_prefill_plan(T, num_seqs, H, d, block, dt)
+    q, k, v, o = w["dev_sets"][0]
+    cu = torch.from_numpy(w["cu"]).cuda()
+    kv = torch.empty((num_seqs, H, d, d), dtype=torch.float32, device="cuda")
+    ws = torch.empty(max(plan["workspace_bytes"], 256), dtype=torch.uint8, device="cuda")
+    call = lambda: la.prefill(q, k, v, cu, block=block, out=o, kv_state_out=kv, workspace=ws)
+    s = gpu_time(torch, hip, call, steps)
+    evs = [(hip.event(), hip.event()) for _ in range(steps)]
+    for a, b in evs:
+        la.prefill(q, k, v, cu, block=block, out=o, kv_state_out=kv, workspace=ws, begin_event=a, end_event=b)
+    torch.cuda.synchronize()
+    kms = float(np.mean([hip.elapsed_ms(a, b) for a, b in evs]))
+    for a, b in evs:
+        hip.destroy(a)
+        hip.destroy(b)
+    algo = T * H * 8 * d
+    roof_th = HBM_PEAK_GBS * 1e9 / (8 * d)
+    return {"workload": w["name"], "block": block, "value": T * H / s, "unit": "token·heads/s",
+            "gpu_ms_per_step": s * 1e3, "steps": steps,
+            "plan": {k2: plan[k2] for k2 in ("seg_len", "value_slices", "num_segments", "scan", "variant", "units")},
+            "block_loop": {"kernel": MAIN_KERNEL[plan["variant"]], "kernel_ms": kms,
+                           "frac": algo / (kms / 1e3) / 1e9 / HBM_PEAK_GBS},
+            "whole_call_frac": T * H / s / roof_th}
 
 
 def with_ceiling(roof: dict, ceiling_gbs: float):
@@ -571,7 +604,7 @@ def main():
     small = args.workload in ("prefill_8k", "tiny_fp32")
     steps = args.small_steps if small and args.steps == 20 else args.steps
     head, w = bench_prefill(args.workload, args, la, torch, hip, steps, args.warmup,
-                            graph=small and not args.no_graph, keep_sets=not args.no_backward)
+                            graph=small and not args.no_graph, keep_sets=True)
     with_ceiling(head["roofline"], prefill_ceiling)
     head["whole_call"]["frac_of_measured_ceiling"] = head["whole_call"]["achieved"] / prefill_ceiling
     rec = {
@@ -593,6 +626,8 @@ def main():
         "gpu_ms_per_step": head["gpu_ms_per_step"],
         "ceilings": ceil,
     }
+    if args.workload == "long_1m" and not args.no_extra and not args.block:
+        rec["long_1m_block128"] = bench_block(la, torch, hip, w, 128, 3)
     if not args.no_backward:
         rec["backward"] = bench_backward(args, la, torch, hip, w, w.pop("dev_sets"), max(2, args.steps // 4))
         with_ceiling(rec["backward"]["roofline"], prefill_ceiling)
@@ -600,6 +635,7 @@ def main():
         rec["cpu_baseline"] = cpu_baseline(w)
     else:
         rec["cpu_baseline"] = None
+    w.pop("dev_sets", None)
     del w
     torch.cuda.empty_cache()
 

@@ -56,6 +56,11 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 
 // Word 3 of a raw buffer resource on gfx9: 32-bit data format, offsets in bytes.
 constexpr int kRsrcWord3 = 0x00020000;
+// Cache-policy bit of a buffer access on gfx950: non-temporal (streaming).
+// The segment-state kernel, a pure read stream, is faster with it (long
+// inputs: 0.74 -> 0.67 ms for 4.2 GB); the block loop is slower with it on
+// its loads or its stores, so it keeps the default policy.
+constexpr int kNonTemporal = 2;
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kRsrcWord3);
@@ -171,13 +176,15 @@ struct DmaTile {
     // nb - 1 - r (the descriptor then starts at the block's lowest physical
     // row): rows past nb wrap to huge offsets and read as zeros either way.
     // last_row_off = (nb - 1) * row_bytes.
+    // CPOL: the loads' cache policy (0 default, kNonTemporal).
+    template <int CPOL = 0>
     __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t rsrc, bf16_t* tile, bool rev = false,
                                           uint32_t last_row_off = 0) const {
 #pragma unroll
         for (int i = 0; i < NI; ++i) {
             const uint32_t off = rev ? last_row_off + coff2[i] - voff[i] : voff[i];
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)(tile + (row0 + RPI * i) * COLS), 16, off, 0,
-                                                     0, 0);
+                                                     0, CPOL);
         }
     }
 };
@@ -354,8 +361,10 @@ __global__ __launch_bounds__(kThreads, 1) void la_segment_state_v2(PrefillParams
             const int nb = __builtin_amdgcn_readfirstlane(max(0, min(B, t_end - b0)));
             const int64_t e0 = ((int64_t)phys_block(p, min(b0, t_end), nb) * p.H + h) * D;
             const uint32_t last = (uint32_t)(nb - 1) * row_bytes;
-            dk.issue(make_rsrc(kg + e0, (uint32_t)nb * row_bytes), kbuf(slot) + half * B * D, p.rev, last);
-            dv.issue(make_rsrc(vg + e0 + s * W, (uint32_t)nb * row_bytes), vbuf(slot) + half * B * W, p.rev, last);
+            dk.template issue<kNonTemporal>(make_rsrc(kg + e0, (uint32_t)nb * row_bytes), kbuf(slot) + half * B * D,
+                                            p.rev, last);
+            dv.template issue<kNonTemporal>(make_rsrc(vg + e0 + s * W, (uint32_t)nb * row_bytes),
+                                            vbuf(slot) + half * B * W, p.rev, last);
         }
     };
     const int npairs = (nblk + 1) / 2;
