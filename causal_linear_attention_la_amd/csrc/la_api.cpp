@@ -39,11 +39,38 @@ la_status scratch_on_current_device(void** out) {
     return LA_OK;
 }
 
+// Key of a forward call's segment states: its inputs' addresses, shapes and
+// plan (FNV-1a over them; never 0).  A backward handed the workspace with
+// forward_states reuses the states only if the key stamped there is its own.
+uint64_t states_key(const Plan& plan, const void* q, const void* k, const void* v, const int32_t* cu, int32_t H,
+                    int32_t d, int32_t block, int32_t num_seqs, int64_t T, la_dtype dtype) {
+    const uint64_t parts[] = {(uint64_t)(uintptr_t)q, (uint64_t)(uintptr_t)k, (uint64_t)(uintptr_t)v,
+                              (uint64_t)(uintptr_t)cu, (uint64_t)H, (uint64_t)d, (uint64_t)block,
+                              (uint64_t)num_seqs, (uint64_t)T, (uint64_t)dtype, (uint64_t)plan.L, (uint64_t)plan.S,
+                              (uint64_t)plan.nseg, (uint64_t)plan.scan, (uint64_t)plan.packed,
+                              (uint64_t)plan.variant, (uint64_t)plan.slots};
+    uint64_t h = 1469598103934665603ull;
+    for (uint64_t x : parts)
+        for (int b = 0; b < 8; ++b) {
+            h ^= (x >> (8 * b)) & 0xff;
+            h *= 1099511628211ull;
+        }
+    return h ? h : 1;
+}
+
+char* ws_at(void* workspace, size_t off) { return static_cast<char*>(workspace) + off; }
+
 // Fills the launch parameters of one validated prefill pass and enqueues it.
+// Every pass with a workspace has its block loop write the workspace's stamp:
+// a forward call (stamp) its key when it leaves segment states there, anything
+// else 0, so a stamp is only ever found next to the states it names.
+// reuse: a backward's decision word (the state and scan kernels then do
+// nothing when it reads 1).
 la_status enqueue_prefill(const Plan& plan, const void* q, const void* k, const void* v, void* o, const int32_t* cu,
                           int32_t H, int32_t d, int32_t block, const float* kv_in, int kv_in_t, float* kv_out,
                           int rev, int32_t num_seqs, int64_t T, la_dtype dtype, void* workspace, void* stream,
-                          hipEvent_t e0, hipEvent_t e1, int skip_prefix = 0) {
+                          hipEvent_t e0, hipEvent_t e1, int skip_prefix = 0, bool stamp = false,
+                          const int32_t* reuse = nullptr) {
     la::PrefillParams p{};
     p.q = q;
     p.k = k;
@@ -70,6 +97,11 @@ la_status enqueue_prefill(const Plan& plan, const void* q, const void* k, const 
     p.kv_in_t = kv_in_t;
     p.slots = plan.slots;
     p.skip_prefix = skip_prefix;
+    if (plan.ws_bytes > 0) {
+        p.marker = reinterpret_cast<uint64_t*>(ws_at(workspace, plan.ws_marker_off));
+        p.key = stamp && plan.states() > 0 ? states_key(plan, q, k, v, cu, H, d, block, num_seqs, T, dtype) : 0;
+    }
+    p.reuse = reuse;
     p.units = plan.units;
     p.per_xcd = (plan.units + 7) / 8;
     hipStream_t s = static_cast<hipStream_t>(stream);
@@ -135,7 +167,7 @@ la_status la_prefill_resume(const void* q, const void* k, const void* v, void* o
     hipEvent_t e0 = opts ? static_cast<hipEvent_t>(opts->main_begin_event) : nullptr;
     hipEvent_t e1 = opts ? static_cast<hipEvent_t>(opts->main_end_event) : nullptr;
     return enqueue_prefill(plan, q, k, v, o, cu_seqlens, H, d, block, kv_state_in, 0, kv_state_out, 0, num_seqs,
-                           total_tokens, dtype, workspace, stream, e0, e1);
+                           total_tokens, dtype, workspace, stream, e0, e1, 0, true);
 }
 
 la_status la_prefill_backward(const void* q, const void* k, const void* v, const void* dout,
@@ -162,15 +194,24 @@ la_status la_prefill_backward(const void* q, const void* k, const void* v, const
     // segment states (sums of v^T k) are the transposes of the forward's
     // (sums of k^T v): when the caller hands back the forward's workspace, they
     // are transposed in place instead of computed again.
-    int reuse_fwd = 0;
+    // The workspace holds the forward's states only if the key the forward
+    // stamped there is this call's: a claim kernel compares the two, writes
+    // its decision to the workspace and clears the stamp (the passes below
+    // overwrite the states).  The transpose runs only on a match; otherwise
+    // the state and scan kernels compute the states as usual.
+    const int32_t* decision = nullptr;
     if (opts && opts->forward_states && p1.variant == 2 && p1.states() > 0) {
-        float* ws = reinterpret_cast<float*>(static_cast<char*>(workspace) + p1.ws_states_off);
-        if (la::launch_ws_transpose(ws, p1.states() * H, d, p1.W, static_cast<hipStream_t>(stream)) != hipSuccess)
-            return LA_ERR_HIP;
-        reuse_fwd = 1;
+        hipStream_t hs = static_cast<hipStream_t>(stream);
+        uint64_t* marker = reinterpret_cast<uint64_t*>(ws_at(workspace, p1.ws_marker_off));
+        int32_t* dec = reinterpret_cast<int32_t*>(ws_at(workspace, p1.ws_marker_off + 64));
+        const uint64_t key = states_key(p1, q, k, v, cu_seqlens, H, d, block, num_seqs, total_tokens, dtype);
+        if (la::launch_ws_claim(marker, key, dec, hs) != hipSuccess) return LA_ERR_HIP;
+        float* ws = reinterpret_cast<float*>(ws_at(workspace, p1.ws_states_off));
+        if (la::launch_ws_transpose(ws, p1.states() * H, d, p1.W, dec, hs) != hipSuccess) return LA_ERR_HIP;
+        decision = dec;
     }
     st = enqueue_prefill(p1, dout, v, k, dq, cu_seqlens, H, d, block, kv_state_in, 1, nullptr, 0, num_seqs,
-                         total_tokens, dtype, workspace, stream, nullptr, nullptr, reuse_fwd);
+                         total_tokens, dtype, workspace, stream, nullptr, nullptr, 0, false, decision);
     if (st != LA_OK) return st;
     // dV (and dKV_in, the reverse state after each document's first token):
     // reverse pass with query K, key Q, value dO, from dKV_out
@@ -185,7 +226,8 @@ la_status la_prefill_backward(const void* q, const void* k, const void* v, const
     if (p2.variant == 2 && p2.states() > 0 && p2.L == p3.L && p2.S == p3.S && p2.nseg == p3.nseg &&
         p2.scan == p3.scan && p2.packed == p3.packed) {
         float* ws = reinterpret_cast<float*>(static_cast<char*>(workspace) + p3.ws_states_off);
-        if (la::launch_ws_transpose(ws, p3.states() * H, d, p3.W, static_cast<hipStream_t>(stream)) != hipSuccess)
+        if (la::launch_ws_transpose(ws, p3.states() * H, d, p3.W, nullptr, static_cast<hipStream_t>(stream)) !=
+            hipSuccess)
             return LA_ERR_HIP;
         reuse = 1;
     }
@@ -225,7 +267,7 @@ la_status la_prefill_noalloc(const void* q, const void* k, const void* v, void* 
                               (int)dtype, ws, plan.ws_bytes, nullptr, &plan);
     if (st != LA_OK) return st;
     return enqueue_prefill(plan, q, k, v, o, cu_seqlens, H, d, block, nullptr, 0, kv_state_out, 0, num_seqs,
-                           total_tokens, dtype, ws, stream, nullptr, nullptr);
+                           total_tokens, dtype, ws, stream, nullptr, nullptr, 0, true);
 }
 
 la_status la_decode(const void* q, const void* k, const void* v, float* kv_state_inout, void* o, int32_t num_seqs,

@@ -181,23 +181,28 @@ la_status make_plan(int64_t T, int32_t num_seqs, int32_t H, int32_t d, int32_t b
     else p.slots = three_ok && p.L / block >= kThreeSlotMinBlocks ? 3 : 2;
     if (p.variant != 2) p.slots = 2;  // (the generic loop has no slot choice)
 
+    // Workspace: a 256-byte header at offset 0 whatever the plan (the stamp of
+    // the forward call whose segment states it holds, and a backward's reuse
+    // decision), then the states and the plan's tables.
     auto round256 = [](size_t x) { return (x + 255) & ~(size_t)255; };
+    constexpr size_t kHeader = 256;
     if (p.packed) {
         int64_t states;
         if (!mul_ok(std::max<int64_t>(p.state_slots, 1), (int64_t)H * d * d, states) || !mul_ok(states, 4, states))
             return LA_ERR_UNSUPPORTED;
-        p.ws_states_off = 0;
-        p.ws_flags_off = round256((size_t)states);
+        p.ws_states_off = kHeader;
+        p.ws_flags_off = kHeader + round256((size_t)states);
         p.ws_pieces_off = p.ws_flags_off + 256;
         p.ws_slots_off = p.ws_pieces_off + round256((size_t)p.max_pieces * 16);
         p.ws_bytes = p.ws_slots_off + round256((size_t)std::max(p.state_slots, 1) * 8);
     } else if (p.nseg > 1) {
         int64_t states;
         if (!mul_ok(nseg, (int64_t)H * d * d, states) || !mul_ok(states, 4, states)) return LA_ERR_UNSUPPORTED;
-        p.ws_states_off = 0;
-        p.ws_flags_off = round256((size_t)states);
+        p.ws_states_off = kHeader;
+        p.ws_flags_off = kHeader + round256((size_t)states);
         p.ws_bytes = p.ws_flags_off + round256((size_t)nseg * 4);
     }
+    p.ws_marker_off = 0;
     (void)kNumCUs;
     *out = p;
     return LA_OK;

@@ -30,6 +30,8 @@ struct Plan {
     size_t ws_flags_off = 0;
     size_t ws_pieces_off = 0;  // packed: piece table, 4 int32 per piece
     size_t ws_slots_off = 0;   // packed: state-slot table, 2 int32 per slot
+    size_t ws_marker_off = 0;  // header at offset 0 of every workspace: 64-bit key of the forward call
+                               // whose states the workspace holds (+0), a backward's reuse decision (+64)
     // segment states per head held in the workspace
     int64_t states() const { return packed ? state_slots : nseg - 1; }
 };

@@ -13,17 +13,21 @@ template __global__ void v2::la_prefill_main_v2<64, 64, 64, 2>(PrefillParams);
 template __global__ void v2::la_segment_state_v2<128, 64, 128>(PrefillParams);
 template __global__ void v2::la_segment_state_v2<128, 64, 64>(PrefillParams);
 template __global__ void v2::la_segment_state_v2<64, 64, 64>(PrefillParams);
-template __global__ void v2::la_ws_transpose_v2<128, 128>(float*, int64_t);
-template __global__ void v2::la_ws_transpose_v2<128, 64>(float*, int64_t);
-template __global__ void v2::la_ws_transpose_v2<64, 64>(float*, int64_t);
+template __global__ void v2::la_ws_transpose_v2<128, 128>(float*, int64_t, const int32_t*);
+template __global__ void v2::la_ws_transpose_v2<128, 64>(float*, int64_t, const int32_t*);
+template __global__ void v2::la_ws_transpose_v2<64, 64>(float*, int64_t, const int32_t*);
 
-hipError_t launch_ws_transpose(float* ws, int64_t states, int D, int W, hipStream_t st) {
+hipError_t launch_ws_transpose(float* ws, int64_t states, int D, int W, const int32_t* reuse, hipStream_t st) {
     if (states <= 0) return hipSuccess;
     const dim3 grid((unsigned)states), block(kThreads);
-    if (D == 128 && W == 128) return launch_kernel(v2::la_ws_transpose_v2<128, 128>, grid, block, st, ws, states);
-    if (D == 128 && W == 64) return launch_kernel(v2::la_ws_transpose_v2<128, 64>, grid, block, st, ws, states);
-    if (D == 64 && W == 64) return launch_kernel(v2::la_ws_transpose_v2<64, 64>, grid, block, st, ws, states);
+    if (D == 128 && W == 128) return launch_kernel(v2::la_ws_transpose_v2<128, 128>, grid, block, st, ws, states, reuse);
+    if (D == 128 && W == 64) return launch_kernel(v2::la_ws_transpose_v2<128, 64>, grid, block, st, ws, states, reuse);
+    if (D == 64 && W == 64) return launch_kernel(v2::la_ws_transpose_v2<64, 64>, grid, block, st, ws, states, reuse);
     return hipErrorInvalidValue;
+}
+
+hipError_t launch_ws_claim(uint64_t* marker, uint64_t key, int32_t* decision, hipStream_t st) {
+    return launch_kernel(la_ws_claim_kernel<64>, dim3(1), dim3(64), st, marker, key, decision);
 }
 
 hipError_t launch_prefill_bf16(const PrefillParams& p, int D, int B, int W, int variant, hipStream_t st, hipEvent_t e0,

@@ -53,9 +53,35 @@ struct PrefillParams {
     int32_t* pieces;      // packed: [max_pieces][4] first token, length (-1: unused), document,
                           //         the document's first state slot (-1: none); longest first
     int32_t* slot_tab;    // packed: [state_slots][2] first token, length (0: unused)
+    uint64_t* marker;     // forward calls with segment states: the block loop stores `key` here
+                          // (the states are complete once it runs), for a backward to reuse
+    const int32_t* reuse; // backward dq pass: 1 here means the workspace already holds this
+                          // pass's segment states (so the state and scan kernels do nothing)
+    uint64_t key;
     int64_t units;   // block-loop workgroups
     int64_t per_xcd; // ceil(units / 8)
 };
+
+// The workspace's segment states are complete before the block loop runs
+// (stream order), so any of its workgroups may stamp the call's key.
+__device__ __forceinline__ void stamp_key(const PrefillParams& p) {
+    if (p.marker && blockIdx.x == 0 && threadIdx.x == 0) *p.marker = p.key;
+}
+// In a backward pass that reuses the forward's states, the state and scan
+// kernels have nothing to do.
+__device__ __forceinline__ bool states_reused(const PrefillParams& p) { return p.reuse && *p.reuse != 0; }
+
+// One lane: whether the workspace holds the states of the forward call whose
+// key is `key` (decision = 1) or anything else (0); either way the key is
+// consumed, so a second backward on the same workspace computes its states.
+template <int NT>
+__global__ __launch_bounds__(NT) void la_ws_claim_kernel(uint64_t* marker, uint64_t key, int32_t* decision) {
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+        const uint64_t m = *marker;
+        *decision = m == key ? 1 : 0;
+        *marker = 0;
+    }
+}
 
 // Document boundaries as the kernels see them.  In reverse mode the packed
 // sequence is read back to front: logical token t is physical token T-1-t,
@@ -404,6 +430,7 @@ __global__ __launch_bounds__(kThreads, 2) void la_segment_state_kernel(PrefillPa
     TIn* Kt = smem;
     TIn* Vt = smem + al8(kt_elems(D, B));
 
+    if (states_reused(p)) return;
     int u, h, s, b0, t_end;
     const int tid = threadIdx.x, lane = tid & 63, li = lane & 15, g = lane >> 4;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -474,7 +501,8 @@ __global__ __launch_bounds__(kThreads, 2) void la_segment_state_kernel(PrefillPa
 // spread the scan over every CU (each CU's stream of requests is the limit).
 template <int CH, int NT>
 __global__ __launch_bounds__(NT) void la_segment_scan_kernel(float* __restrict__ ws, const int32_t* __restrict__ flags,
-                                                             int nseg, int64_t entries) {
+                                                             int nseg, int64_t entries, const int32_t* reuse) {
+    if (reuse && *reuse) return;  // the workspace already holds the (transposed) prefixes
     const int64_t idx = ((int64_t)blockIdx.x * NT + threadIdx.x) * 4;
     if (idx >= entries) return;
     f32x4_t carry = zero4();
@@ -546,6 +574,7 @@ __global__ __launch_bounds__(kThreads, 1) void la_prefill_main_kernel(PrefillPar
     TIn* Ps = smem + OPS;
     TIn* KVt = smem + OKV;
 
+    stamp_key(p);
     int u = 0, h, s, t0, t1;
     int lb0 = 0, lb1 = 0;  // packed: state slots of the document's earlier pieces
     const int tid = threadIdx.x, lane = tid & 63, li = lane & 15, g = lane >> 4;

@@ -56,7 +56,7 @@ hipError_t run_prefill(const PrefillParams& p, int variant, hipStream_t st, hipE
                 const int64_t threads = entries / 4;
                 constexpr int NT = 128;
                 e = launch_kernel(la_segment_scan_kernel<32, NT>, dim3((unsigned)((threads + NT - 1) / NT)), dim3(NT),
-                                  st, p.ws, (const int32_t*)p.flags, (int)p.nseg, entries);
+                                  st, p.ws, (const int32_t*)p.flags, (int)p.nseg, entries, p.reuse);
                 if (e != hipSuccess) return e;
             }
         }

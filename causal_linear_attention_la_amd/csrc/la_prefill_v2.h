@@ -308,6 +308,7 @@ __global__ __launch_bounds__(kThreads, 1) void la_segment_state_v2(PrefillParams
     __shared__ __align__(16) bf16_t Vb0[2 * B * W], Vb1[2 * B * W];
     auto kbuf = [&](auto slot) -> bf16_t* { if constexpr (decltype(slot)::value == 0) return Kb0; else return Kb1; };
     auto vbuf = [&](auto slot) -> bf16_t* { if constexpr (decltype(slot)::value == 0) return Vb0; else return Vb1; };
+    if (states_reused(p)) return;
     int u, h, s, first, t_end;
     const int tid = threadIdx.x, lane = tid & 63, li = lane & 15, g = lane >> 4;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -408,12 +409,14 @@ __global__ __launch_bounds__(kThreads, 1) void la_segment_state_v2(PrefillParams
 // state goes through LDS as a plain matrix (rows padded by 4 floats, so the
 // 16-byte column reads are conflict free).
 template <int D, int W>
-__global__ __launch_bounds__(kThreads) void la_ws_transpose_v2(float* __restrict__ ws, int64_t states) {
+__global__ __launch_bounds__(kThreads) void la_ws_transpose_v2(float* __restrict__ ws, int64_t states,
+                                                                const int32_t* reuse) {
     constexpr int NCW = W / 64;  // 16-column tiles per block-loop wave (W / 4 columns)
     constexpr int PITCH = D + 4;
     constexpr int PER_WAVE = D * W / 16, PER_SLICE = D * W / 4;  // 16-byte entries
     __shared__ __align__(16) float M[D * PITCH];
     if ((int64_t)blockIdx.x >= states) return;
+    if (reuse && !*reuse) return;  // the states were not the forward's: they are computed instead
     f32x4_t* base = reinterpret_cast<f32x4_t*>(ws + (int64_t)blockIdx.x * D * D);
     // entry e holds rows i0 .. i0 + 3 of column j (store_ws's order)
     auto place = [](int e, int& i0, int& j) {
@@ -494,6 +497,7 @@ __global__ __launch_bounds__(kThreads, 1) void la_prefill_main_v2(PrefillParams 
         else return V2;
     };
 
+    stamp_key(p);
     int u = 0, h, s, t0, t1;
     int lb0 = 0, lb1 = 0;  // packed: state slots of the document's earlier pieces
     const int tid = threadIdx.x, lane = tid & 63, li = lane & 15, g = lane >> 4;

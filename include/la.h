@@ -163,13 +163,20 @@ typedef struct {
                                (3 on segments of 16 blocks or more), 2, or 3 (loads
                                two blocks ahead; d = 128 only) */
     int32_t forward_states; /* la_prefill_backward only (the forward entry points
-                               ignore it): 1 = `workspace` still holds what the
-                               forward call (la_prefill / _ex / _resume) on the same
-                               q, k, v, cu_seqlens, shapes, dtype and opts left in it;
-                               the dq pass then takes those segment states
-                               (transposed) instead of computing them again.  The
-                               contents cannot be checked: with any other workspace
-                               the gradients are wrong. */
+                               ignore it): 1 = `workspace` may hold the segment states
+                               of a forward call (la_prefill / _ex / _resume) on the
+                               same q, k, v, cu_seqlens, shapes, dtype and plan; the dq
+                               pass then takes them (transposed) instead of computing
+                               them again.  Every forward call stamps its workspace
+                               with a key of those pointers, shapes and plan (or clears
+                               the stamp when it leaves no states); the backward
+                               compares the stamp with its own key on the device and
+                               reuses the states only on a match, else computes them;
+                               either way it consumes the stamp, so a second backward
+                               on the same workspace computes its own, and a backward
+                               without forward_states clears it.  What cannot be
+                               checked: the contents of q, k, v and cu_seqlens must be
+                               those the stamping forward read. */
     int32_t work_list;      /* 0 = automatic, 1 = fixed segments of seg_len tokens,
                                2 = document pieces: each document cut into pieces of
                                at most seg_len tokens, ordered longest first on the

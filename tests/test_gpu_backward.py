@@ -133,6 +133,69 @@ def test_backward_with_forward_states(opts, with_states):
         assert np.array_equal(a, to_host(b)), "only the dq pass may change"
 
 
+def test_forward_states_are_claimed_once():
+    """forward_states reuses the forward's segment states only while the
+    workspace holds the stamp of a forward call on these very inputs, shapes
+    and plan, and the first backward consumes it.  Checked three ways:
+    (1) the states region is zeroed after the forward (the stamp stays): the
+    first backward takes the zeros, as reuse must (the contents are the
+    caller's precondition), and its dq is far from the truth, while a second
+    backward on the same workspace computes its states and equals the fresh
+    backward bit for bit; (2) a forward on other tensors of the same shape
+    leaves a stamp that does not match; (3) a forward with another plan
+    neither, even right after one with this plan; (4) a backward without
+    forward_states clears the stamp of the states it overwrites."""
+    import torch
+
+    lens = [300, 0, 1, 700, 64, 0, 129, 1500]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    T, H, d = int(cu[-1]), 3, 128
+    q, k, v, dout = inputs(161, T, H, d, "bf16")
+    qd, kd, vd, dod, cud = to_dev(q), to_dev(k), to_dev(v), to_dev(dout), to_dev(cu)
+    opts = dict(seg_len=192)
+    plan = la.la_prefill_plan(T, len(lens), H, d, 64, la.LA_BF16, la.make_opts(**opts))
+    other = la.la_prefill_plan(T, len(lens), H, d, 64, la.LA_BF16, la.make_opts(seg_len=128))
+    assert plan["num_segments"] > 2 and plan["packed"] == 0
+    ws = torch.empty(max(plan["workspace_bytes"], other["workspace_bytes"]), dtype=torch.uint8, device="cuda")
+    header = 256  # the workspace's stamp; the segment states follow it
+    states = ws[header:header + (plan["num_segments"] - 1) * H * d * d * 4]
+    fresh = [to_host(x) for x in la.backward(qd, kd, vd, dod, cud, block=64, **opts)[:3]]
+    ref = oracle.backward(q, k, v, dout, cu)
+
+    def bwd():
+        got = la.backward(qd, kd, vd, dod, cud, block=64, forward_workspace=ws, **opts)
+        torch.cuda.synchronize()
+        return [to_host(x) for x in got[:3]]
+
+    # (1) reuse happens once, and only once
+    la.prefill(qd, kd, vd, cud, block=64, workspace=ws, **opts)
+    states.zero_()
+    first = bwd()
+    e = ErrAcc().add(first[0], ref[0])
+    log(f"    dq from zeroed reused states: rel_l2={e.rel_l2:.3e}")
+    assert e.rel_l2 > 0.1, "the first backward must take the stamped workspace's states"
+    second = bwd()
+    for g, f in zip(second, fresh):
+        assert np.array_equal(g, f), "a consumed stamp must not be reused"
+    # (2) a forward on other tensors of the same shape
+    q2, k2, v2 = (to_dev(x) for x in inputs(162, T, H, d, "bf16")[:3])
+    la.prefill(q2, k2, v2, cud, block=64, workspace=ws, **opts)
+    for g, f in zip(bwd(), fresh):
+        assert np.array_equal(g, f), "states of other inputs must not be reused"
+    # (3) a forward with another plan on the same workspace, after one with this plan
+    la.prefill(qd, kd, vd, cud, block=64, workspace=ws, **opts)
+    la.prefill(qd, kd, vd, cud, block=64, workspace=ws, seg_len=128)
+    for g, f in zip(bwd(), fresh):
+        assert np.array_equal(g, f), "states of another plan must not be reused"
+    # (4) a backward without forward_states overwrites the states: its stamp goes too
+    la.prefill(qd, kd, vd, cud, block=64, workspace=ws, **opts)
+    la.backward(qd, kd, vd, dod, cud, block=64, workspace=ws, **opts)
+    for g, f in zip(bwd(), fresh):
+        assert np.array_equal(g, f), "states overwritten by a backward must not be reused"
+    for name, g, r in zip(("dq", "dk", "dv"), second, ref[:3]):
+        ErrAcc().add(g, r).check(False, f"second backward {name}")
+
+
 def test_backward_prefill_8k_workload():
     w = la_inputs.prefill_inputs("prefill_8k")
     T, H, d = w["T"], w["H"], w["d"]
