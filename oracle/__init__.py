@@ -11,6 +11,10 @@ Forms (see ``la_oracle.c`` for the page citations):
 * :func:`quadratic` -- form (a), masked left product (tiny inputs only).
 * :func:`decode_step` -- one length-1 step: state update, then read.
 
+Each takes ``decay`` (per-head factors in [0, 1]; per pair for decode_step)
+for the decayed variant S_t = lambda S_{t-1} + k_t^T v_t (a reading of the
+decay the pages name but never define; ``None`` = no decay).
+
 Inputs are numpy arrays: bf16 as uint16 bit patterns, or float32 / float64.
 """
 from __future__ import annotations
@@ -31,7 +35,7 @@ def build(force: bool = False, out: str | None = None, extra_flags=()) -> str:
     target = out or _SO
     if force or out or not os.path.exists(target) or os.path.getmtime(target) < os.path.getmtime(_SRC):
         tmp = target + ".tmp"
-        subprocess.check_call(["gcc", "-O2", "-fPIC", "-shared", "-pthread", *extra_flags, _SRC, "-o", tmp])
+        subprocess.check_call(["gcc", "-O2", "-fPIC", "-shared", "-pthread", *extra_flags, _SRC, "-o", tmp, "-lm"])
         os.replace(tmp, target)
     return target
 
@@ -42,6 +46,10 @@ def _bind(lib):
     lib.ora_quadratic.argtypes = [vp, vp, vp, ctypes.c_int, vp, i32, i32, i32, vp, vp, vp]
     lib.ora_decode_step.argtypes = [vp, vp, vp, ctypes.c_int, i64, i32, vp, vp, ctypes.c_int]
     lib.ora_backward.argtypes = [vp, vp, vp, vp, ctypes.c_int, vp, i32, i32, i32, vp, vp, vp, vp, vp, vp, ctypes.c_int]
+    lib.ora_recurrent_decay.argtypes = [vp, vp, vp, ctypes.c_int, vp, i32, i32, i32, i32, i32, vp, vp, vp, vp,
+                                        ctypes.c_int]
+    lib.ora_quadratic_decay.argtypes = [vp, vp, vp, ctypes.c_int, vp, i32, i32, i32, vp, vp, vp, vp]
+    lib.ora_decode_step_decay.argtypes = [vp, vp, vp, ctypes.c_int, i64, i32, vp, vp, vp, ctypes.c_int]
     lib.ora_last_threads.restype = ctypes.c_int
     return lib
 
@@ -80,8 +88,16 @@ def _c(a, dt=None):
     return np.ascontiguousarray(a if dt is None else np.asarray(a, dtype=dt))
 
 
+def _decay(decay, n):
+    if decay is None:
+        return None
+    a = np.ascontiguousarray(np.asarray(decay, dtype=np.float64).reshape(-1))
+    assert a.size == n, (a.size, n)
+    return a
+
+
 def recurrent(q, k, v, cu_seqlens, kv_in=None, want_o=True, want_state=True, heads=None,
-              nthreads: int = 0, lib=None):
+              nthreads: int = 0, lib=None, decay=None):
     """Form (b).  q, k, v: [T, H, d].  Returns (o [T, nh, d] fp64 or None,
     kv_out [num_seqs, H, d, d] fp64 or None); with ``heads=(h0, h1)`` only that
     head range is computed (kv_out rows of other heads stay zero)."""
@@ -96,14 +112,19 @@ def recurrent(q, k, v, cu_seqlens, kv_in=None, want_o=True, want_state=True, hea
     kvi = None if kv_in is None else _c(kv_in, np.float64)
     o = np.empty((T, h1 - h0, d), dtype=np.float64) if want_o else None
     kvo = np.zeros((D, H, d, d), dtype=np.float64) if want_state else None
-    rc = lib.ora_recurrent(_p(q), _p(k), _p(v), _dtype_code(q), _p(cu), D, H, d, h0, h1, _p(kvi), _p(o), _p(kvo),
-                           nthreads)
+    lam = _decay(decay, H)
+    if lam is None:
+        rc = lib.ora_recurrent(_p(q), _p(k), _p(v), _dtype_code(q), _p(cu), D, H, d, h0, h1, _p(kvi), _p(o), _p(kvo),
+                               nthreads)
+    else:
+        rc = lib.ora_recurrent_decay(_p(q), _p(k), _p(v), _dtype_code(q), _p(cu), D, H, d, h0, h1, _p(lam), _p(kvi),
+                                     _p(o), _p(kvo), nthreads)
     if rc != 0:
         raise ValueError("ora_recurrent rejected its arguments")
     return o, kvo
 
 
-def quadratic(q, k, v, cu_seqlens, kv_in=None, lib=None):
+def quadratic(q, k, v, cu_seqlens, kv_in=None, lib=None, decay=None):
     """Form (a), every head, single thread.  Returns (o, kv_out) in fp64."""
     lib = lib or load()
     q, k, v = _c(q), _c(k), _c(v)
@@ -113,7 +134,12 @@ def quadratic(q, k, v, cu_seqlens, kv_in=None, lib=None):
     kvi = None if kv_in is None else _c(kv_in, np.float64)
     o = np.empty((T, H, d), dtype=np.float64)
     kvo = np.empty((D, H, d, d), dtype=np.float64)
-    rc = lib.ora_quadratic(_p(q), _p(k), _p(v), _dtype_code(q), _p(cu), D, H, d, _p(kvi), _p(o), _p(kvo))
+    lam = _decay(decay, H)
+    if lam is None:
+        rc = lib.ora_quadratic(_p(q), _p(k), _p(v), _dtype_code(q), _p(cu), D, H, d, _p(kvi), _p(o), _p(kvo))
+    else:
+        rc = lib.ora_quadratic_decay(_p(q), _p(k), _p(v), _dtype_code(q), _p(cu), D, H, d, _p(lam), _p(kvi), _p(o),
+                                     _p(kvo))
     if rc != 0:
         raise ValueError("ora_quadratic rejected its arguments")
     return o, kvo
@@ -140,15 +166,20 @@ def backward(q, k, v, dout, cu_seqlens, kv_in=None, dkv_out=None, want_dkv_in=Tr
     return dq, dk, dv, dki
 
 
-def decode_step(q, k, v, S, nthreads: int = 0, lib=None):
-    """S (fp64 [P, d, d]) is updated in place; returns o fp64 [P, d]."""
+def decode_step(q, k, v, S, nthreads: int = 0, lib=None, decay=None):
+    """S (fp64 [P, d, d]) is updated in place; returns o fp64 [P, d].
+    decay: per-pair factors [P] (the decayed variant) or None."""
     lib = lib or load()
     q, k, v = _c(q), _c(k), _c(v)
     d = q.shape[-1]
     P = q.size // d
     assert S.dtype == np.float64 and S.flags.c_contiguous and S.size == P * d * d
     o = np.empty((P, d), dtype=np.float64)
-    rc = lib.ora_decode_step(_p(q), _p(k), _p(v), _dtype_code(q), P, d, _p(S), _p(o), nthreads)
+    lam = _decay(decay, P)
+    if lam is None:
+        rc = lib.ora_decode_step(_p(q), _p(k), _p(v), _dtype_code(q), P, d, _p(S), _p(o), nthreads)
+    else:
+        rc = lib.ora_decode_step_decay(_p(q), _p(k), _p(v), _dtype_code(q), P, d, _p(lam), _p(S), _p(o), nthreads)
     if rc != 0:
         raise ValueError("ora_decode_step rejected its arguments")
     return o

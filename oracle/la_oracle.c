@@ -17,15 +17,23 @@
  *    (分离预填充和解码执行): decode is a length-1 step that updates the
  *    prefix key-value cache.
  * Readings where the pages are silent (their formulas were images): no scale,
- * feature map, normaliser or decay; the causal mask includes the current
- * token (s <= t); the state is KV = sum k^T v (key x value) and o = q . KV;
- * a decode step updates the state before reading it.
+ * feature map or normaliser; the causal mask includes the current token
+ * (s <= t); the state is KV = sum k^T v (key x value) and o = q . KV; a decode
+ * step updates the state before reading it.
+ *  - "MiniMax-01技术报告解读", §3.3 item 1 (批处理内核融合) names a decay-value
+ *    computation (衰减值计算) among the fused prefill steps but never defines
+ *    it.  The *_decay functions take the plainest reading that keeps the
+ *    recurrence: a per-head factor lambda in [0, 1] by which the state fades
+ *    before each token's update, S_t = lambda S_{t-1} + k_t^T v_t, so that
+ *    o_t = sum_{s <= t} lambda^(t - s) (q_t . k_s) v_s; lambda = 1 is the
+ *    undecayed operation.  The functions without _decay have no decay.
  *
  * Build: gcc -O2 -fPIC -shared -pthread la_oracle.c -o _laoracle.so
  * (no -ffast-math: the sums must stay in program order).
  */
 #include "la_oracle.h"
 
+#include <math.h>
 #include <pthread.h>
 #include <stdatomic.h>
 #include <stdlib.h>
@@ -121,6 +129,7 @@ typedef struct {
     int32_t num_seqs, H, d, h0, h1, nslice;
     const double* kv_in;
     double *o, *kv_out;
+    const double* decay; /* per-head factor, or NULL (no decay) */
 } rec_ctx;
 
 static void rec_task(void* cv, int64_t task) {
@@ -149,6 +158,10 @@ static void rec_task(void* cv, int64_t task) {
             qq[i] = widen(c->q, c->dtype, row + i);
         }
         for (int32_t jj = 0; jj < nj; ++jj) vv[jj] = widen(c->v, c->dtype, row + j0 + jj);
+        /* decayed variant: S <- lambda_h S first (the state before token t fades by one step) */
+        if (c->decay)
+            for (int32_t i = 0; i < d; ++i)
+                for (int32_t jj = 0; jj < nj; ++jj) S[i * ORA_COLS + jj] *= c->decay[h];
         /* S <- S + k_t^T v_t  (rank-1 update) */
         for (int32_t i = 0; i < d; ++i)
             for (int32_t jj = 0; jj < nj; ++jj) S[i * ORA_COLS + jj] += kk[i] * vv[jj];
@@ -175,7 +188,27 @@ int ora_recurrent(const void* q, const void* k, const void* v, int dtype, const 
                   double* o, double* kv_out, int nthreads) {
     if (!q || !k || !v || dtype < 0 || dtype > 2 || H < 1 || d < 1 || h0 < 0 || h1 > H || h0 >= h1) return -1;
     if (check_cu(cu_seqlens, num_seqs)) return -1;
-    rec_ctx c = {q, k, v, dtype, cu_seqlens, num_seqs, H, d, h0, h1, (d + ORA_COLS - 1) / ORA_COLS, kv_in, o, kv_out};
+    rec_ctx c = {q, k, v, dtype, cu_seqlens, num_seqs, H, d, h0, h1, (d + ORA_COLS - 1) / ORA_COLS, kv_in, o, kv_out,
+                 NULL};
+    int64_t ntasks = (int64_t)num_seqs * (h1 - h0) * c.nslice;
+    run_tasks(ntasks, nthreads, rec_task, &c);
+    return 0;
+}
+
+static int check_decay(const double* decay, int32_t H) {
+    if (!decay) return -1;
+    for (int32_t h = 0; h < H; ++h)
+        if (!(decay[h] >= 0.0 && decay[h] <= 1.0)) return -1;
+    return 0;
+}
+
+int ora_recurrent_decay(const void* q, const void* k, const void* v, int dtype, const int32_t* cu_seqlens,
+                        int32_t num_seqs, int32_t H, int32_t d, int32_t h0, int32_t h1, const double* decay,
+                        const double* kv_in, double* o, double* kv_out, int nthreads) {
+    if (!q || !k || !v || dtype < 0 || dtype > 2 || H < 1 || d < 1 || h0 < 0 || h1 > H || h0 >= h1) return -1;
+    if (check_cu(cu_seqlens, num_seqs) || check_decay(decay, H)) return -1;
+    rec_ctx c = {q, k, v, dtype, cu_seqlens, num_seqs, H, d, h0, h1, (d + ORA_COLS - 1) / ORA_COLS, kv_in, o, kv_out,
+                 decay};
     int64_t ntasks = (int64_t)num_seqs * (h1 - h0) * c.nslice;
     run_tasks(ntasks, nthreads, rec_task, &c);
     return 0;
@@ -218,6 +251,59 @@ int ora_quadratic(const void* q, const void* k, const void* v, int dtype, const 
                         double acc = kv_in ? kv_in[sbase + (size_t)i * d + j] : 0.0;
                         for (int64_t cc = 0; cc < n; ++cc)
                             acc += widen(k, dtype, ((s0 + cc) * H + h) * d + i) * widen(v, dtype, ((s0 + cc) * H + h) * d + j);
+                        kv_out[sbase + (size_t)i * d + j] = acc;
+                    }
+            free(A);
+        }
+    }
+    return 0;
+}
+
+/* The decayed variant in form (a): the score of key c for query r carries
+ * lambda^(r - c), the incoming state reaches token r faded r + 1 times, and
+ * the final state holds every token faded to the document's end:
+ *   A[r][c] = lambda^(r - c) q_r . k_c  (c <= r)
+ *   o_r     = sum_c A[r][c] v_c + lambda^(r + 1) q_r . kv_in
+ *   kv_out  = lambda^n kv_in + sum_c lambda^(n - 1 - c) k_c^T v_c
+ * (pow(lambda, m) with pow(0, 0) = 1). */
+int ora_quadratic_decay(const void* q, const void* k, const void* v, int dtype, const int32_t* cu_seqlens,
+                        int32_t num_seqs, int32_t H, int32_t d, const double* decay, const double* kv_in, double* o,
+                        double* kv_out) {
+    if (!q || !k || !v || dtype < 0 || dtype > 2 || H < 1 || d < 1) return -1;
+    if (check_cu(cu_seqlens, num_seqs) || check_decay(decay, H)) return -1;
+    g_last_threads = 1;
+    for (int32_t doc = 0; doc < num_seqs; ++doc) {
+        const int64_t s0 = cu_seqlens[doc], n = cu_seqlens[doc + 1] - s0;
+        for (int32_t h = 0; h < H; ++h) {
+            const double lam = decay[h];
+            const size_t sbase = ((size_t)doc * H + h) * (size_t)d * d;
+            double* A = (double*)calloc((size_t)(n > 0 ? n * n : 1), sizeof(double));
+            for (int64_t r = 0; r < n; ++r)
+                for (int64_t cc = 0; cc <= r; ++cc) {
+                    double dot = 0.0;
+                    for (int32_t i = 0; i < d; ++i)
+                        dot += widen(q, dtype, ((s0 + r) * H + h) * d + i) * widen(k, dtype, ((s0 + cc) * H + h) * d + i);
+                    A[r * n + cc] = pow(lam, (double)(r - cc)) * dot;
+                }
+            if (o)
+                for (int64_t r = 0; r < n; ++r)
+                    for (int32_t j = 0; j < d; ++j) {
+                        double acc = 0.0;
+                        for (int64_t cc = 0; cc < n; ++cc) acc += A[r * n + cc] * widen(v, dtype, ((s0 + cc) * H + h) * d + j);
+                        if (kv_in) {
+                            const double f = pow(lam, (double)(r + 1));
+                            for (int32_t i = 0; i < d; ++i)
+                                acc += f * widen(q, dtype, ((s0 + r) * H + h) * d + i) * kv_in[sbase + (size_t)i * d + j];
+                        }
+                        o[((s0 + r) * H + h) * d + j] = acc;
+                    }
+            if (kv_out)
+                for (int32_t i = 0; i < d; ++i)
+                    for (int32_t j = 0; j < d; ++j) {
+                        double acc = kv_in ? pow(lam, (double)n) * kv_in[sbase + (size_t)i * d + j] : 0.0;
+                        for (int64_t cc = 0; cc < n; ++cc)
+                            acc += pow(lam, (double)(n - 1 - cc)) * widen(k, dtype, ((s0 + cc) * H + h) * d + i) *
+                                   widen(v, dtype, ((s0 + cc) * H + h) * d + j);
                         kv_out[sbase + (size_t)i * d + j] = acc;
                     }
             free(A);
@@ -317,6 +403,7 @@ typedef struct {
     int dtype;
     int32_t d;
     double *S, *o;
+    const double* decay; /* per-pair factor, or NULL */
 } dec_ctx;
 
 static void dec_task(void* cv, int64_t p) {
@@ -324,6 +411,9 @@ static void dec_task(void* cv, int64_t p) {
     const int32_t d = c->d;
     double* S = c->S + (size_t)p * d * d;
     const int64_t row = p * (int64_t)d;
+    /* decayed variant: S <- lambda S first */
+    if (c->decay)
+        for (size_t e = 0; e < (size_t)d * d; ++e) S[e] *= c->decay[p];
     /* S <- S + k^T v */
     for (int32_t i = 0; i < d; ++i) {
         double ki = widen(c->k, c->dtype, row + i);
@@ -341,7 +431,17 @@ static void dec_task(void* cv, int64_t p) {
 int ora_decode_step(const void* q, const void* k, const void* v, int dtype, int64_t npairs, int32_t d,
                     double* S, double* o, int nthreads) {
     if (!q || !k || !v || !S || dtype < 0 || dtype > 2 || npairs < 0 || d < 1) return -1;
-    dec_ctx c = {q, k, v, dtype, d, S, o};
+    dec_ctx c = {q, k, v, dtype, d, S, o, NULL};
+    run_tasks(npairs, nthreads, dec_task, &c);
+    return 0;
+}
+
+int ora_decode_step_decay(const void* q, const void* k, const void* v, int dtype, int64_t npairs, int32_t d,
+                          const double* decay, double* S, double* o, int nthreads) {
+    if (!q || !k || !v || !S || !decay || dtype < 0 || dtype > 2 || npairs < 0 || d < 1) return -1;
+    for (int64_t p = 0; p < npairs; ++p)
+        if (!(decay[p] >= 0.0 && decay[p] <= 1.0)) return -1;
+    dec_ctx c = {q, k, v, dtype, d, S, o, decay};
     run_tasks(npairs, nthreads, dec_task, &c);
     return 0;
 }

@@ -59,6 +59,25 @@ int ora_backward(const void* q, const void* k, const void* v, const void* dout, 
                  int32_t num_seqs, int32_t H, int32_t d, const double* kv_in, const double* dkv_out, double* dq,
                  double* dk, double* dv, double* dkv_in, int nthreads);
 
+/* The decayed variant (a reading: the pages name a decay among the fused
+ * prefill steps, "MiniMax-01技术报告解读" §3.3 item 1, but never define it):
+ * per head h a factor lambda_h = decay[h] in [0, 1] (fp64 [H]) fades the state
+ * before each token's update,
+ *     S_t = lambda_h S_{t-1} + k_t^T v_t ,   o_t = q_t . S_t ,
+ * starting from S = kv_in (or zero) before the document's first token.
+ * Form (b) and form (a) (o_r = sum_{c <= r} lambda^(r-c) (q_r . k_c) v_c +
+ * lambda^(r+1) q_r . kv_in), and the decode step with a factor per pair
+ * (decay fp64 [npairs]): S <- lambda S + k^T v ; o = q . S.  Arguments
+ * otherwise as in the undecayed functions; a factor outside [0, 1] returns -1. */
+int ora_recurrent_decay(const void* q, const void* k, const void* v, int dtype, const int32_t* cu_seqlens,
+                        int32_t num_seqs, int32_t H, int32_t d, int32_t h0, int32_t h1, const double* decay,
+                        const double* kv_in, double* o, double* kv_out, int nthreads);
+int ora_quadratic_decay(const void* q, const void* k, const void* v, int dtype, const int32_t* cu_seqlens,
+                        int32_t num_seqs, int32_t H, int32_t d, const double* decay, const double* kv_in, double* o,
+                        double* kv_out);
+int ora_decode_step_decay(const void* q, const void* k, const void* v, int dtype, int64_t npairs, int32_t d,
+                          const double* decay, double* S, double* o, int nthreads);
+
 /* Threads the last call used (for reporting). */
 int ora_last_threads(void);
 

@@ -1,8 +1,9 @@
 """Pins for the fp64 oracle (CPU only).
 
-The oracle is checked against things other than itself: a hand-worked example
-(tests/golden/hand_worked_d2.txt), closed forms that reduce to numpy routines
-(cumsum, tril, matmul), algebraic identities of the definition (left product
+The oracle is checked against things other than itself: hand-worked examples
+(tests/golden/hand_worked_d2.txt, and hand_worked_d2_decay.txt for the decayed
+variant), closed forms that reduce to numpy or scipy routines (cumsum, tril,
+matmul, a first-order recursive filter) or to a geometric series, algebraic identities of the definition (left product
 == right product, split-then-resume, linearity, packed == separate), and the
 two forms against each other.  ``test_planted_mistakes`` rebuilds the oracle
 with one plausible mistake at a time and checks that some pin fails.
@@ -231,8 +232,142 @@ def pin_backward_finite_differences(lib):
     return True
 
 
+# ------------------------------------------------------ decayed variant
+
+GOLDEN_DECAY = os.path.join(os.path.dirname(__file__), "golden", "hand_worked_d2_decay.txt")
+
+
+def pin_decay_hand_worked(lib):
+    g = {}
+    with open(GOLDEN_DECAY, encoding="utf-8") as f:
+        for line in f:
+            line = line.split("#", 1)[0].strip()
+            if line:
+                name, *vals = line.split()
+                g[name] = [float(x) for x in vals]
+    lam = np.array(g["lambda"])
+    toks = [g[f"tok{i}"] for i in range(1, 7)]
+    q = np.array([t[0:2] for t in toks]).reshape(6, 1, 2)
+    k = np.array([t[2:4] for t in toks]).reshape(6, 1, 2)
+    v = np.array([t[4:6] for t in toks]).reshape(6, 1, 2)
+    sel = [0, 1, 2, 4, 5]
+    cu = np.array([0, 3, 5], dtype=np.int32)
+    exp_o = np.array([g["o1"], g["o2"], g["o3"], g["o5"], g["o6"]]).reshape(5, 1, 2)
+    exp_S = np.stack([np.array(g["S3"]).reshape(2, 2), np.array(g["S6"]).reshape(2, 2)]).reshape(2, 1, 2, 2)
+    ok = True
+    for fn in (oracle.recurrent, oracle.quadratic):
+        o, s = fn(q[sel], k[sel], v[sel], cu, lib=lib, decay=lam)
+        ok &= np.array_equal(o, exp_o) and np.array_equal(s, exp_S)
+    S = np.array(g["S3"]).reshape(1, 2, 2).copy()
+    o4 = oracle.decode_step(q[3].reshape(1, 2), k[3].reshape(1, 2), v[3].reshape(1, 2), S, lib=lib, decay=lam)
+    ok &= np.array_equal(o4, np.array([g["o4"]])) and np.array_equal(S.reshape(4), np.array(g["S4"]))
+    return bool(ok)
+
+
+def pin_decay_one_is_undecayed(lib):
+    """lambda = 1 gives the undecayed results bit for bit (every form)."""
+    rng = np.random.default_rng(41)
+    q, k, v = _rand(rng, 37, 3, 6)
+    cu = np.array([0, 10, 10, 37], np.int32)
+    kv_in = rng.standard_normal((3, 3, 6, 6))
+    ones = np.ones(3)
+    for fn in (oracle.recurrent, oracle.quadratic):
+        a = fn(q, k, v, cu, kv_in=kv_in, lib=lib)
+        b = fn(q, k, v, cu, kv_in=kv_in, lib=lib, decay=ones)
+        if not (np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])):
+            return False
+    S0 = rng.standard_normal((4, 6, 6))
+    qq, kk, vv = (rng.standard_normal((4, 6)) for _ in range(3))
+    S1, S2 = S0.copy(), S0.copy()
+    o1 = oracle.decode_step(qq, kk, vv, S1, lib=lib)
+    o2 = oracle.decode_step(qq, kk, vv, S2, lib=lib, decay=np.ones(4))
+    return np.array_equal(o1, o2) and np.array_equal(S1, S2)
+
+
+def pin_decay_forms_agree(lib):
+    """Recurrent and quadratic decayed forms, per-head factors including 0 and
+    1, with and without incoming states, packed documents with empty ones."""
+    rng = np.random.default_rng(43)
+    for lam in ([0.0, 0.25, 0.9, 1.0], [0.5, 0.5, 0.5, 0.5], [0.999, 0.1, 0.0, 0.7]):
+        for kv in (False, True):
+            q, k, v = _rand(rng, 45, 4, 5)
+            cu = np.array([0, 0, 13, 13, 40, 45], np.int32)
+            kv_in = rng.standard_normal((5, 4, 5, 5)) if kv else None
+            ob, sb = oracle.recurrent(q, k, v, cu, kv_in=kv_in, lib=lib, decay=lam)
+            oa, sa = oracle.quadratic(q, k, v, cu, kv_in=kv_in, lib=lib, decay=lam)
+            if not (_close(ob, oa) and _close(sb, sa)):
+                return False
+    return True
+
+
+def pin_decay_closed_forms(lib):
+    from scipy.signal import lfilter
+
+    rng = np.random.default_rng(47)
+    # d = 1: the state is the first-order recursive filter y_t = x_t + lambda y_{t-1}
+    # of x_t = k_t v_t (scipy's lfilter), and o_t = q_t y_t
+    n, lam = 80, 0.83
+    q, k, v = _rand(rng, n, 1, 1)
+    o, s = oracle.recurrent(q, k, v, np.array([0, n], np.int32), lib=lib, decay=[lam])
+    y = lfilter([1.0], [1.0, -lam], k[:, 0, 0] * v[:, 0, 0])
+    if not (_close(o[:, 0, 0], q[:, 0, 0] * y) and _close(s[0, 0, 0, 0], y[-1])):
+        return False
+    # q_t = k_t = e_1, v_t = u: a geometric series, o_t = u (1 - lambda^(t+1)) / (1 - lambda)
+    n, d, lam = 30, 3, 0.6
+    e1 = np.zeros((n, 1, d))
+    e1[:, 0, 0] = 1.0
+    u = rng.standard_normal(d)
+    vv = np.tile(u, (n, 1)).reshape(n, 1, d)
+    o, _ = oracle.recurrent(e1, e1.copy(), vv, np.array([0, n], np.int32), lib=lib, decay=[lam])
+    t = np.arange(n)[:, None]
+    if not _close(o[:, 0, :], u[None, :] * (1.0 - lam ** (t + 1)) / (1.0 - lam)):
+        return False
+    # lambda = 0: only the current token (and no incoming state) survives: o_t = (q_t . k_t) v_t
+    q, k, v = _rand(rng, 20, 2, 4)
+    kv_in = rng.standard_normal((1, 2, 4, 4))
+    o, s = oracle.recurrent(q, k, v, np.array([0, 20], np.int32), kv_in=kv_in, lib=lib, decay=[0.0, 0.0])
+    if not _close(o, np.einsum("thi,thi->th", q, k)[:, :, None] * v):
+        return False
+    if not _close(s[0], np.einsum("hi,hj->hij", k[-1], v[-1])):
+        return False
+    # per-head factors: each head equals a one-head run with its own factor
+    q, k, v = _rand(rng, 25, 3, 4)
+    lams = [0.2, 0.95, 0.6]
+    cu = np.array([0, 25], np.int32)
+    o, s = oracle.recurrent(q, k, v, cu, lib=lib, decay=lams)
+    for h in range(3):
+        oh, sh = oracle.recurrent(q[:, h:h + 1], k[:, h:h + 1], v[:, h:h + 1], cu, lib=lib, decay=[lams[h]])
+        if not (_close(o[:, h:h + 1], oh) and _close(s[:, h:h + 1], sh)):
+            return False
+    return True
+
+
+def pin_decay_split_resume(lib):
+    rng = np.random.default_rng(53)
+    n, H, d = 20, 2, 5
+    lam = [0.7, 0.95]
+    q, k, v = _rand(rng, n, H, d)
+    o_full, s_full = oracle.recurrent(q, k, v, np.array([0, n], np.int32), lib=lib, decay=lam)
+    for m in range(0, n + 1):
+        _, s_m = oracle.recurrent(q[:m], k[:m], v[:m], np.array([0, m], np.int32), want_o=False, lib=lib, decay=lam)
+        o_t, s_t = oracle.recurrent(q[m:], k[m:], v[m:], np.array([0, n - m], np.int32), kv_in=s_m, lib=lib,
+                                    decay=lam)
+        if not (_close(o_t, o_full[m:]) and _close(s_t, s_full)):
+            return False
+    # decode continues the decayed prefill
+    m = 12
+    _, S = oracle.recurrent(q[:m], k[:m], v[:m], np.array([0, m], np.int32), want_o=False, lib=lib, decay=lam)
+    S = S[0].copy()
+    for t in range(m, n):
+        if not _close(oracle.decode_step(q[t], k[t], v[t], S, lib=lib, decay=lam), o_full[t]):
+            return False
+    return True
+
+
 PINS = [pin_hand_worked, pin_forms_agree, pin_split_resume, pin_closed_forms, pin_linearity,
-        pin_packed_equals_separate, pin_decode_continues_prefill, pin_backward_finite_differences]
+        pin_packed_equals_separate, pin_decode_continues_prefill, pin_backward_finite_differences,
+        pin_decay_hand_worked, pin_decay_one_is_undecayed, pin_decay_forms_agree, pin_decay_closed_forms,
+        pin_decay_split_resume]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -304,6 +439,16 @@ MUTANTS = [
      r"acc \+= M\[\(size_t\)i \* d \+ j\] \* b\[j\];\n(\s+)c->dq", "acc += M[(size_t)j * d + i] * b[j];\n\\1c->dq"),
     ("backward: dv from the transposed reverse state",
      r"acc \+= a\[i\] \* M\[\(size_t\)i \* d \+ j\];", "acc += a[i] * M[(size_t)j * d + i];"),
+    ("decay: factor ignored in the recurrence",
+     r"S\[i \* ORA_COLS \+ jj\] \*= c->decay\[h\];", "S[i * ORA_COLS + jj] *= 1.0;"),
+    ("decay: the first head's factor for every head",
+     r"S\[i \* ORA_COLS \+ jj\] \*= c->decay\[h\];", "S[i * ORA_COLS + jj] *= c->decay[0];"),
+    ("decay: quadratic form's exponent off by one",
+     r"pow\(lam, \(double\)\(r - cc\)\)", "pow(lam, (double)(r - cc + 1))"),
+    ("decay: incoming state not faded in the quadratic form",
+     r"const double f = pow\(lam, \(double\)\(r \+ 1\)\);", "const double f = 1.0;"),
+    ("decay: decode fades the state twice",
+     r"S\[e\] \*= c->decay\[p\];", "S[e] *= c->decay[p] * c->decay[p];"),
     ("backward: token s left out of its own reverse sum",
      r"(\s+)for \(int32_t i = 0; i < d; \+\+i\) a\[i\] = widen\(c->q, c->dtype, row \+ i\);",
      "\\1for (int32_t i = 0; i < d; ++i) a[i] = (t == (int64_t)c->cu[doc + 1] - 1) ? 0.0 : widen(c->q, c->dtype, row + i + H * d);"),
@@ -322,7 +467,7 @@ def test_planted_mistakes(tmp_path, oracle_lib, desc, pat, rep):
 
     shutil.copy(os.path.join(os.path.dirname(oracle._SRC), "la_oracle.h"), tmp_path / "la_oracle.h")
     so = str(tmp_path / "mut.so")
-    subprocess.check_call(["gcc", "-O2", "-fPIC", "-shared", "-pthread", str(msrc), "-o", so])
+    subprocess.check_call(["gcc", "-O2", "-fPIC", "-shared", "-pthread", str(msrc), "-o", so, "-lm"])
     lib = oracle.load(so)
     failed = []
     for pin in PINS:
