@@ -21,7 +21,7 @@ LA_BF16, LA_FP32 = 0, 1
 
 EXPORTED = ("la_prefill", "la_decode", "la_prefill_workspace_size", "la_status_string", "la_prefill_plan",
             "la_prefill_workspace_size_ex", "la_prefill_ex", "la_prefill_resume", "la_prefill_backward",
-            "la_bench_stream", "la_prefill_noalloc")
+            "la_bench_stream", "la_prefill_noalloc", "la_prefill_decay", "la_decode_decay")
 
 
 class LAError(RuntimeError):
@@ -86,6 +86,11 @@ def load():
     lib.la_prefill_plan.restype = ctypes.c_int
     lib.la_status_string.argtypes = [ctypes.c_int]
     lib.la_status_string.restype = ctypes.c_char_p
+    lib.la_prefill_decay.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, vp, vp, vp, i32, i64, ctypes.c_int, vp, sz, vp,
+                                     ctypes.POINTER(la_prefill_opts)]
+    lib.la_prefill_decay.restype = ctypes.c_int
+    lib.la_decode_decay.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, ctypes.c_int, vp]
+    lib.la_decode_decay.restype = ctypes.c_int
     lib.la_prefill_noalloc.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, vp, i32, i64, ctypes.c_int, vp]
     lib.la_prefill_noalloc.restype = ctypes.c_int
     lib.la_bench_stream.argtypes = [i32, vp, vp, vp, vp, sz, i32, i32, vp]
@@ -129,6 +134,17 @@ def la_prefill_backward(q, k, v, dout, cu_seqlens, H, d, block, kv_state_in, dkv
 
 def la_decode(q, k, v, kv_state_inout, o, num_seqs, H, d, dtype, stream) -> int:
     return load().la_decode(q, k, v, kv_state_inout, o, num_seqs, H, d, dtype, stream)
+
+
+def la_prefill_decay(q, k, v, o, cu_seqlens, H, d, block, decay, kv_state_in, kv_state_out, num_seqs, total_tokens,
+                     dtype, workspace, workspace_bytes, stream, opts: la_prefill_opts | None) -> int:
+    return load().la_prefill_decay(q, k, v, o, cu_seqlens, H, d, block, decay, kv_state_in, kv_state_out, num_seqs,
+                                   total_tokens, dtype, workspace, workspace_bytes, stream,
+                                   ctypes.byref(opts) if opts is not None else None)
+
+
+def la_decode_decay(q, k, v, decay, kv_state_inout, o, num_seqs, H, d, dtype, stream) -> int:
+    return load().la_decode_decay(q, k, v, decay, kv_state_inout, o, num_seqs, H, d, dtype, stream)
 
 
 def la_prefill_noalloc(q, k, v, o, cu_seqlens, H, d, block, kv_state_out, num_seqs, total_tokens, dtype,
@@ -250,14 +266,16 @@ def _check_ws(ws, ref, where: str):
 def prefill(q, k, v, cu_seqlens, block: int = 64, want_state: bool = True, out=None, kv_state_out=None,
             workspace=None, seg_len: int = 0, value_slices: int = 0, force_scan: bool = False, stream=None,
             begin_event=None, end_event=None, variant: int = 0, kv_state_in=None, slots: int = 0,
-            work_list: int = 0):
+            work_list: int = 0, decay=None):
     """Lightning-style causal linear attention over packed documents.
 
     q, k, v: [T, H, d] bf16/fp32 CUDA tensors; cu_seqlens: int32 [num_seqs + 1]
     CUDA tensor.  Returns (o, kv_state) with kv_state fp32 [num_seqs, H, d, d]
     (None when want_state is False).  kv_state_in (fp32 [num_seqs, H, d, d],
     optional) is each document's state before its first token (la_prefill_resume).
-    Asynchronous on the current stream (or `stream`).
+    Asynchronous on the current stream (or `stream`).  decay (fp32 [H] CUDA
+    tensor, optional): each head's factor lambda in [0, 1] of the decayed
+    variant (la_prefill_decay).
     """
     import torch
 
@@ -270,7 +288,8 @@ def prefill(q, k, v, cu_seqlens, block: int = 64, want_state: bool = True, out=N
     _check_tensors(q, {"k": (k, None, q.shape), "v": (v, None, q.shape), "out": (out, None, q.shape),
                        "kv_state_out": (kv_state_out, torch.float32, st_shape),
                        "kv_state_in": (kv_state_in, torch.float32, st_shape),
-                       "cu_seqlens": (cu_seqlens, torch.int32, (num_seqs + 1,)), "q": (q, None, q.shape)},
+                       "cu_seqlens": (cu_seqlens, torch.int32, (num_seqs + 1,)),
+                       "decay": (decay, torch.float32, (H,)), "q": (q, None, q.shape)},
                    "prefill")
     _check_ws(workspace, q, "prefill")
     o = out if out is not None else torch.empty_like(q)
@@ -284,11 +303,16 @@ def prefill(q, k, v, cu_seqlens, block: int = 64, want_state: bool = True, out=N
     if need and (ws is None or ws.numel() * ws.element_size() < need):
         ws = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_bytes = ws.numel() * ws.element_size() if ws is not None else 0
-    st = la_prefill_resume(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(cu_seqlens), H, d, block, _ptr(kv_state_in),
-                           _ptr(kv), num_seqs, T, dt, _ptr(ws) if need else None, ws_bytes if need else 0,
-                           _stream_ptr(stream), opts)
+    if decay is not None:
+        st = la_prefill_decay(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(cu_seqlens), H, d, block, _ptr(decay),
+                              _ptr(kv_state_in), _ptr(kv), num_seqs, T, dt, _ptr(ws) if need else None,
+                              ws_bytes if need else 0, _stream_ptr(stream), opts)
+    else:
+        st = la_prefill_resume(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(cu_seqlens), H, d, block, _ptr(kv_state_in),
+                               _ptr(kv), num_seqs, T, dt, _ptr(ws) if need else None, ws_bytes if need else 0,
+                               _stream_ptr(stream), opts)
     if st != LA_OK:
-        raise LAError(st, "la_prefill")
+        raise LAError(st, "la_prefill_decay" if decay is not None else "la_prefill")
     return o, kv
 
 
@@ -344,9 +368,10 @@ def backward(q, k, v, dout, cu_seqlens, block: int = 64, kv_state_in=None, dkv_s
     return dq, dk, dv, dkv_in
 
 
-def decode(q, k, v, kv_state, out=None, stream=None):
+def decode(q, k, v, kv_state, out=None, stream=None, decay=None):
     """One decode step; kv_state (fp32 [num_seqs, H, d, d]) is updated in place.
-    q, k, v: [num_seqs, H, d].  Returns o."""
+    q, k, v: [num_seqs, H, d].  decay (fp32 [H], optional): the decayed
+    variant (la_decode_decay).  Returns o."""
     import torch
 
     _check(q.dim() == 3, ValueError, f"decode: q must be [num_seqs, H, d], got shape {tuple(q.shape)}")
@@ -354,13 +379,18 @@ def decode(q, k, v, kv_state, out=None, stream=None):
     _dtype_code(q)
     _check(kv_state is not None, ValueError, "decode: kv_state is required")
     _check_tensors(q, {"k": (k, None, q.shape), "v": (v, None, q.shape), "out": (out, None, q.shape),
-                       "kv_state": (kv_state, torch.float32, (num_seqs, H, d, d)), "q": (q, None, q.shape)},
+                       "kv_state": (kv_state, torch.float32, (num_seqs, H, d, d)),
+                       "decay": (decay, torch.float32, (H,)), "q": (q, None, q.shape)},
                    "decode")
     o = out if out is not None else torch.empty_like(q)
-    st = la_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(kv_state), _ptr(o), num_seqs, H, d, _dtype_code(q),
-                   _stream_ptr(stream))
+    if decay is not None:
+        st = la_decode_decay(_ptr(q), _ptr(k), _ptr(v), _ptr(decay), _ptr(kv_state), _ptr(o), num_seqs, H, d,
+                             _dtype_code(q), _stream_ptr(stream))
+    else:
+        st = la_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(kv_state), _ptr(o), num_seqs, H, d, _dtype_code(q),
+                       _stream_ptr(stream))
     if st != LA_OK:
-        raise LAError(st, "la_decode")
+        raise LAError(st, "la_decode_decay" if decay is not None else "la_decode")
     return o
 
 

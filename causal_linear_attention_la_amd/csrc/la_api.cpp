@@ -43,8 +43,10 @@ la_status scratch_on_current_device(void** out) {
 // plan (FNV-1a over them; never 0).  A backward handed the workspace with
 // forward_states reuses the states only if the key stamped there is its own.
 uint64_t states_key(const Plan& plan, const void* q, const void* k, const void* v, const int32_t* cu, int32_t H,
-                    int32_t d, int32_t block, int32_t num_seqs, int64_t T, la_dtype dtype) {
-    const uint64_t parts[] = {(uint64_t)(uintptr_t)q, (uint64_t)(uintptr_t)k, (uint64_t)(uintptr_t)v,
+                    int32_t d, int32_t block, int32_t num_seqs, int64_t T, la_dtype dtype,
+                    const float* decay = nullptr) {
+    const uint64_t parts[] = {(uint64_t)(uintptr_t)decay, (uint64_t)(uintptr_t)q, (uint64_t)(uintptr_t)k,
+                              (uint64_t)(uintptr_t)v,
                               (uint64_t)(uintptr_t)cu, (uint64_t)H, (uint64_t)d, (uint64_t)block,
                               (uint64_t)num_seqs, (uint64_t)T, (uint64_t)dtype, (uint64_t)plan.L, (uint64_t)plan.S,
                               (uint64_t)plan.nseg, (uint64_t)plan.scan, (uint64_t)plan.packed,
@@ -70,7 +72,7 @@ la_status enqueue_prefill(const Plan& plan, const void* q, const void* k, const 
                           int32_t H, int32_t d, int32_t block, const float* kv_in, int kv_in_t, float* kv_out,
                           int rev, int32_t num_seqs, int64_t T, la_dtype dtype, void* workspace, void* stream,
                           hipEvent_t e0, hipEvent_t e1, int skip_prefix = 0, bool stamp = false,
-                          const int32_t* reuse = nullptr) {
+                          const int32_t* reuse = nullptr, const float* decay = nullptr) {
     la::PrefillParams p{};
     p.q = q;
     p.k = k;
@@ -99,9 +101,11 @@ la_status enqueue_prefill(const Plan& plan, const void* q, const void* k, const 
     p.skip_prefix = skip_prefix;
     if (plan.ws_bytes > 0) {
         p.marker = reinterpret_cast<uint64_t*>(ws_at(workspace, plan.ws_marker_off));
-        p.key = stamp && plan.states() > 0 ? states_key(plan, q, k, v, cu, H, d, block, num_seqs, T, dtype) : 0;
+        p.key = stamp && plan.states() > 0 ? states_key(plan, q, k, v, cu, H, d, block, num_seqs, T, dtype, decay)
+                                           : 0;
     }
     p.reuse = reuse;
+    p.decay = decay;
     p.units = plan.units;
     p.per_xcd = (plan.units + 7) / 8;
     hipStream_t s = static_cast<hipStream_t>(stream);
@@ -168,6 +172,25 @@ la_status la_prefill_resume(const void* q, const void* k, const void* v, void* o
     hipEvent_t e1 = opts ? static_cast<hipEvent_t>(opts->main_end_event) : nullptr;
     return enqueue_prefill(plan, q, k, v, o, cu_seqlens, H, d, block, kv_state_in, 0, kv_state_out, 0, num_seqs,
                            total_tokens, dtype, workspace, stream, e0, e1, 0, true);
+}
+
+la_status la_prefill_decay(const void* q, const void* k, const void* v, void* o, const int32_t* cu_seqlens,
+                           int32_t H, int32_t d, int32_t block, const float* decay, const float* kv_state_in,
+                           float* kv_state_out, int32_t num_seqs, int64_t total_tokens, la_dtype dtype,
+                           void* workspace, size_t workspace_bytes, void* stream, const la_prefill_opts* opts) {
+    if (!decay || reinterpret_cast<uintptr_t>(decay) % 4 != 0) return LA_ERR_INVALID_ARG;
+    Plan plan;
+    la_status st = la::validate_prefill(q, k, v, o, cu_seqlens, H, d, block, kv_state_in, kv_state_out, num_seqs,
+                                        total_tokens, (int)dtype, workspace, workspace_bytes, opts, &plan, true);
+    if (st != LA_OK) return st;
+    // the factors are read while the outputs are written: no overlap with any output
+    if (la::overlaps_outputs(decay, (size_t)H * 4, o, kv_state_out, workspace, plan, total_tokens, num_seqs, H, d,
+                             (int)dtype))
+        return LA_ERR_INVALID_ARG;
+    hipEvent_t e0 = opts ? static_cast<hipEvent_t>(opts->main_begin_event) : nullptr;
+    hipEvent_t e1 = opts ? static_cast<hipEvent_t>(opts->main_end_event) : nullptr;
+    return enqueue_prefill(plan, q, k, v, o, cu_seqlens, H, d, block, kv_state_in, 0, kv_state_out, 0, num_seqs,
+                           total_tokens, dtype, workspace, stream, e0, e1, 0, true, nullptr, decay);
 }
 
 la_status la_prefill_backward(const void* q, const void* k, const void* v, const void* dout,
@@ -270,8 +293,8 @@ la_status la_prefill_noalloc(const void* q, const void* k, const void* v, void* 
                            total_tokens, dtype, ws, stream, nullptr, nullptr, 0, true);
 }
 
-la_status la_decode(const void* q, const void* k, const void* v, float* kv_state_inout, void* o, int32_t num_seqs,
-                    int32_t H, int32_t d, la_dtype dtype, void* stream) {
+static la_status decode_impl(const void* q, const void* k, const void* v, const float* decay, float* kv_state_inout,
+                             void* o, int32_t num_seqs, int32_t H, int32_t d, la_dtype dtype, void* stream) {
     la_status st = la::validate_decode(q, k, v, kv_state_inout, o, num_seqs, H, d, (int)dtype);
     if (st != LA_OK) return st;
     la::DecodeParams p{};
@@ -281,8 +304,24 @@ la_status la_decode(const void* q, const void* k, const void* v, float* kv_state
     p.S = kv_state_inout;
     p.o = o;
     p.pairs = (int64_t)num_seqs * H;
+    p.decay = decay;
+    p.H = H;
     hipError_t e = la::launch_decode(p, d, (int)dtype, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? LA_OK : LA_ERR_HIP;
+}
+
+la_status la_decode(const void* q, const void* k, const void* v, float* kv_state_inout, void* o, int32_t num_seqs,
+                    int32_t H, int32_t d, la_dtype dtype, void* stream) {
+    return decode_impl(q, k, v, nullptr, kv_state_inout, o, num_seqs, H, d, dtype, stream);
+}
+
+la_status la_decode_decay(const void* q, const void* k, const void* v, const float* decay, float* kv_state_inout,
+                          void* o, int32_t num_seqs, int32_t H, int32_t d, la_dtype dtype, void* stream) {
+    if (!decay || reinterpret_cast<uintptr_t>(decay) % 4 != 0) return LA_ERR_INVALID_ARG;
+    if (la::overlaps_range(decay, (size_t)H * 4, kv_state_inout, (size_t)num_seqs * H * d * d * 4) ||
+        la::overlaps_range(decay, (size_t)H * 4, o, (size_t)num_seqs * H * d * la::elem_size((int)dtype)))
+        return LA_ERR_INVALID_ARG;
+    return decode_impl(q, k, v, decay, kv_state_inout, o, num_seqs, H, d, dtype, stream);
 }
 
 }  // extern "C"

@@ -3,14 +3,14 @@
 
 namespace la {
 namespace {
-template <typename T>
+template <typename T, bool DK>
 hipError_t run_decode(const DecodeParams& p, int D, hipStream_t st) {
     const dim3 grid((unsigned)p.pairs), block(kThreads);
     switch (D) {
-        case 16: return launch_kernel(la_decode_kernel<T, 16>, grid, block, st, p);
-        case 32: return launch_kernel(la_decode_kernel<T, 32>, grid, block, st, p);
-        case 64: return launch_kernel(la_decode_kernel<T, 64>, grid, block, st, p);
-        case 128: return launch_kernel(la_decode_kernel<T, 128>, grid, block, st, p);
+        case 16: return launch_kernel(la_decode_kernel<T, 16, DK>, grid, block, st, p);
+        case 32: return launch_kernel(la_decode_kernel<T, 32, DK>, grid, block, st, p);
+        case 64: return launch_kernel(la_decode_kernel<T, 64, DK>, grid, block, st, p);
+        case 128: return launch_kernel(la_decode_kernel<T, 128, DK>, grid, block, st, p);
         default: return hipErrorInvalidValue;
     }
 }
@@ -18,6 +18,7 @@ hipError_t run_decode(const DecodeParams& p, int D, hipStream_t st) {
 
 hipError_t launch_decode(const DecodeParams& p, int D, int dtype, hipStream_t st) {
     if (p.pairs == 0) return hipSuccess;
-    return dtype == 0 ? run_decode<bf16_t>(p, D, st) : run_decode<float>(p, D, st);
+    if (p.decay) return dtype == 0 ? run_decode<bf16_t, true>(p, D, st) : run_decode<float, true>(p, D, st);
+    return dtype == 0 ? run_decode<bf16_t, false>(p, D, st) : run_decode<float, false>(p, D, st);
 }
 }  // namespace la

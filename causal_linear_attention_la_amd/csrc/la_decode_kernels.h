@@ -19,6 +19,8 @@ struct DecodeParams {
     float* S;
     void* o;
     int64_t pairs;
+    const float* decay;  // decayed variant: per-head lambda (device, [H]), or null
+    int32_t H;
 };
 
 // One workgroup per pair.  Thread t owns 4 consecutive value columns
@@ -26,7 +28,8 @@ struct DecodeParams {
 // rg = t / (D/4).  Each state row is read and written once as coalesced
 // float4s; the partial dot products of q with the updated columns are reduced
 // across row groups through LDS in a fixed order (deterministic).
-template <typename TIn, int D>
+// Decayed variant (DK): KV <- lambda KV + k^T v with the pair's head's lambda.
+template <typename TIn, int D, bool DK = false>
 __global__ __launch_bounds__(kThreads) void la_decode_kernel(DecodeParams p) {
     constexpr int LPR = D / 4;                      // threads per state row
     constexpr int RG = kThreads / LPR;              // row groups
@@ -48,6 +51,7 @@ __global__ __launch_bounds__(kThreads) void la_decode_kernel(DecodeParams p) {
     const float v0 = to_f32(vg[4 * cq + 0]), v1 = to_f32(vg[4 * cq + 1]);
     const float v2 = to_f32(vg[4 * cq + 2]), v3 = to_f32(vg[4 * cq + 3]);
     f32x4_t* S = reinterpret_cast<f32x4_t*>(p.S + pair * (int64_t)D * D);
+    const float lam = DK ? p.decay[pair % p.H] : 1.f;
 
     f32x4_t st[RPT];
 #pragma unroll
@@ -63,6 +67,7 @@ __global__ __launch_bounds__(kThreads) void la_decode_kernel(DecodeParams p) {
         if (i < D) {
             const float ki = ks[i], qi = qs[i];
             f32x4_t x = st[r];
+            if constexpr (DK) x *= lam;
             x[0] = fmaf(ki, v0, x[0]);
             x[1] = fmaf(ki, v1, x[1]);
             x[2] = fmaf(ki, v2, x[2]);

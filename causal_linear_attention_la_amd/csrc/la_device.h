@@ -91,6 +91,27 @@ __device__ __forceinline__ void store4_zero(float* p) { *reinterpret_cast<float4
 
 __device__ __forceinline__ f32x4_t zero4() { return f32x4_t{0.f, 0.f, 0.f, 0.f}; }
 
+// Decayed variant: lambda^m for m >= 0 from l2 = log2(lambda), as exp2(m l2);
+// lambda^0 = 1 also for lambda = 0 (l2 = -inf).
+__device__ __forceinline__ float decay_pow(float l2, int m) { return m <= 0 ? 1.f : exp2f(l2 * (float)m); }
+
+// A bf16 fragment (8 elements) scaled element by element, rounded to nearest
+// even; element e of lo.x, lo.y, hi.x, hi.y is (e % 2 == 0 ? low : high) half.
+__device__ __forceinline__ Frag<bf16_t> scale_frag(const Frag<bf16_t>& f, const float (&w)[8]) {
+    const uint32_t in[4] = {f.lo.x, f.lo.y, f.hi.x, f.hi.y};
+    uint32_t out[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float a = __uint_as_float(in[i] << 16) * w[2 * i];
+        const float b = __uint_as_float(in[i] & 0xffff0000u) * w[2 * i + 1];
+        out[i] = pack_bf16x2(a, b);
+    }
+    Frag<bf16_t> r;
+    r.lo = make_uint2(out[0], out[1]);
+    r.hi = make_uint2(out[2], out[3]);
+    return r;
+}
+
 // Element e (0..7 for bf16, 0..3 for fp32) of a 16-byte vector.
 __device__ __forceinline__ uint32_t lane16(const uint4& v, int e) {
     uint32_t w = e < 2 ? v.x : e < 4 ? v.y : e < 6 ? v.z : v.w;

@@ -62,7 +62,7 @@ bool mul_ok(int64_t a, int64_t b, int64_t& out) {
 size_t elem_size(int dtype) { return dtype == LA_BF16 ? 2 : dtype == LA_FP32 ? 4 : 0; }
 
 la_status make_plan(int64_t T, int32_t num_seqs, int32_t H, int32_t d, int32_t block, int dtype,
-                    const la_prefill_opts* opts, Plan* out) {
+                    const la_prefill_opts* opts, Plan* out, bool decay) {
     if (H < 1 || num_seqs < 1 || T < 0 || T > INT32_MAX) return LA_ERR_INVALID_ARG;
     const size_t es = elem_size(dtype);
     if (es == 0) return LA_ERR_UNSUPPORTED;
@@ -175,7 +175,8 @@ la_status make_plan(int64_t T, int32_t num_seqs, int32_t H, int32_t d, int32_t b
     if (p.scan && (int64_t)H * d * d / 4 > (((int64_t)1 << 32) - 1)) return LA_ERR_UNSUPPORTED;
     const int32_t slots = opts ? opts->slots : 0;
     if (!(slots == 0 || slots == 2 || slots == 3)) return LA_ERR_UNSUPPORTED;
-    const bool three_ok = p.variant == 2 && d == 128;
+    // (the decayed full-width loop has no registers for a third slot)
+    const bool three_ok = p.variant == 2 && d == 128 && !(decay && p.W == 128);
     if (slots == 3 && !three_ok) return LA_ERR_UNSUPPORTED;
     if (slots != 0) p.slots = slots;
     else p.slots = three_ok && p.L / block >= kThreeSlotMinBlocks ? 3 : 2;
@@ -211,9 +212,9 @@ la_status make_plan(int64_t T, int32_t num_seqs, int32_t H, int32_t d, int32_t b
 la_status validate_prefill(const void* q, const void* k, const void* v, const void* o, const int32_t* cu, int32_t H,
                            int32_t d, int32_t block, const float* kv_in, const float* kv_out, int32_t num_seqs,
                            int64_t T, int dtype, const void* ws, size_t ws_bytes, const la_prefill_opts* opts,
-                           Plan* plan) {
+                           Plan* plan, bool decay) {
     if (!q || !k || !v || !o || !cu) return LA_ERR_INVALID_ARG;
-    la_status st = make_plan(T, num_seqs, H, d, block, dtype, opts, plan);
+    la_status st = make_plan(T, num_seqs, H, d, block, dtype, opts, plan, decay);
     if (st != LA_OK) return st;
     const size_t es = elem_size(dtype);
     int64_t n;
@@ -265,6 +266,15 @@ la_status validate_backward_outputs(const void* q, const void* k, const void* v,
     }
     if (dkv_in && !aligned(dkv_in, 16)) return LA_ERR_INVALID_ARG;
     return LA_OK;
+}
+
+bool overlaps_range(const void* a, size_t na, const void* b, size_t nb) { return overlap(a, na, b, nb); }
+
+bool overlaps_outputs(const void* a, size_t na, const void* o, const float* kv_out, const void* ws, const Plan& plan,
+                      int64_t T, int32_t num_seqs, int32_t H, int32_t d, int dtype) {
+    const size_t tensor = (size_t)T * H * d * elem_size(dtype);
+    const size_t state = (size_t)num_seqs * H * d * d * 4;
+    return overlap(a, na, o, tensor) || overlap(a, na, kv_out, state) || overlap(a, na, ws, plan.ws_bytes);
 }
 
 la_status validate_decode(const void* q, const void* k, const void* v, const float* S, const void* o,

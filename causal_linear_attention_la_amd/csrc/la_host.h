@@ -42,18 +42,25 @@ size_t elem_size(int dtype);
 // Planning from shapes only; LA_OK or the status la_prefill would return for
 // these shapes.
 la_status make_plan(int64_t T, int32_t num_seqs, int32_t H, int32_t d, int32_t block, int dtype,
-                    const la_prefill_opts* opts, Plan* out);
+                    const la_prefill_opts* opts, Plan* out, bool decay = false);
 
 // Full prefill validation (shapes, plan, pointers, alignment, overlap, workspace).
 la_status validate_prefill(const void* q, const void* k, const void* v, const void* o, const int32_t* cu, int32_t H,
                            int32_t d, int32_t block, const float* kv_in, const float* kv_out, int32_t num_seqs,
                            int64_t T, int dtype, const void* ws, size_t ws_bytes, const la_prefill_opts* opts,
-                           Plan* plan);
+                           Plan* plan, bool decay = false);
 
 // Backward: outputs (dq, dk, dv, dkv_in) overlap neither an input nor each other.
 la_status validate_backward_outputs(const void* q, const void* k, const void* v, const void* dout, const float* kv_in,
                                     const float* dkv_out, const void* dq, const void* dk, const void* dv,
                                     const float* dkv_in, int32_t num_seqs, int32_t H, int32_t d, int64_t T, int dtype);
+
+// [a, a + na) and [b, b + nb) overlap (empty ranges or null pointers never do).
+bool overlaps_range(const void* a, size_t na, const void* b, size_t nb);
+// A read-only buffer [a, a + na) overlaps one of a prefill's outputs: o, the
+// final states (when given) or the plan's workspace.
+bool overlaps_outputs(const void* a, size_t na, const void* o, const float* kv_out, const void* ws, const Plan& plan,
+                      int64_t T, int32_t num_seqs, int32_t H, int32_t d, int dtype);
 
 la_status validate_decode(const void* q, const void* k, const void* v, const float* S, const void* o,
                           int32_t num_seqs, int32_t H, int32_t d, int dtype);

@@ -5,14 +5,21 @@
 namespace la {
 // Explicit instantiations: the host pass otherwise calls, but does not emit,
 // the launch stubs of the transpose-read kernels.
-template __global__ void v2::la_prefill_main_v2<128, 64, 128, 2>(PrefillParams);
-template __global__ void v2::la_prefill_main_v2<128, 64, 128, 3>(PrefillParams);
-template __global__ void v2::la_prefill_main_v2<128, 64, 64, 2>(PrefillParams);
-template __global__ void v2::la_prefill_main_v2<128, 64, 64, 3>(PrefillParams);
-template __global__ void v2::la_prefill_main_v2<64, 64, 64, 2>(PrefillParams);
-template __global__ void v2::la_segment_state_v2<128, 64, 128>(PrefillParams);
-template __global__ void v2::la_segment_state_v2<128, 64, 64>(PrefillParams);
-template __global__ void v2::la_segment_state_v2<64, 64, 64>(PrefillParams);
+template __global__ void v2::la_prefill_main_v2<128, 64, 128, 2, false>(PrefillParams);
+template __global__ void v2::la_prefill_main_v2<128, 64, 128, 3, false>(PrefillParams);
+template __global__ void v2::la_prefill_main_v2<128, 64, 64, 2, false>(PrefillParams);
+template __global__ void v2::la_prefill_main_v2<128, 64, 64, 3, false>(PrefillParams);
+template __global__ void v2::la_prefill_main_v2<64, 64, 64, 2, false>(PrefillParams);
+template __global__ void v2::la_segment_state_v2<128, 64, 128, false>(PrefillParams);
+template __global__ void v2::la_segment_state_v2<128, 64, 64, false>(PrefillParams);
+template __global__ void v2::la_segment_state_v2<64, 64, 64, false>(PrefillParams);
+template __global__ void v2::la_prefill_main_v2<128, 64, 128, 2, true>(PrefillParams);
+template __global__ void v2::la_prefill_main_v2<128, 64, 64, 2, true>(PrefillParams);
+template __global__ void v2::la_prefill_main_v2<128, 64, 64, 3, true>(PrefillParams);
+template __global__ void v2::la_prefill_main_v2<64, 64, 64, 2, true>(PrefillParams);
+template __global__ void v2::la_segment_state_v2<128, 64, 128, true>(PrefillParams);
+template __global__ void v2::la_segment_state_v2<128, 64, 64, true>(PrefillParams);
+template __global__ void v2::la_segment_state_v2<64, 64, 64, true>(PrefillParams);
 template __global__ void v2::la_ws_transpose_v2<128, 128>(float*, int64_t, const int32_t*);
 template __global__ void v2::la_ws_transpose_v2<128, 64>(float*, int64_t, const int32_t*);
 template __global__ void v2::la_ws_transpose_v2<64, 64>(float*, int64_t, const int32_t*);

@@ -53,6 +53,7 @@ struct PrefillParams {
     int32_t* pieces;      // packed: [max_pieces][4] first token, length (-1: unused), document,
                           //         the document's first state slot (-1: none); longest first
     int32_t* slot_tab;    // packed: [state_slots][2] first token, length (0: unused)
+    const float* decay;   // decayed variant: per-head lambda in [0, 1] (device, [H]), or null
     uint64_t* marker;     // forward calls with segment states: the block loop stores `key` here
                           // (the states are complete once it runs), for a backward to reuse
     const int32_t* reuse; // backward dq pass: 1 here means the workspace already holds this
@@ -378,6 +379,30 @@ struct TileRegs {
             }
         }
     }
+    // transposed, each row (token) r scaled by lambda^(nb - 1 - r) and rows
+    // from nb on by 0 (the decayed state update's weights; l2 = log2 lambda)
+    __device__ __forceinline__ void store_cols_weighted(T* lds, int pitch, int tid, float l2, int nb) const {
+#pragma unroll
+        for (int p = 0; p < PER; ++p) {
+            const int item = tid + p * kThreads;
+            if (item < ITEMS) {
+                const int rq = item / CPR, c = item % CPR;
+                float w[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) w[i] = 4 * rq + i < nb ? decay_pow(l2, nb - 1 - (4 * rq + i)) : 0.f;
+#pragma unroll
+                for (int e = 0; e < CE; ++e) {
+                    float x[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        if constexpr (sizeof(T) == 2) x[i] = __uint_as_float(lane16(r[p][i], e) << 16) * w[i];
+                        else x[i] = __uint_as_float(lane32(r[p][i], e)) * w[i];
+                    }
+                    store4(lds + (c * CE + e) * pitch + 4 * rq, x[0], x[1], x[2], x[3]);
+                }
+            }
+        }
+    }
     // transposed: lds[col][row], 4 rows per write
     __device__ __forceinline__ void store_cols(T* lds, int pitch, int tid) const {
 #pragma unroll
@@ -421,7 +446,7 @@ __device__ __forceinline__ void state_update(f32x4_t (&kv)[KVPW], const TIn* Kt,
 // ---------------------------------------------------------------------------
 // Segment states: for every segment whose last document continues into the
 // next segment, K^T V over that document's piece of the segment.
-template <typename TIn, int D, int B, int W>
+template <typename TIn, int D, int B, int W, bool DECAY = false>
 __global__ __launch_bounds__(kThreads, 2) void la_segment_state_kernel(PrefillParams p) {
     constexpr int TP = t_pitch(B);
     constexpr int NKV = (D / 16) * (W / 16);
@@ -462,12 +487,21 @@ __global__ __launch_bounds__(kThreads, 2) void la_segment_state_kernel(PrefillPa
 
     TileRegs<TIn, B, D> lk;
     TileRegs<TIn, B, W> lv;
+    // decayed variant: the state is faded to the end of the piece, block by block
+    const float l2 = DECAY ? log2f(p.decay[h]) : 0.f;
     int nb = min(B, t_end - b0);
     lk.load(kg + ((int64_t)phys_tok(p, b0) * p.H + h) * D, ld, nb, tid);
     lv.load(vg + ((int64_t)phys_tok(p, b0) * p.H + h) * D + s * W, ld, nb, tid);
     while (nb > 0) {
         __syncthreads();
-        lk.store_cols(Kt, TP, tid);
+        if constexpr (DECAY) {
+            lk.store_cols_weighted(Kt, TP, tid, l2, nb);
+            const float f = decay_pow(l2, nb);
+#pragma unroll
+            for (int j = 0; j < KVPW; ++j) kv[j] *= f;
+        } else {
+            lk.store_cols(Kt, TP, tid);
+        }
         lv.store_cols(Vt, TP, tid);
         const int nb0 = b0 + nb;
         const int nnb = min(B, t_end - nb0);
@@ -501,10 +535,13 @@ __global__ __launch_bounds__(kThreads, 2) void la_segment_state_kernel(PrefillPa
 // spread the scan over every CU (each CU's stream of requests is the limit).
 template <int CH, int NT>
 __global__ __launch_bounds__(NT) void la_segment_scan_kernel(float* __restrict__ ws, const int32_t* __restrict__ flags,
-                                                             int nseg, int64_t entries, const int32_t* reuse) {
+                                                             int nseg, int64_t entries, const int32_t* reuse,
+                                                             const float* decay, int64_t per_head, int L) {
     if (reuse && *reuse) return;  // the workspace already holds the (transposed) prefixes
     const int64_t idx = ((int64_t)blockIdx.x * NT + threadIdx.x) * 4;
     if (idx >= entries) return;
+    // decayed variant: a carried prefix fades by lambda^L across one more segment
+    const float fL = decay ? decay_pow(log2f(decay[idx / per_head]), L) : 1.f;
     f32x4_t carry = zero4();
     for (int u0 = 0; u0 < nseg - 1; u0 += CH) {
         f32x4_t a[CH];
@@ -518,7 +555,7 @@ __global__ __launch_bounds__(NT) void la_segment_scan_kernel(float* __restrict__
 #pragma unroll
         for (int c = 0; c < CH; ++c) {
             if (f[c] & 1) {
-                carry = (f[c] & 2) ? carry + a[c] : a[c];
+                carry = (f[c] & 2) ? fL * carry + a[c] : a[c];
                 *reinterpret_cast<f32x4_t*>(ws + (int64_t)(u0 + c) * entries + idx) = carry;
             }
         }
@@ -548,7 +585,7 @@ __device__ __forceinline__ void empty_doc_states(const PrefillParams& p, int u, 
 
 // ---------------------------------------------------------------------------
 // The block loop.
-template <typename TIn, int D, int B, int W>
+template <typename TIn, int D, int B, int W, bool DECAY = false>
 __global__ __launch_bounds__(kThreads, 1) void la_prefill_main_kernel(PrefillParams p) {
     constexpr int ES = (int)sizeof(TIn);
     constexpr int CE = 16 / ES;
@@ -611,8 +648,12 @@ __global__ __launch_bounds__(kThreads, 1) void la_prefill_main_kernel(PrefillPar
 
     Cursor cur;
     cursor_first(cur, cuv, p.num_seqs, t0, t1, B);
+    // decayed variant: this head's log2 lambda
+    const float l2 = DECAY ? log2f(p.decay[h]) : 0.f;
 
-    // Initial state: zero, or the document's state at the segment start.
+    // Initial state: zero, or the document's state at the segment start
+    // (decayed: each earlier piece's state faded by the tokens between its end
+    // and this unit's start).
     f32x4_t kv[KVPW];
 #pragma unroll
     for (int j = 0; j < KVPW; ++j) kv[j] = zero4();
@@ -621,19 +662,21 @@ __global__ __launch_bounds__(kThreads, 1) void la_prefill_main_kernel(PrefillPar
         const int u_end = p.packed ? lb1 : u;
         for (int uu = u_first; uu < u_end; ++uu) {
             const float* src = p.ws + (((int64_t)uu * p.H + h) * D) * D + s * W;
+            const float f = DECAY ? decay_pow(l2, (u_end - uu - 1) * p.L) : 1.f;
 #pragma unroll
             for (int j = 0; j < KVPW; ++j) {
                 const int t = wave + kWaves * j;
                 if (t < NKV) {
                     const int a = t / NCT, c = t % NCT;
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) kv[j][r] += src[(int64_t)(16 * a + 4 * g + r) * D + 16 * c + li];
+                    for (int r = 0; r < 4; ++r) kv[j][r] += f * src[(int64_t)(16 * a + 4 * g + r) * D + 16 * c + li];
                 }
             }
         }
     }
-    // A caller-supplied state before the document's first token joins the prefix.
-    auto add_kv_in = [&](int doc) {
+    // A caller-supplied state before the document's first token joins the
+    // prefix (decayed: faded by factor f).
+    auto add_kv_in = [&](int doc, float f) {
         const float* src = p.kv_in + (((int64_t)phys_doc(p, doc) * p.H + h) * D) * D;
 #pragma unroll
         for (int j = 0; j < KVPW; ++j) {
@@ -644,12 +687,12 @@ __global__ __launch_bounds__(kThreads, 1) void la_prefill_main_kernel(PrefillPar
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int row = 16 * a + 4 * g + r;
-                    kv[j][r] += p.kv_in_t ? src[(int64_t)col * D + row] : src[(int64_t)row * D + col];
+                    kv[j][r] += f * (p.kv_in_t ? src[(int64_t)col * D + row] : src[(int64_t)row * D + col]);
                 }
             }
         }
     };
-    if (p.kv_in && cur.nb > 0) add_kv_in(cur.doc);
+    if (p.kv_in && cur.nb > 0) add_kv_in(cur.doc, DECAY ? decay_pow(l2, t0 - cuv[cur.doc]) : 1.f);
     __syncthreads();  // LDS zeroed before the state copy below
 #pragma unroll
     for (int j = 0; j < KVPW; ++j) {
@@ -679,7 +722,8 @@ __global__ __launch_bounds__(kThreads, 1) void la_prefill_main_kernel(PrefillPar
                 *reinterpret_cast<uint4*>(Ks + row * QP + D + c * CE) = make_uint4(0u, 0u, 0u, 0u);
             }
         }
-        lk.store_cols(Kt, TP, tid);
+        if constexpr (DECAY) lk.store_cols_weighted(Kt, TP, tid, l2, cur.nb);  // (Kt feeds only the state update)
+        else lk.store_cols(Kt, TP, tid);
         lv.store_cols(Vt, TP, tid);
         Cursor nxt = cur;
         cursor_next(nxt, cuv, p.num_seqs, t1, B);
@@ -716,7 +760,13 @@ __global__ __launch_bounds__(kThreads, 1) void la_prefill_main_kernel(PrefillPar
                 load_frag(fb, Qs + (16 * b + li) * QP + 32 * m, g);
                 mma(acc, fa, fb);
             }
-            if (a == b) {
+            if constexpr (DECAY) {  // lambda^(query - key), 0 above the diagonal
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int m = (16 * b + li) - (16 * a + 4 * g + r);
+                    acc[r] = m >= 0 ? acc[r] * decay_pow(l2, m) : 0.f;
+                }
+            } else if (a == b) {
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
                     if (4 * g + r > li) acc[r] = 0.f;
@@ -736,16 +786,27 @@ __global__ __launch_bounds__(kThreads, 1) void la_prefill_main_kernel(PrefillPar
                 load_frag(fb, Ps + (16 * b + li) * TP + 32 * kc, g);
                 mma(acc, fa, fb);
             }
+            // inter product; decayed: in its own accumulator, then faded by
+            // lambda^(query + 1) for query row 16 b + li
+            f32x4_t acce = zero4();
+            f32x4_t& ae = DECAY ? acce : acc;
 #pragma unroll
             for (int m = 0; m < DK / 32; ++m) {
                 Frag<TIn> fa, fb;
                 load_frag(fa, KVt + (16 * c + li) * KP + 32 * m, g);
                 load_frag(fb, Qs + (16 * b + li) * QP + 32 * m, g);
-                mma(acc, fa, fb);
+                mma(ae, fa, fb);
             }
+            if constexpr (DECAY) acc += decay_pow(l2, 16 * b + li + 1) * acce;
             store4(Os + (16 * b + li) * OP + 16 * c + 4 * g, acc[0], acc[1], acc[2], acc[3]);
         }
-        // State update after the inter product used the old state.
+        // State update after the inter product used the old state (decayed:
+        // KV <- lambda^nb KV + weighted K^T V, the weights already on Kt).
+        if constexpr (DECAY) {
+            const float f = decay_pow(l2, cur.nb);
+#pragma unroll
+            for (int j = 0; j < KVPW; ++j) kv[j] *= f;
+        }
         state_update<TIn, D, B, W, KVPW>(kv, Kt, Vt, wave, li, g);
         __syncthreads();  // (D) O staged, old KVt no longer read
 
@@ -774,7 +835,7 @@ __global__ __launch_bounds__(kThreads, 1) void la_prefill_main_kernel(PrefillPar
         if (nxt.nb > 0 && nxt.first_of_doc) {
 #pragma unroll
             for (int j = 0; j < KVPW; ++j) kv[j] = zero4();
-            if (p.kv_in) add_kv_in(nxt.doc);
+            if (p.kv_in) add_kv_in(nxt.doc, 1.f);  // a document starting here starts from its state
         }
 #pragma unroll
         for (int j = 0; j < KVPW; ++j) {

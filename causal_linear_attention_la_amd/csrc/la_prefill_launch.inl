@@ -21,8 +21,9 @@ inline hipError_t launch_main(void (*kernel)(PrefillParams), dim3 grid, dim3 blo
     return hipExtLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, args, 0, st, e0, e1, 0);
 }
 
-template <typename T, int D, int B, int W>
-hipError_t run_prefill(const PrefillParams& p, int variant, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
+// The kernels of one plan, without (DK = false) or with the decay.
+template <typename T, int D, int B, int W, bool DK>
+hipError_t run_prefill_k(const PrefillParams& p, int variant, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
     if constexpr (!main_fits((int)sizeof(T), D, B, W)) {
         return hipErrorInvalidValue;
     } else {
@@ -33,22 +34,18 @@ hipError_t run_prefill(const PrefillParams& p, int variant, hipStream_t st, hipE
         bool use_v2 = false;
         if constexpr (has_v2<T, D, B, W>()) use_v2 = (variant != 1);
         if (variant == 2 && !use_v2) return hipErrorInvalidValue;
+        void (*seg_kernel)(PrefillParams) = la_segment_state_kernel<T, D, B, W, DK>;
+        if constexpr (has_v2<T, D, B, W>()) {
+            if (use_v2) seg_kernel = v2::la_segment_state_v2<D, B, W, DK>;
+        }
         if (p.packed) {
             hipError_t e = launch_kernel(la_plan_pieces_kernel<kPlanThreads>, dim3(1), dim3(kPlanThreads), st, p);
             if (e != hipSuccess) return e;
             if (p.state_slots > 0 && !p.skip_prefix) {
-                void (*seg_kernel)(PrefillParams) = la_segment_state_kernel<T, D, B, W>;
-                if constexpr (has_v2<T, D, B, W>()) {
-                    if (use_v2) seg_kernel = v2::la_segment_state_v2<D, B, W>;
-                }
                 e = launch_kernel(seg_kernel, dim3((unsigned)((int64_t)p.state_slots * p.H * p.S)), block, st, p);
                 if (e != hipSuccess) return e;
             }
         } else if (p.nseg > 1 && !p.skip_prefix) {
-            void (*seg_kernel)(PrefillParams) = la_segment_state_kernel<T, D, B, W>;
-            if constexpr (has_v2<T, D, B, W>()) {
-                if (use_v2) seg_kernel = v2::la_segment_state_v2<D, B, W>;
-            }
             hipError_t e = launch_kernel(seg_kernel, grid, block, st, p);
             if (e != hipSuccess) return e;
             if (p.scan) {
@@ -56,23 +53,35 @@ hipError_t run_prefill(const PrefillParams& p, int variant, hipStream_t st, hipE
                 const int64_t threads = entries / 4;
                 constexpr int NT = 128;
                 e = launch_kernel(la_segment_scan_kernel<32, NT>, dim3((unsigned)((threads + NT - 1) / NT)), dim3(NT),
-                                  st, p.ws, (const int32_t*)p.flags, (int)p.nseg, entries, p.reuse);
+                                  st, p.ws, (const int32_t*)p.flags, (int)p.nseg, entries, p.reuse, p.decay,
+                                  (int64_t)D * D, (int)p.L);
                 if (e != hipSuccess) return e;
             }
         }
-        void (*main_kernel)(PrefillParams) = la_prefill_main_kernel<T, D, B, W>;
+        void (*main_kernel)(PrefillParams) = la_prefill_main_kernel<T, D, B, W, DK>;
         if constexpr (has_v2<T, D, B, W>()) {
             if (use_v2) {
-                if constexpr (D == 128) {
-                    main_kernel = p.slots == 3 ? v2::la_prefill_main_v2<D, B, W, 3> : v2::la_prefill_main_v2<D, B, W, 2>;
+                if constexpr (D == 128 && DK && W == 128) {
+                    // (the decayed full-width loop has no registers for a third slot: the planner gives it two)
+                    if (p.slots == 3) return hipErrorInvalidValue;
+                    main_kernel = v2::la_prefill_main_v2<D, B, W, 2, DK>;
+                } else if constexpr (D == 128) {
+                    main_kernel = p.slots == 3 ? v2::la_prefill_main_v2<D, B, W, 3, DK>
+                                               : v2::la_prefill_main_v2<D, B, W, 2, DK>;
                 } else {
                     if (p.slots == 3) return hipErrorInvalidValue;
-                    main_kernel = v2::la_prefill_main_v2<D, B, W, 2>;
+                    main_kernel = v2::la_prefill_main_v2<D, B, W, 2, DK>;
                 }
             }
         }
         return launch_main(main_kernel, grid, block, p, st, e0, e1);
     }
+}
+
+template <typename T, int D, int B, int W>
+hipError_t run_prefill(const PrefillParams& p, int variant, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
+    return p.decay ? run_prefill_k<T, D, B, W, true>(p, variant, st, e0, e1)
+                   : run_prefill_k<T, D, B, W, false>(p, variant, st, e0, e1);
 }
 
 template <typename T, int D, int B>

@@ -209,12 +209,22 @@ struct Geo {
 };
 
 // KV[:, own cols] += K^T V over one block; keeps the V^T fragments (A operands
-// of the intra product).
-template <int D, int B, int W, int NA, int NC, int NK>
+// of the intra product).  Decayed variant (DK, l2 = log2 lambda, nb tokens in
+// the block): KV <- lambda^nb KV + sum_c lambda^(nb - 1 - c) k_c^T v_c, the
+// weights applied to a bf16 copy of the V^T fragments (lane group g holds
+// tokens 32 kc + 8 g + e of each chunk); the kept fragments stay unscaled.
+template <int D, int B, int W, bool DK = false, int NA, int NC, int NK>
 __device__ __forceinline__ void state_update(f32x4_t (&kv)[NA][NC], Frag<bf16_t> (&vfr)[NC][NK], const bf16_t* Ks,
-                                             const bf16_t* Vs, int col0, int lane) {
+                                             const bf16_t* Vs, int col0, int lane, float l2 = 0.f, int nb = B) {
     using G = Geo<D, B, W>;
     static_assert(NA == G::NDT && NC == G::NCW && NK == B / 32, "tile counts");
+    if constexpr (DK) {
+        const float f = decay_pow(l2, nb);
+#pragma unroll
+        for (int a = 0; a < G::NDT; ++a)
+#pragma unroll
+            for (int c = 0; c < G::NCW; ++c) kv[a][c] *= f;
+    }
 #pragma unroll
     for (int kc = 0; kc < B / 32; ++kc) {
 #pragma unroll
@@ -222,12 +232,26 @@ __device__ __forceinline__ void state_update(f32x4_t (&kv)[NA][NC], Frag<bf16_t>
             if constexpr (G::NCW == 2) load_tr<W, 8>(vfr[c][kc], Vs, 32 * kc, col0, 4 * c, lane);
             else load_tr<W, 4>(vfr[c][kc], Vs, 32 * kc, col0 + 16 * c, 0, lane);
         }
+        Frag<bf16_t> vs[G::NCW];
+        if constexpr (DK) {
+            float w[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int tok = 32 * kc + 8 * (lane >> 4) + e;
+                w[e] = tok < nb ? decay_pow(l2, nb - 1 - tok) : 0.f;
+            }
+#pragma unroll
+            for (int c = 0; c < G::NCW; ++c) vs[c] = scale_frag(vfr[c][kc], w);
+        } else {
+#pragma unroll
+            for (int c = 0; c < G::NCW; ++c) vs[c] = vfr[c][kc];
+        }
 #pragma unroll
         for (int a = 0; a < G::NDT; ++a) {
             Frag<bf16_t> kf;
             load_tr<D, 8>(kf, Ks, 32 * kc, 32 * (a >> 1), 4 * (a & 1), lane);
 #pragma unroll
-            for (int c = 0; c < G::NCW; ++c) mma(kv[a][c], kf, vfr[c][kc]);
+            for (int c = 0; c < G::NCW; ++c) mma(kv[a][c], kf, vs[c]);
         }
     }
 }
@@ -237,15 +261,18 @@ __device__ __forceinline__ void state_update(f32x4_t (&kv)[NA][NC], Frag<bf16_t>
 // 4 consecutive wave blocks of D * W / 4 floats, each [tile a][tile c][lane]
 // of 4-float runs -- 16-byte, fully coalesced loads and stores.  (The scan
 // kernel adds states entry by entry and does not care about the order.)
-template <int D, int B, int W, int NA, int NC>
-__device__ __forceinline__ void load_ws(f32x4_t (&kv)[NA][NC], const float* src, int lane) {
+template <int D, int B, int W, bool DK = false, int NA, int NC>
+__device__ __forceinline__ void load_ws(f32x4_t (&kv)[NA][NC], const float* src, int lane, float f = 1.f) {
     using G = Geo<D, B, W>;
     static_assert(NA == G::NDT && NC == G::NCW, "tile counts");
     const f32x4_t* s4 = reinterpret_cast<const f32x4_t*>(src);
 #pragma unroll
     for (int a = 0; a < G::NDT; ++a)
 #pragma unroll
-        for (int c = 0; c < G::NCW; ++c) kv[a][c] += s4[(a * G::NCW + c) * 64 + lane];
+        for (int c = 0; c < G::NCW; ++c) {
+            if constexpr (DK) kv[a][c] += f * s4[(a * G::NCW + c) * 64 + lane];
+            else kv[a][c] += s4[(a * G::NCW + c) * 64 + lane];
+        }
 }
 
 template <int D, int B, int W, int NA, int NC>
@@ -270,7 +297,7 @@ __device__ __forceinline__ int64_t ws_offset(const PrefillParams& p, int u, int 
 // matrix, col0 = the first value column this wave owns.
 template <int D, int B, int W, int NA, int NC>
 __device__ __forceinline__ void add_state(f32x4_t (&kv)[NA][NC], const float* base, int col0, int transposed, int g,
-                                          int li) {
+                                          int li, float f = 1.f) {
     using G = Geo<D, B, W>;
     static_assert(NA == G::NDT && NC == G::NCW, "tile counts");
 #pragma unroll
@@ -280,7 +307,7 @@ __device__ __forceinline__ void add_state(f32x4_t (&kv)[NA][NC], const float* ba
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int64_t i = state_row(a, g, r), j = col0 + state_col<NC>(c, li);
-                kv[a][c][r] += transposed ? base[j * D + i] : base[i * D + j];
+                kv[a][c][r] += f * (transposed ? base[j * D + i] : base[i * D + j]);
             }
 }
 
@@ -299,7 +326,7 @@ __device__ __forceinline__ void store_state(const f32x4_t (&kv)[NA][NC], float* 
 // ---------------------------------------------------------------------------
 // Segment states (see la_segment_state_kernel): K^T V of each segment's last
 // document piece when that document continues into the next segment.
-template <int D, int B, int W>
+template <int D, int B, int W, bool DK = false>
 __global__ __launch_bounds__(kThreads, 1) void la_segment_state_v2(PrefillParams p) {
     using G = Geo<D, B, W>;
     // Two slots of two blocks each, one LDS variable per tile; the loads of
@@ -338,6 +365,8 @@ __global__ __launch_bounds__(kThreads, 1) void la_segment_state_v2(PrefillParams
     const bf16_t* vg = static_cast<const bf16_t*>(p.v);
     const uint32_t row_bytes = (uint32_t)(p.H * D * 2);
     const int col0 = wave * G::CW;
+    // decayed variant: the state is faded to the end of the piece
+    const float l2 = DK ? log2f(p.decay[h]) : 0.f;
     DmaTile<D> dk;
     DmaTile<W> dv;
     dk.init(wave, lane, row_bytes);
@@ -383,9 +412,12 @@ __global__ __launch_bounds__(kThreads, 1) void la_segment_state_v2(PrefillParams
         if (i > 0) {
             vm_wait<LP>();  // pair i - 1 is in (pair i may still be in flight) ...
             lds_barrier();  // ... for every wave
-            state_update<D, B, W>(kv, vfr, kbuf(Slot<1 - SLOT>{}), vbuf(Slot<1 - SLOT>{}), col0, lane);
-            state_update<D, B, W>(kv, vfr, kbuf(Slot<1 - SLOT>{}) + B * D, vbuf(Slot<1 - SLOT>{}) + B * W, col0,
-                                  lane);
+            // tokens in the two blocks of pair i - 1 (0 past the end)
+            const int b0 = first + 2 * (i - 1) * B;
+            const int nb0 = max(0, min(B, t_end - b0)), nb1 = max(0, min(B, t_end - b0 - B));
+            state_update<D, B, W, DK>(kv, vfr, kbuf(Slot<1 - SLOT>{}), vbuf(Slot<1 - SLOT>{}), col0, lane, l2, nb0);
+            state_update<D, B, W, DK>(kv, vfr, kbuf(Slot<1 - SLOT>{}) + B * D, vbuf(Slot<1 - SLOT>{}) + B * W, col0,
+                                      lane, l2, nb1);
         }
         ++i;
     };
@@ -455,7 +487,7 @@ __global__ __launch_bounds__(kThreads) void la_ws_transpose_v2(float* __restrict
 // load has a whole iteration more to arrive and twice the bytes are in flight
 // per CU -- what a 4-wave workgroup needs to keep HBM busy.  (On short
 // segments the deeper start costs more than it hides.)
-template <int D, int B, int W, int NS>
+template <int D, int B, int W, int NS, bool DK = false>
 __global__ __launch_bounds__(kThreads, 1) void la_prefill_main_v2(PrefillParams p) {
     using G = Geo<D, B, W>;
     constexpr int NQT = G::NQT, NCW = G::NCW, NDT = G::NDT;
@@ -533,6 +565,24 @@ __global__ __launch_bounds__(kThreads, 1) void la_prefill_main_v2(PrefillParams 
     const CuView cuv = cu_view(p);
     Cursor c0;
     cursor_first(c0, cuv, p.num_seqs, t0, t1, B);
+
+    // Decayed variant: this head's log2 lambda and the per-lane factors that
+    // do not change from block to block: lambda^(query - key) on the scores
+    // (0 above the diagonal: the causal mask), lambda^(query + 1) on the inter
+    // product of query row 16 b + li.
+    float l2 = 0.f, sfac[DK ? NQT : 1][4], ifac[DK ? NQT : 1];
+    if constexpr (DK) {
+        l2 = log2f(p.decay[h]);
+#pragma unroll
+        for (int b = 0; b < NQT; ++b) {
+            ifac[b] = decay_pow(l2, 16 * b + li + 1);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int m = (16 * b + li) - (16 * wave + 4 * g + r);
+                sfac[b][r] = m >= 0 ? decay_pow(l2, m) : 0.f;
+            }
+        }
+    }
 
     f32x4_t kv[NDT][NCW];
 #pragma unroll
@@ -670,13 +720,17 @@ __global__ __launch_bounds__(kThreads, 1) void la_prefill_main_v2(PrefillParams 
     if (c0.nb > 0 && !c0.first_of_doc) {
         const int u_first = p.packed ? lb0 : p.scan ? u - 1 : cuv[c0.doc] / p.L;
         const int u_end = p.packed ? lb1 : u;
-        for (int uu = u_first; uu < u_end; ++uu)
-            load_ws<D, B, W>(kv, p.ws + ws_offset<D, W>(p, uu, h, s, wave), lane);
+        for (int uu = u_first; uu < u_end; ++uu) {
+            // (decayed: slot uu ends (u_end - uu - 1) L tokens before this unit starts)
+            load_ws<D, B, W, DK>(kv, p.ws + ws_offset<D, W>(p, uu, h, s, wave), lane,
+                                 DK ? decay_pow(l2, (u_end - uu - 1) * p.L) : 1.f);
+        }
     }
     // a caller-supplied state before the document's first token joins the prefix
+    // (decayed: faded by the tokens between the document start and this unit's)
     if (p.kv_in && c0.nb > 0)
         add_state<D, B, W>(kv, p.kv_in + (((int64_t)phys_doc(p, c0.doc) * p.H + h) * D) * D, s * W + col0, p.kv_in_t,
-                           g, li);
+                           g, li, DK ? decay_pow(l2, t0 - cuv[c0.doc]) : 1.f);
     int pb0 = t0, pnb = 0;
     int j = 0;
     // One block (j); its tiles sit in slot SLOT.  This iteration loads block
@@ -757,20 +811,29 @@ __global__ __launch_bounds__(kThreads, 1) void la_prefill_main_v2(PrefillParams 
                 }
             }
         }
+        // decayed: the state reaches query row r faded r + 1 times
+        if constexpr (DK) {
+#pragma unroll
+            for (int b = 0; b < NQT; ++b)
+#pragma unroll
+                for (int c = 0; c < NCW; ++c) oacc[b][c] *= ifac[b];
+        }
         issue_tile(cf, Slot<FILL>{}, Slot<2>{});
         // block j-1's rows leave after this iteration's loads: the next
         // iteration's wait for those loads lets these stores stay in flight
         if constexpr (LATE) finish_store(pb0, pnb);
         // state: KV += K^T V (after the inter product read it)
-        state_update<D, B, W>(kv, vfr, Ks, Vs, col0, lane);
+        state_update<D, B, W, DK>(kv, vfr, Ks, Vs, col0, lane, l2, c0.nb);
 
         // P[query][key] for keys of band w: causal mask (key <= query), the
         // tiles above the diagonal come out as zeros
 #pragma unroll
         for (int b = 0; b < NQT; ++b) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-                if (16 * wave + 4 * g + r > 16 * b + li) sacc[b][r] = 0.f;
+            for (int r = 0; r < 4; ++r) {
+                if constexpr (DK) sacc[b][r] *= sfac[b][r];  // lambda^(query - key), 0 above the diagonal
+                else if (16 * wave + 4 * g + r > 16 * b + li) sacc[b][r] = 0.f;
+            }
             store4(Ps + soff<PP>(16 * b + li, 16 * wave + 4 * g), sacc[b][0], sacc[b][1], sacc[b][2], sacc[b][3]);
         }
 

@@ -9,8 +9,9 @@
  * (qingkelab), §2.2 线性注意力 -- the right-product trick with a recursively
  * updated key-value product; Q, K, V are tiled along the sequence into blocks,
  * with a left product inside each block and a right product across blocks.
- * There is no scale, feature map, normaliser or decay (the pages define none);
- * the causal mask includes the current token.
+ * There is no scale, feature map or normaliser (the pages define none); the
+ * causal mask includes the current token.  A decay is named on the pages but
+ * not defined: la_prefill_decay / la_decode_decay take one reading of it.
  *
  * Layouts
  *   q, k, v, o : token-major packed [T, H, d]; element (t, h, i) at (t*H + h)*d + i.
@@ -262,6 +263,41 @@ la_status la_prefill_backward(const void* q, const void* k, const void* v, const
                               const float* kv_state_in, const float* dkv_state_out, void* dq, void* dk, void* dv,
                               float* dkv_state_in, int32_t num_seqs, int64_t total_tokens, la_dtype dtype,
                               void* workspace, size_t workspace_bytes, void* stream, const la_prefill_opts* opts);
+
+/* Decayed variant: the same prefill with each head's state fading by a factor
+ * lambda_h before every token's update.  "MiniMax-01技术报告解读" §3.3 item 1
+ * (批处理内核融合) lists a decay-value computation (衰减值计算) among the fused
+ * prefill steps but never defines it; the reading taken here keeps the
+ * recurrence, per document and head h:
+ *     S_t = lambda_h S_{t-1} + k_t^T v_t ,   o_t = q_t . S_t
+ *     i.e. o_t = sum_{s <= t} lambda_h^(t - s) (q_t . k_s) v_s  (+ lambda_h^(t+1-t0) q_t . kv_in)
+ * with S = kv_state_in (or zero) before the document's first token t0;
+ * lambda_h = 1 is la_prefill_resume's operation.  Blockwise: the intra-block
+ * scores carry lambda^(query - key), the inter-block product lambda^(row + 1),
+ * and KV <- lambda^nb KV + sum_c lambda^(nb - 1 - c) k_c^T v_c (the weights on
+ * a bf16 copy of V for bf16 inputs); segment states are faded across the
+ * segments between them.
+ *
+ *   decay       fp32 [H] in DEVICE memory, 4-byte aligned: lambda_h in [0, 1]
+ *               (a precondition: the values are not checked).  Must not overlap
+ *               o, kv_state_out or the workspace.  NULL: LA_ERR_INVALID_ARG.
+ *   Everything else as in la_prefill_resume (opts may be NULL; its
+ *   forward_states is ignored).  The workspace size is
+ *   la_prefill_workspace_size_ex's for the same shapes and opts; on the
+ *   full-width d = 128 loop the decayed call uses two tile slots (an explicit
+ *   slots = 3 there returns LA_ERR_UNSUPPORTED).  There is no decayed backward.
+ */
+la_status la_prefill_decay(const void* q, const void* k, const void* v, void* o, const int32_t* cu_seqlens,
+                           int32_t H, int32_t d, int32_t block, const float* decay, const float* kv_state_in,
+                           float* kv_state_out, int32_t num_seqs, int64_t total_tokens, la_dtype dtype,
+                           void* workspace, size_t workspace_bytes, void* stream, const la_prefill_opts* opts);
+
+/* Decayed decode step (the reading above), per (seq, head):
+ *     KV <- lambda_h KV + k^T v ;   o = q . KV
+ * decay: fp32 [H], device, 4-byte aligned, lambda_h in [0, 1], overlapping
+ * neither kv_state_inout nor o.  Otherwise as la_decode. */
+la_status la_decode_decay(const void* q, const void* k, const void* v, const float* decay, float* kv_state_inout,
+                          void* o, int32_t num_seqs, int32_t H, int32_t d, la_dtype dtype, void* stream);
 
 #ifdef __cplusplus
 }

@@ -118,6 +118,32 @@ def test_bench_stream_rejects(lib, args):
     assert la.la_bench_stream(mode, vp(a), vp(b), vp(c), vp(dst), n, wgs, nt, None) == la.LA_ERR_INVALID_ARG
 
 
+def test_decay_entry_points_reject(lib):
+    """The decayed prefill and decode refuse a missing, misaligned or
+    overlapping factor array on the host, and otherwise validate as the plain calls."""
+    vp = ctypes.c_void_p
+
+    def pre(decay, o=4 * G, kv=6 * G, d=128):
+        return la.la_prefill_decay(vp(G), vp(2 * G), vp(3 * G), vp(o), vp(5 * G), 8, d, 64, vp(decay) if decay else None,
+                                   None, vp(kv), 1, 8192, la.LA_BF16, vp(7 * G), 1 << 30, None, None)
+
+    assert pre(0) == la.LA_ERR_INVALID_ARG
+    assert pre(9 * G + 2) == la.LA_ERR_INVALID_ARG            # misaligned
+    assert pre(4 * G + 64) == la.LA_ERR_INVALID_ARG           # inside o
+    assert pre(6 * G + 64) == la.LA_ERR_INVALID_ARG           # inside the final states
+    assert pre(7 * G + 512) == la.LA_ERR_INVALID_ARG          # inside the workspace
+    assert pre(9 * G, d=48) == la.LA_ERR_UNSUPPORTED          # the plain call's checks follow
+
+    def dec(decay, S=6 * G, o=4 * G):
+        return la.la_decode_decay(vp(G), vp(2 * G), vp(3 * G), vp(decay) if decay else None, vp(S), vp(o), 256, 64,
+                                  128, la.LA_BF16, None)
+
+    assert dec(0) == la.LA_ERR_INVALID_ARG
+    assert dec(9 * G + 1) == la.LA_ERR_INVALID_ARG
+    assert dec(6 * G + 4096) == la.LA_ERR_INVALID_ARG         # inside the state
+    assert dec(4 * G + 16) == la.LA_ERR_INVALID_ARG           # inside o
+
+
 def test_noalloc_refuses_plans_beyond_its_array(lib):
     """la_prefill_noalloc refuses, on the host and before any device call, a
     plan whose workspace exceeds the library's static 32 MiB array."""
