@@ -23,11 +23,12 @@ contiguous HBM streams written here (include/la_bench.h) timed in the same
 run, 3 reads + 1 write for prefill and 1 read + 1 write for decode.
 
 Reported beside the headline, in the same line: the packed-document and 8k
-prefill workloads (`workloads`), the prefill's backward and a forward +
-backward training step on the headline workload (`backward`), the decode
-workload (256 sequences x 64 heads, fp32 state, 1000 steps, `decode`), and
-`cpu_baseline`: the fp64 oracle (recurrent form) on the host cores over a
-bounded sample of the headline workload.
+prefill workloads (`workloads`), the headline workload at block 128 and with
+the decayed variant (`long_1m_block128`, `decay`), the prefill's backward and a
+forward + backward training step on the headline workload (`backward`), the
+decode workload (256 sequences x 64 heads, fp32 state, 1000 steps, `decode`,
+with its decayed step), and `cpu_baseline`: the fp64 oracle (recurrent form)
+on the host cores over a bounded sample of the headline workload.
 """
 from __future__ import annotations
 
@@ -147,7 +148,7 @@ def cpu_model() -> str:
 
 def stream_ceilings(la, torch, hip) -> dict:
     """Bandwidth (GB/s of bytes read + written) of the contiguous streams in
-    la_bench_stream over 1 GiB per source: the best of 256 and 512
+    la_bench_stream over 1 GiB per source: the best of 128 to 1024
     workgroups, plain and non-temporal accesses, two rounds of 20 passes."""
     lib = la.load()
     bufs = [torch.empty(GIB, dtype=torch.uint8, device="cuda").fill_(i + 1) for i in range(4)]
@@ -157,7 +158,7 @@ def stream_ceilings(la, torch, hip) -> dict:
     for mode, name, nbytes in ((0, "copy_1r1w", 2 * GIB), (1, "stream_3r1w", 4 * GIB)):
         best, how = 0.0, None
         for _ in range(2):
-            for wgs in (256, 512):
+            for wgs in (128, 256, 512, 1024):
                 for nt in (0, 1):
                     def fn():
                         st = lib.la_bench_stream(mode, P(bufs[0]), P(bufs[1]), P(bufs[2]), P(bufs[3]), GIB, wgs, nt,
@@ -296,12 +297,12 @@ def bench_prefill(name, args, la, torch, hip, steps: int, warmup: int, graph: bo
         "graph_replay_value": graph_value,
     }
     rec["roofline"]["whole_call_frac"] = rec["whole_call"]["frac"]
-    # outputs of the seeded input set, for the error against the oracle
+    # outputs of the seeded input set, for the error against the oracle (copies:
+    # later measurements reuse these buffers)
     step(0)
     torch.cuda.synchronize()
-    o0 = sets[0][3]
-    w["gpu_o"] = o0
-    w["gpu_kv"] = kv
+    w["gpu_o"] = sets[0][3].clone()
+    w["gpu_kv"] = kv.clone()
     if keep_sets:
         w["dev_sets"] = sets
     return rec, w
@@ -333,6 +334,39 @@ def bench_block(la, torch, hip, w, block: int, steps: int) -> dict:
     return {"workload": w["name"], "block": block, "value": T * H / s, "unit": "token·heads/s",
             "gpu_ms_per_step": s * 1e3, "steps": steps,
             "plan": {k2: plan[k2] for k2 in ("seg_len", "value_slices", "num_segments", "scan", "variant", "units")},
+            "block_loop": {"kernel": MAIN_KERNEL[plan["variant"]], "kernel_ms": kms,
+                           "frac": algo / (kms / 1e3) / 1e9 / HBM_PEAK_GBS},
+            "whole_call_frac": T * H / s / roof_th}
+
+
+def bench_decay(la, torch, hip, w, steps: int) -> dict:
+    """The decayed variant (la_prefill_decay) on the same workload and device
+    inputs, per-head factors lambda_h = 1 - 2^-(5 + h): whole call and the
+    block-loop kernel (events)."""
+    T, H, d = w["T"], w["H"], w["d"]
+    num_seqs = len(w["cu"]) - 1
+    dt = la.LA_BF16 if w["dtype"] == "bf16" else la.LA_FP32
+    plan = la.la_prefill_plan(T, num_seqs, H, d, 64, dt)
+    q, k, v, o = w["dev_sets"][0]
+    cu = torch.from_numpy(w["cu"]).cuda()
+    kv = torch.empty((num_seqs, H, d, d), dtype=torch.float32, device="cuda")
+    ws = torch.empty(max(plan["workspace_bytes"], 256), dtype=torch.uint8, device="cuda")
+    lam = torch.tensor([1.0 - 2.0 ** -(5 + h) for h in range(H)], dtype=torch.float32, device="cuda")
+    call = lambda a=None, b=None: la.prefill(q, k, v, cu, block=64, out=o, kv_state_out=kv, workspace=ws, decay=lam,
+                                             begin_event=a, end_event=b)
+    s = gpu_time(torch, hip, call, steps)
+    evs = [(hip.event(), hip.event()) for _ in range(steps)]
+    for a, b in evs:
+        call(a, b)
+    torch.cuda.synchronize()
+    kms = float(np.mean([hip.elapsed_ms(a, b) for a, b in evs]))
+    for a, b in evs:
+        hip.destroy(a)
+        hip.destroy(b)
+    algo = T * H * 8 * d
+    roof_th = HBM_PEAK_GBS * 1e9 / (8 * d)
+    return {"workload": w["name"], "lambda": "1 - 2^-(5 + h)", "value": T * H / s, "unit": "token·heads/s",
+            "gpu_ms_per_step": s * 1e3, "steps": steps,
             "block_loop": {"kernel": MAIN_KERNEL[plan["variant"]], "kernel_ms": kms,
                            "frac": algo / (kms / 1e3) / 1e9 / HBM_PEAK_GBS},
             "whole_call_frac": T * H / s / roof_th}
@@ -441,13 +475,24 @@ def bench_decode(args, la, torch, hip):
     hip.destroy(e1)
     bytes_step = ns * H * (2 * d * d * 4 + 4 * d * 2)
     achieved = bytes_step * steps / gpu_s / 1e9
+    # the decayed step (la_decode_decay), per-head factors 1 - 2^-(5 + h mod 8)
+    lam = torch.tensor([1.0 - 2.0 ** -(5 + h % 8) for h in range(H)], dtype=torch.float32, device="cuda")
+    it = [0]
+
+    def dstep():
+        la.decode(*sets[it[0] % pool], S, out=o, decay=lam)
+        it[0] += 1
+
+    dec_s = gpu_time(torch, hip, dstep, 200)
     del S, sets, o
     torch.cuda.empty_cache()
     return {"workload": "decode_256x64", "value": steps / wall, "unit": "steps/s", "steps": steps,
             "ms_per_step": wall / steps * 1e3, "gpu_ms_per_step": gpu_s / steps * 1e3,
             "roofline": {"bound": "hbm", "kernel": "la_decode_kernel", "achieved": achieved, "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "bytes_per_step": bytes_step,
-                         "kernel_sources_sha": sources_sha(DECODE_SOURCES)}}
+                         "kernel_sources_sha": sources_sha(DECODE_SOURCES)},
+            "decay": {"gpu_ms_per_step": dec_s * 1e3, "value": 1.0 / dec_s, "unit": "steps/s", "steps": 200,
+                      "frac": bytes_step / dec_s / 1e9 / HBM_PEAK_GBS}}
 
 
 # -------------------------------------------------------------- CPU baseline
@@ -628,6 +673,8 @@ def main():
     }
     if args.workload == "long_1m" and not args.no_extra and not args.block:
         rec["long_1m_block128"] = bench_block(la, torch, hip, w, 128, 3)
+    if not args.no_extra and not args.block and w["dtype"] == "bf16":
+        rec["decay"] = bench_decay(la, torch, hip, w, max(3, args.steps // 2))
     if not args.no_backward:
         rec["backward"] = bench_backward(args, la, torch, hip, w, w.pop("dev_sets"), max(2, args.steps // 4))
         with_ceiling(rec["backward"]["roofline"], prefill_ceiling)

@@ -306,6 +306,7 @@ static la_status decode_impl(const void* q, const void* k, const void* v, const 
     p.pairs = (int64_t)num_seqs * H;
     p.decay = decay;
     p.H = H;
+    p.unit = 1.0f;
     hipError_t e = la::launch_decode(p, d, (int)dtype, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? LA_OK : LA_ERR_HIP;
 }

@@ -21,6 +21,7 @@ struct DecodeParams {
     int64_t pairs;
     const float* decay;  // decayed variant: per-head lambda (device, [H]), or null
     int32_t H;
+    float unit;          // 1.0f: the plain step's factor (see the kernel)
 };
 
 // One workgroup per pair.  Thread t owns 4 consecutive value columns
@@ -51,7 +52,11 @@ __global__ __launch_bounds__(kThreads) void la_decode_kernel(DecodeParams p) {
     const float v0 = to_f32(vg[4 * cq + 0]), v1 = to_f32(vg[4 * cq + 1]);
     const float v2 = to_f32(vg[4 * cq + 2]), v3 = to_f32(vg[4 * cq + 3]);
     f32x4_t* S = reinterpret_cast<f32x4_t*>(p.S + pair * (int64_t)D * D);
-    const float lam = DK ? p.decay[pair % p.H] : 1.f;
+    // The plain step scales the state by p.unit = 1 (exact): it then has the
+    // decayed step's instruction schedule, which keeps more of the state's
+    // loads in flight behind its stores -- measured 0.368 against 0.383 ms per
+    // 256 x 64 x 128 step with the multiply left out.
+    const float lam = DK ? p.decay[pair % p.H] : p.unit;
 
     f32x4_t st[RPT];
 #pragma unroll
@@ -67,7 +72,7 @@ __global__ __launch_bounds__(kThreads) void la_decode_kernel(DecodeParams p) {
         if (i < D) {
             const float ki = ks[i], qi = qs[i];
             f32x4_t x = st[r];
-            if constexpr (DK) x *= lam;
+            x *= lam;
             x[0] = fmaf(ki, v0, x[0]);
             x[1] = fmaf(ki, v1, x[1]);
             x[2] = fmaf(ki, v2, x[2]);
