@@ -23,7 +23,8 @@ contiguous HBM streams written here (include/la_bench.h) timed in the same
 run, 3 reads + 1 write for prefill and 1 read + 1 write for decode.
 
 Reported beside the headline, in the same line: the packed-document and 8k
-prefill workloads (`workloads`), the headline workload at block 128 and with
+prefill workloads (`workloads`, the packed one also at block 128), the
+headline workload at block 128 and with
 the decayed variant (`long_1m_block128`, `decay`), the prefill's backward and a
 forward + backward training step on the headline workload (`backward`), the
 decode workload (256 sequences x 64 heads, fp32 state, 1000 steps, `decode`,
@@ -693,10 +694,13 @@ def main():
                 continue
             sm = name == "prefill_8k"
             r, wx = bench_prefill(name, args, la, torch, hip, args.small_steps if sm else args.steps, args.warmup,
-                                  graph=sm and not args.no_graph)
+                                  graph=sm and not args.no_graph, keep_sets=name == "varlen_128k")
             with_ceiling(r["roofline"], prefill_ceiling)
             r["whole_call"]["frac_of_measured_ceiling"] = r["whole_call"]["achieved"] / prefill_ceiling
+            if name == "varlen_128k" and not args.block:
+                r["block128"] = bench_block(la, torch, hip, wx, 128, 3)
             extras[name] = r
+            wx.pop("dev_sets", None)
             del wx
             torch.cuda.empty_cache()
         rec["workloads"] = extras
