@@ -386,7 +386,8 @@ def bench_backward(args, la, torch, hip, w, dev_sets, steps: int):
     q, k, v, dO read and dq, dk, dv written once, 14 d bytes per token-head
     in bf16.  Timed with one event pair on the launch stream around all calls.
     Then a training step's attention work: the forward, and the backward handed
-    the forward's workspace."""
+    the forward's workspace (of the backward's size, la_prefill_backward_workspace_size,
+    so that the backward's dv and dk passes share a launch)."""
     import la_inputs
 
     T, H, d = w["T"], w["H"], w["d"]
@@ -405,7 +406,9 @@ def bench_backward(args, la, torch, hip, w, dev_sets, steps: int):
     outs = (torch.empty_like(dout0), torch.empty_like(dout0), torch.empty_like(dout0), None)
     num_seqs = len(w["cu"]) - 1
     dt = la.LA_BF16 if w["dtype"] == "bf16" else la.LA_FP32
-    need = la.la_prefill_workspace_size_ex(T, num_seqs, H, d, block, dt, la.make_opts(**opts))
+    # the backward's workspace size: room for the transposed segment states, so
+    # the dv and dk passes share a launch (the forward uses a prefix of it)
+    need = la.la_prefill_backward_workspace_size(T, num_seqs, H, d, block, dt, la.make_opts(**opts))
     ws = torch.empty(max(need, 256), dtype=torch.uint8, device="cuda")
     it = [0]
 

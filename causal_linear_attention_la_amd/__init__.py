@@ -21,7 +21,8 @@ LA_BF16, LA_FP32 = 0, 1
 
 EXPORTED = ("la_prefill", "la_decode", "la_prefill_workspace_size", "la_status_string", "la_prefill_plan",
             "la_prefill_workspace_size_ex", "la_prefill_ex", "la_prefill_resume", "la_prefill_backward",
-            "la_bench_stream", "la_prefill_noalloc", "la_prefill_decay", "la_decode_decay")
+            "la_bench_stream", "la_prefill_noalloc", "la_prefill_decay", "la_decode_decay",
+            "la_prefill_backward_workspace_size")
 
 
 class LAError(RuntimeError):
@@ -81,6 +82,8 @@ def load():
     lib.la_prefill_workspace_size_ex.argtypes = [i64, i32, i32, i32, i32, ctypes.c_int,
                                                  ctypes.POINTER(la_prefill_opts)]
     lib.la_prefill_workspace_size_ex.restype = sz
+    lib.la_prefill_backward_workspace_size.argtypes = lib.la_prefill_workspace_size_ex.argtypes
+    lib.la_prefill_backward_workspace_size.restype = sz
     lib.la_prefill_plan.argtypes = [i64, i32, i32, i32, i32, ctypes.c_int, ctypes.POINTER(la_prefill_opts),
                                     ctypes.POINTER(la_prefill_plan_info)]
     lib.la_prefill_plan.restype = ctypes.c_int
@@ -172,6 +175,11 @@ def make_opts(seg_len: int = 0, value_slices: int = 0, force_scan: bool = False,
 def la_prefill_workspace_size_ex(total_tokens, num_seqs, H, d, block, dtype, opts=None) -> int:
     return int(load().la_prefill_workspace_size_ex(total_tokens, num_seqs, H, d, block, dtype,
                                                    ctypes.byref(opts) if opts is not None else None))
+
+
+def la_prefill_backward_workspace_size(total_tokens, num_seqs, H, d, block, dtype, opts=None) -> int:
+    return int(load().la_prefill_backward_workspace_size(total_tokens, num_seqs, H, d, block, dtype,
+                                                         ctypes.byref(opts) if opts is not None else None))
 
 
 def la_prefill_plan(total_tokens, num_seqs, H, d, block, dtype, opts=None) -> dict:
@@ -325,7 +333,10 @@ def backward(q, k, v, dout, cu_seqlens, block: int = 64, kv_state_in=None, dkv_s
     None) is dL/dkv_state_out.  out = (dq, dk, dv, dkv_in) preallocated
     (dkv_in may be None), else they are allocated.  forward_workspace: the
     workspace the forward call on the same inputs and options used, untouched
-    since; the backward then reuses (and overwrites) its segment states.
+    since; the backward then reuses (and overwrites) its segment states.  A
+    workspace of la_prefill_backward_workspace_size bytes (what is allocated
+    here when none is given) lets the dv and dk passes share a launch; one of
+    the forward's size runs them one after the other.
     Returns (dq, dk, dv, dkv_state_in or None)."""
     import torch
 
@@ -358,7 +369,8 @@ def backward(q, k, v, dout, cu_seqlens, block: int = 64, kv_state_in=None, dkv_s
     if need and (ws is None or ws.numel() * ws.element_size() < need):
         if forward_workspace is not None:
             raise ValueError("forward_workspace is smaller than this plan's workspace")
-        ws = torch.empty(need, dtype=torch.uint8, device=q.device)
+        ws = torch.empty(la_prefill_backward_workspace_size(T, num_seqs, H, d, block, dt, opts), dtype=torch.uint8,
+                         device=q.device)
     ws_bytes = ws.numel() * ws.element_size() if ws is not None else 0
     st = la_prefill_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(cu_seqlens), H, d, block, _ptr(kv_state_in),
                              _ptr(dkv_state_out), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dkv_in), num_seqs, T, dt,

@@ -68,11 +68,11 @@ char* ws_at(void* workspace, size_t off) { return static_cast<char*>(workspace) 
 // else 0, so a stamp is only ever found next to the states it names.
 // reuse: a backward's decision word (the state and scan kernels then do
 // nothing when it reads 1).
-la_status enqueue_prefill(const Plan& plan, const void* q, const void* k, const void* v, void* o, const int32_t* cu,
-                          int32_t H, int32_t d, int32_t block, const float* kv_in, int kv_in_t, float* kv_out,
-                          int rev, int32_t num_seqs, int64_t T, la_dtype dtype, void* workspace, void* stream,
-                          hipEvent_t e0, hipEvent_t e1, int skip_prefix = 0, bool stamp = false,
-                          const int32_t* reuse = nullptr, const float* decay = nullptr) {
+// The kernel parameters of one prefill pass.
+la::PrefillParams make_params(const Plan& plan, const void* q, const void* k, const void* v, void* o,
+                              const int32_t* cu, int32_t H, int32_t d, int32_t block, const float* kv_in, int kv_in_t,
+                              float* kv_out, int rev, int32_t num_seqs, int64_t T, la_dtype dtype, void* workspace,
+                              int skip_prefix, bool stamp, const int32_t* reuse, const float* decay) {
     la::PrefillParams p{};
     p.q = q;
     p.k = k;
@@ -108,10 +108,32 @@ la_status enqueue_prefill(const Plan& plan, const void* q, const void* k, const 
     p.decay = decay;
     p.units = plan.units;
     p.per_xcd = (plan.units + 7) / 8;
+    return p;
+}
+
+la_status launch(const la::PrefillParams& p, const Plan& plan, int32_t d, int32_t block, la_dtype dtype, void* stream,
+                 hipEvent_t e0 = nullptr, hipEvent_t e1 = nullptr) {
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e = dtype == LA_BF16 ? la::launch_prefill_bf16(p, d, block, plan.W, plan.variant, s, e0, e1)
                                     : la::launch_prefill_fp32(p, d, block, plan.W, plan.variant, s, e0, e1);
     return e == hipSuccess ? LA_OK : LA_ERR_HIP;
+}
+
+la_status enqueue_prefill(const Plan& plan, const void* q, const void* k, const void* v, void* o, const int32_t* cu,
+                          int32_t H, int32_t d, int32_t block, const float* kv_in, int kv_in_t, float* kv_out,
+                          int rev, int32_t num_seqs, int64_t T, la_dtype dtype, void* workspace, void* stream,
+                          hipEvent_t e0, hipEvent_t e1, int skip_prefix = 0, bool stamp = false,
+                          const int32_t* reuse = nullptr, const float* decay = nullptr) {
+    const la::PrefillParams p = make_params(plan, q, k, v, o, cu, H, d, block, kv_in, kv_in_t, kv_out, rev, num_seqs,
+                                            T, dtype, workspace, skip_prefix, stamp, reuse, decay);
+    return launch(p, plan, d, block, dtype, stream, e0, e1);
+}
+
+// Two plans that decompose the work identically (the backward's two reverse passes).
+bool same_plan(const Plan& a, const Plan& b) {
+    return a.L == b.L && a.S == b.S && a.W == b.W && a.nseg == b.nseg && a.scan == b.scan && a.variant == b.variant &&
+           a.slots == b.slots && a.units == b.units && a.packed == b.packed && a.max_pieces == b.max_pieces &&
+           a.state_slots == b.state_slots && a.ws_bytes == b.ws_bytes;
 }
 
 }  // namespace
@@ -158,6 +180,13 @@ size_t la_prefill_workspace_size_ex(int64_t total_tokens, int32_t num_seqs, int3
 size_t la_prefill_workspace_size(int64_t total_tokens, int32_t num_seqs, int32_t H, int32_t d, int32_t block,
                                  la_dtype dtype) {
     return la_prefill_workspace_size_ex(total_tokens, num_seqs, H, d, block, dtype, nullptr);
+}
+
+size_t la_prefill_backward_workspace_size(int64_t total_tokens, int32_t num_seqs, int32_t H, int32_t d, int32_t block,
+                                          la_dtype dtype, const la_prefill_opts* opts) {
+    Plan p;
+    if (la::make_plan(total_tokens, num_seqs, H, d, block, (int)dtype, opts, &p) != LA_OK) return 0;
+    return p.bwd_ws_bytes;
 }
 
 la_status la_prefill_resume(const void* q, const void* k, const void* v, void* o, const int32_t* cu_seqlens,
@@ -230,28 +259,51 @@ la_status la_prefill_backward(const void* q, const void* k, const void* v, const
         const uint64_t key = states_key(p1, q, k, v, cu_seqlens, H, d, block, num_seqs, total_tokens, dtype);
         if (la::launch_ws_claim(marker, key, dec, hs) != hipSuccess) return LA_ERR_HIP;
         float* ws = reinterpret_cast<float*>(ws_at(workspace, p1.ws_states_off));
-        if (la::launch_ws_transpose(ws, p1.states() * H, d, p1.W, dec, hs) != hipSuccess) return LA_ERR_HIP;
+        if (la::launch_ws_transpose(ws, ws, p1.states() * H, d, p1.W, dec, hs) != hipSuccess) return LA_ERR_HIP;
         decision = dec;
     }
     st = enqueue_prefill(p1, dout, v, k, dq, cu_seqlens, H, d, block, kv_state_in, 1, nullptr, 0, num_seqs,
                          total_tokens, dtype, workspace, stream, nullptr, nullptr, 0, false, decision);
     if (st != LA_OK) return st;
     // dV (and dKV_in, the reverse state after each document's first token):
-    // reverse pass with query K, key Q, value dO, from dKV_out
+    // reverse pass with query K, key Q, value dO, from dKV_out.
+    // dK: reverse pass with query V, key dO, value Q, from dKV_out^T.  Its
+    // segment states (sums of dO^T q) are the transposes of the dV pass's
+    // (sums of q^T dO) over the same segments, so they are transposed rather
+    // than computed again from Q and dO.  The two passes read the same Q and
+    // dO tiles in the same order: on the transpose-read loop, with room in the
+    // workspace for the transposed copy, their block loops run in one launch,
+    // each unit's two workgroups side by side on one XCD (la_prefill_pair_v2),
+    // and the tiles one of them loads come from L2 for the other.
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    if (dtype == LA_BF16 && p2.variant == 2 && same_plan(p2, p3) &&
+        (p3.states() == 0 || workspace_bytes >= p3.bwd_ws_bytes)) {
+        la::PrefillParams pv = make_params(p3, k, q, dout, dv, cu_seqlens, H, d, block, dkv_state_out, 0,
+                                           dkv_state_in, 1, num_seqs, total_tokens, dtype, workspace, 0, false,
+                                           nullptr, nullptr);
+        la::PrefillParams pk = make_params(p2, v, dout, q, dk, cu_seqlens, H, d, block, dkv_state_out, 1, nullptr, 1,
+                                           num_seqs, total_tokens, dtype, workspace, 1, false, nullptr, nullptr);
+        pv.prefix_only = 1;  // the dV pass's planning, state and scan kernels
+        st = launch(pv, p3, d, block, dtype, stream);
+        if (st != LA_OK) return st;
+        pv.prefix_only = 0;
+        if (p3.states() > 0) {
+            float* tstates = reinterpret_cast<float*>(ws_at(workspace, p3.ws_tstates_off));
+            if (la::launch_ws_transpose(pv.ws, tstates, p3.states() * H, d, p3.W, nullptr, hs) != hipSuccess)
+                return LA_ERR_HIP;
+            pk.ws = tstates;
+        }
+        return la::launch_prefill_pair(pv, pk, d, p3.W, p3.slots, hs) == hipSuccess ? LA_OK : LA_ERR_HIP;
+    }
     st = enqueue_prefill(p3, k, q, dout, dv, cu_seqlens, H, d, block, dkv_state_out, 0, dkv_state_in, 1, num_seqs,
                          total_tokens, dtype, workspace, stream, nullptr, nullptr);
     if (st != LA_OK) return st;
-    // dK: reverse pass with query V, key dO, value Q, from dKV_out^T.  Its
-    // segment states (sums of dO^T q) are the transposes of the dV pass's
-    // (sums of q^T dO) over the same segments: on the transpose-read loop they
-    // are transposed in place rather than computed again from Q and dO.
+    // (otherwise one after the other: the dK pass takes the dV pass's states
+    // transposed in place)
     int reuse = 0;
-    if (p2.variant == 2 && p2.states() > 0 && p2.L == p3.L && p2.S == p3.S && p2.nseg == p3.nseg &&
-        p2.scan == p3.scan && p2.packed == p3.packed) {
+    if (p2.variant == 2 && p2.states() > 0 && same_plan(p2, p3)) {
         float* ws = reinterpret_cast<float*>(static_cast<char*>(workspace) + p3.ws_states_off);
-        if (la::launch_ws_transpose(ws, p3.states() * H, d, p3.W, nullptr, static_cast<hipStream_t>(stream)) !=
-            hipSuccess)
-            return LA_ERR_HIP;
+        if (la::launch_ws_transpose(ws, ws, p3.states() * H, d, p3.W, nullptr, hs) != hipSuccess) return LA_ERR_HIP;
         reuse = 1;
     }
     return enqueue_prefill(p2, v, dout, q, dk, cu_seqlens, H, d, block, dkv_state_out, 1, nullptr, 1, num_seqs,

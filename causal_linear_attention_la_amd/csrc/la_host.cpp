@@ -204,7 +204,13 @@ la_status make_plan(int64_t T, int32_t num_seqs, int32_t H, int32_t d, int32_t b
         p.ws_bytes = p.ws_flags_off + round256((size_t)nseg * 4);
     }
     p.ws_marker_off = 0;
-    (void)kNumCUs;
+    p.bwd_ws_bytes = p.ws_bytes;
+    if (p.variant == 2 && p.states() > 0) {
+        int64_t states;
+        if (!mul_ok(p.states(), (int64_t)H * d * d, states) || !mul_ok(states, 4, states)) return LA_ERR_UNSUPPORTED;
+        p.ws_tstates_off = round256(p.ws_bytes);
+        p.bwd_ws_bytes = p.ws_tstates_off + round256((size_t)states);
+    }
     *out = p;
     return LA_OK;
 }

@@ -32,6 +32,12 @@ struct Plan {
     size_t ws_slots_off = 0;   // packed: state-slot table, 2 int32 per slot
     size_t ws_marker_off = 0;  // header at offset 0 of every workspace: 64-bit key of the forward call
                                // whose states the workspace holds (+0), a backward's reuse decision (+64)
+    // The backward runs its two reverse passes in one launch (la_prefill_pair_v2)
+    // when the workspace also holds, after ws_bytes, a transposed copy of the
+    // segment states (the second pass's): bwd_ws_bytes in all, which is
+    // ws_bytes when the plan has no segment states or no transpose-read loop.
+    size_t ws_tstates_off = 0;
+    size_t bwd_ws_bytes = 0;
     // segment states per head held in the workspace
     int64_t states() const { return packed ? state_slots : nseg - 1; }
 };

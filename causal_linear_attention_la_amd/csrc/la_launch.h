@@ -35,9 +35,15 @@ hipError_t launch_prefill_fp32(const PrefillParams& p, int D, int B, int W, int 
                                hipEvent_t ev_begin, hipEvent_t ev_end);
 hipError_t launch_decode(const DecodeParams& p, int D, int dtype, hipStream_t st);
 // Transposes the first `states` segment states of a transpose-read plan's
-// workspace in place (la_ws_transpose_v2); D, W as in that plan.  With
-// `reuse` non-null, only if *reuse is 1 when the kernel runs.
-hipError_t launch_ws_transpose(float* ws, int64_t states, int D, int W, const int32_t* reuse, hipStream_t st);
+// workspace from src into dst, which may be src itself (la_ws_transpose_v2);
+// D, W as in that plan.  With `reuse` non-null, only if *reuse is 1 when the
+// kernel runs.
+hipError_t launch_ws_transpose(const float* src, float* dst, int64_t states, int D, int W, const int32_t* reuse,
+                               hipStream_t st);
+// The block loops of two transpose-read passes with the same plan (bf16,
+// block 64; W and slots as in that plan) in one launch (la_prefill_pair_v2).
+hipError_t launch_prefill_pair(const PrefillParams& p0, const PrefillParams& p1, int D, int W, int slots,
+                               hipStream_t st);
 // Compares the workspace's stamped key with `key`, writes the result (1 or 0)
 // to *decision and clears the stamp (la_ws_claim_kernel).
 hipError_t launch_ws_claim(uint64_t* marker, uint64_t key, int32_t* decision, hipStream_t st);

@@ -47,6 +47,8 @@ struct PrefillParams {
     int32_t kv_in_t; // 1: kv_in holds transposed states ([value][key])
     int32_t slots;   // tile slots of the transpose-read block loop (2 or 3)
     int32_t skip_prefix;  // 1: ws already holds this pass's states; run only the block loop
+    int32_t prefix_only;  // host side, 1: enqueue the planning, state and scan kernels but not
+                          // the block loop (which then runs in a launch of its own)
     int32_t packed;       // 1: the work list is document pieces (pieces / slot_tab, written on the device)
     int32_t max_pieces;   // packed: entries of pieces
     int32_t state_slots;  // packed: entries of slot_tab
@@ -64,10 +66,12 @@ struct PrefillParams {
 };
 
 // The workspace's segment states are complete before the block loop runs
-// (stream order), so any of its workgroups may stamp the call's key.
-__device__ __forceinline__ void stamp_key(const PrefillParams& p) {
-    if (p.marker && blockIdx.x == 0 && threadIdx.x == 0) *p.marker = p.key;
+// (stream order), so any of its workgroups may stamp the call's key: the one
+// with (pass-local) workgroup index g = 0.
+__device__ __forceinline__ void stamp_key(const PrefillParams& p, int64_t g) {
+    if (p.marker && g == 0 && threadIdx.x == 0) *p.marker = p.key;
 }
+__device__ __forceinline__ void stamp_key(const PrefillParams& p) { stamp_key(p, blockIdx.x); }
 // In a backward pass that reuses the forward's states, the state and scan
 // kernels have nothing to do.
 __device__ __forceinline__ bool states_reused(const PrefillParams& p) { return p.reuse && *p.reuse != 0; }
@@ -134,14 +138,18 @@ __device__ __forceinline__ int doc_lower(const CuView& cu, int n, int t) {
 // slices of one (segment, head) -- which read the same Q and K rows -- share
 // that XCD's L2, and so do the segments of one head, whose block loops read
 // the same earlier segment states when they sum their prefix.
-__device__ __forceinline__ bool unit_of(const PrefillParams& p, int& u, int& h, int& s) {
-    const int64_t g = blockIdx.x;
+// g is the workgroup index within the pass (blockIdx.x, except where two
+// passes share a launch).
+__device__ __forceinline__ bool unit_of(const PrefillParams& p, int64_t g, int& u, int& h, int& s) {
     const int64_t x = (g & 7) * p.per_xcd + (g >> 3);
     if (x >= p.units) return false;
     s = (int)(x % p.S);
     u = (int)((x / p.S) % p.nseg);
     h = (int)(x / ((int64_t)p.S * p.nseg));
     return true;
+}
+__device__ __forceinline__ bool unit_of(const PrefillParams& p, int& u, int& h, int& s) {
+    return unit_of(p, blockIdx.x, u, h, s);
 }
 
 // Packed work list: workgroup g takes entry g / (H S) of the piece table,
@@ -152,8 +160,7 @@ __device__ __forceinline__ bool unit_of(const PrefillParams& p, int& u, int& h, 
 struct Piece {
     int t0, len, doc, base;
 };
-__device__ __forceinline__ bool piece_of(const PrefillParams& p, Piece& pc, int& h, int& s) {
-    const int64_t g = blockIdx.x;
+__device__ __forceinline__ bool piece_of(const PrefillParams& p, int64_t g, Piece& pc, int& h, int& s) {
     const int64_t r = g / ((int64_t)p.H * p.S);
     if (r >= p.max_pieces) return false;
     const int4 e = reinterpret_cast<const int4*>(p.pieces)[r];
@@ -165,6 +172,9 @@ __device__ __forceinline__ bool piece_of(const PrefillParams& p, Piece& pc, int&
     h = (int)((g / p.S) % p.H);
     s = (int)(g % p.S);
     return true;
+}
+__device__ __forceinline__ bool piece_of(const PrefillParams& p, Piece& pc, int& h, int& s) {
+    return piece_of(p, blockIdx.x, pc, h, s);
 }
 // Packed work list, segment-state kernels: workgroup g takes state slot
 // g / (H S) (a piece that is not its document's last), head and slice as above.

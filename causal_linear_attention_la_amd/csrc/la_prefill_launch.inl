@@ -58,6 +58,7 @@ hipError_t run_prefill_k(const PrefillParams& p, int variant, hipStream_t st, hi
                 if (e != hipSuccess) return e;
             }
         }
+        if (p.prefix_only) return hipSuccess;
         void (*main_kernel)(PrefillParams) = la_prefill_main_kernel<T, D, B, W, DK>;
         if constexpr (has_v2<T, D, B, W>()) {
             if (use_v2) {

@@ -432,16 +432,17 @@ __global__ __launch_bounds__(kThreads, 1) void la_segment_state_v2(PrefillParams
 }
 
 // ---------------------------------------------------------------------------
-// Transposes, in place, the first `states` segment states of the workspace
-// while keeping the block loop's register order: where a (segment, head)
-// entry held the state X, it then holds X^T, laid out as the block loop with
-// the same (D, W) expects a state.  The two reverse passes of the backward
+// Transposes the first `states` segment states of src into dst (the same
+// place, or another area of the workspace) while keeping the block loop's
+// register order: where a (segment, head) entry of src holds the state X, the
+// entry of dst then holds X^T, laid out as the block loop with the same (D, W)
+// expects a state.  (Each workgroup reads its whole entry before it writes.)  The two reverse passes of the backward
 // sum transposed states over the same segments (q^T dO and dO^T q), so one
 // pass's prefix states serve the other.  One workgroup per entry: the D x D
 // state goes through LDS as a plain matrix (rows padded by 4 floats, so the
 // 16-byte column reads are conflict free).
 template <int D, int W>
-__global__ __launch_bounds__(kThreads) void la_ws_transpose_v2(float* __restrict__ ws, int64_t states,
+__global__ __launch_bounds__(kThreads) void la_ws_transpose_v2(const float* src, float* dst, int64_t states,
                                                                 const int32_t* reuse) {
     constexpr int NCW = W / 64;  // 16-column tiles per block-loop wave (W / 4 columns)
     constexpr int PITCH = D + 4;
@@ -449,7 +450,8 @@ __global__ __launch_bounds__(kThreads) void la_ws_transpose_v2(float* __restrict
     __shared__ __align__(16) float M[D * PITCH];
     if ((int64_t)blockIdx.x >= states) return;
     if (reuse && !*reuse) return;  // the states were not the forward's: they are computed instead
-    f32x4_t* base = reinterpret_cast<f32x4_t*>(ws + (int64_t)blockIdx.x * D * D);
+    const f32x4_t* base = reinterpret_cast<const f32x4_t*>(src + (int64_t)blockIdx.x * D * D);
+    f32x4_t* out = reinterpret_cast<f32x4_t*>(dst + (int64_t)blockIdx.x * D * D);
     // entry e holds rows i0 .. i0 + 3 of column j (store_ws's order)
     auto place = [](int e, int& i0, int& j) {
         const int s = e / PER_SLICE, w = (e % PER_SLICE) / PER_WAVE, q = e % PER_WAVE;
@@ -477,7 +479,7 @@ __global__ __launch_bounds__(kThreads) void la_ws_transpose_v2(float* __restrict
         const int e = threadIdx.x + k * kThreads;
         int i0, j;
         place(e, i0, j);
-        base[e] = *reinterpret_cast<const f32x4_t*>(M + j * PITCH + i0);  // (X^T)[i0 + r][j] = X[j][i0 + r]
+        out[e] = *reinterpret_cast<const f32x4_t*>(M + j * PITCH + i0);  // (X^T)[i0 + r][j] = X[j][i0 + r]
     }
 }
 
@@ -487,8 +489,11 @@ __global__ __launch_bounds__(kThreads) void la_ws_transpose_v2(float* __restrict
 // load has a whole iteration more to arrive and twice the bytes are in flight
 // per CU -- what a 4-wave workgroup needs to keep HBM busy.  (On short
 // segments the deeper start costs more than it hides.)
+//
+// The body runs the unit of pass-local workgroup index wg (blockIdx.x, except
+// in la_prefill_pair_v2 below).
 template <int D, int B, int W, int NS, bool DK = false>
-__global__ __launch_bounds__(kThreads, 1) void la_prefill_main_v2(PrefillParams p) {
+__device__ __forceinline__ void main_v2(const PrefillParams& p, const int64_t wg) {
     using G = Geo<D, B, W>;
     constexpr int NQT = G::NQT, NCW = G::NCW, NDT = G::NDT;
     static_assert(NQT == kWaves, "wave w takes key band w");
@@ -529,14 +534,14 @@ __global__ __launch_bounds__(kThreads, 1) void la_prefill_main_v2(PrefillParams 
         else return V2;
     };
 
-    stamp_key(p);
+    stamp_key(p, wg);
     int u = 0, h, s, t0, t1;
     int lb0 = 0, lb1 = 0;  // packed: state slots of the document's earlier pieces
     const int tid = threadIdx.x, lane = tid & 63, li = lane & 15, g = lane >> 4;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: descriptors in SGPRs
     if (p.packed) {
         Piece pc;
-        if (!piece_of(p, pc, h, s)) return;
+        if (!piece_of(p, wg, pc, h, s)) return;
         if (pc.len == 0) {  // an empty document: only its final state
             if (p.kv_out) one_empty_doc_state<D, W>(p, pc.doc, h, s, tid);
             return;
@@ -546,7 +551,7 @@ __global__ __launch_bounds__(kThreads, 1) void la_prefill_main_v2(PrefillParams 
         lb0 = pc.base;
         lb1 = pc.base + (t0 - cu_view(p)[pc.doc]) / p.L;
     } else {
-        if (!unit_of(p, u, h, s)) return;
+        if (!unit_of(p, wg, u, h, s)) return;
         t0 = u * p.L;
         t1 = min(p.T, t0 + p.L);
     }
@@ -880,6 +885,27 @@ __global__ __launch_bounds__(kThreads, 1) void la_prefill_main_v2(PrefillParams 
 
     if (p.kv_out && !p.packed) empty_doc_states<D, W>(p, u, h, s, t0, t1, tid);
     vm_wait<0>();  // no tile load may still be writing into this workgroup's LDS when it ends
+}
+
+template <int D, int B, int W, int NS, bool DK = false>
+__global__ __launch_bounds__(kThreads, 1) void la_prefill_main_v2(PrefillParams p) {
+    main_v2<D, B, W, NS, DK>(p, blockIdx.x);
+}
+
+// Two passes with the same plan in one launch: the backward's dv and dk
+// passes, which read the same Q and dO tiles (one as keys and values, the
+// other as values and keys) in the same order.  Workgroup g runs on XCD
+// g mod 8 (dispatch is round-robin); of the workgroups of one XCD, in dispatch
+// order, the even ones run the units of pass p0 and the odd ones the same
+// units of pass p1, so the two workgroups of a unit run side by side on one
+// XCD and the second to ask for a shared tile finds it in that XCD's L2.  The
+// grid is twice the single pass's (a multiple of 16): pass-local index
+// 8 (l / 2) + g mod 8 for local index l = g / 8.
+template <int D, int B, int W, int NS>
+__global__ __launch_bounds__(kThreads, 1) void la_prefill_pair_v2(PrefillParams p0, PrefillParams p1) {
+    const int64_t g = blockIdx.x, l = g >> 3;
+    const int64_t wg = ((l >> 1) << 3) | (g & 7);
+    main_v2<D, B, W, NS, false>((l & 1) ? p1 : p0, wg);
 }
 
 }  // namespace v2

@@ -246,23 +246,38 @@ la_status la_prefill_resume(const void* q, const void* k, const void* v, void* o
  * from its last token to its first (query k / key q / value dO from dKV_out,
  * then query v / key dO / value q from dKV_out^T).  The dk pass's segment
  * states are the transposes of the dv pass's; on the transpose-read loop they
- * are transposed in the workspace instead of being computed again.
+ * are transposed in the workspace instead of being computed again, and, when
+ * the workspace also has room for that transposed copy
+ * (la_prefill_backward_workspace_size), the dv and dk block loops run in one
+ * launch, where the two workgroups of each unit share the Q and dO tiles
+ * through L2.  The results are the same either way, bit for bit.
  *
  *   q, k, v, dout      [T, H, d] dtype, device, 16-byte aligned, read only.
  *   kv_state_in        the forward's incoming states or NULL (zero).
  *   dkv_state_out      [num_seqs, H, d, d] fp32 gradient of the final states, or NULL (zero).
  *   dq, dk, dv         [T, H, d] dtype, device, 16-byte aligned, fully overwritten.
  *   dkv_state_in       [num_seqs, H, d, d] fp32 or NULL: gradient of kv_state_in.
- *   Outputs overlap neither an input nor each other.  The workspace is that of
- *   la_prefill_workspace_size_ex for the same shapes and opts (one buffer
- *   serves the three passes, which run in order on `stream`).  Shapes, dtypes,
- *   blocks and tuning options as in la_prefill_ex; opts' events are ignored.
+ *   Outputs overlap neither an input nor each other.  The workspace is at
+ *   least that of la_prefill_workspace_size_ex for the same shapes and opts
+ *   (one buffer serves the passes, which run in order on `stream`);
+ *   la_prefill_backward_workspace_size bytes let the two reverse passes share
+ *   a launch.  Shapes, dtypes, blocks and tuning options as in la_prefill_ex;
+ *   opts' events are ignored.
  */
 la_status la_prefill_backward(const void* q, const void* k, const void* v, const void* dout,
                               const int32_t* cu_seqlens, int32_t H, int32_t d, int32_t block,
                               const float* kv_state_in, const float* dkv_state_out, void* dq, void* dk, void* dv,
                               float* dkv_state_in, int32_t num_seqs, int64_t total_tokens, la_dtype dtype,
                               void* workspace, size_t workspace_bytes, void* stream, const la_prefill_opts* opts);
+
+/* Workspace bytes with which la_prefill_backward runs its dv and dk passes in
+ * one launch: la_prefill_workspace_size_ex's bytes plus a transposed copy of
+ * the segment states (the same when the plan has no segment states or does not
+ * use the transpose-read loop).  The forward's layout is a prefix of it, so one
+ * buffer of this size serves a forward call and the backward that reuses its
+ * states (forward_states).  0 for unsupported shapes. */
+size_t la_prefill_backward_workspace_size(int64_t total_tokens, int32_t num_seqs, int32_t H, int32_t d,
+                                          int32_t block, la_dtype dtype, const la_prefill_opts* opts);
 
 /* Decayed variant: the same prefill with each head's state fading by a factor
  * lambda_h before every token's update.  "MiniMax-01技术报告解读" §3.3 item 1

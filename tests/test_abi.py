@@ -187,6 +187,32 @@ def test_plans(lib):
         la.la_prefill_plan(8192, 1, 8, 64, 64, la.LA_BF16, la.make_opts(slots=3))
 
 
+def test_backward_workspace_size(lib):
+    """The backward's workspace with room for the transposed segment states:
+    the forward's bytes (rounded to 256) plus one fp32 d x d state per segment
+    state and head, also rounded; the forward's size when the plan keeps no
+    segment states or runs the generic loop; 0 for shapes the planner rejects."""
+    r256 = lambda x: (x + 255) // 256 * 256
+    for T, D, H, d, B, dt, o in [(8192, 1, 8, 128, 64, la.LA_BF16, None),
+                                 (1048576, 1, 8, 128, 64, la.LA_BF16, None),
+                                 (8192, 1, 8, 128, 64, la.LA_BF16, la.make_opts(seg_len=64, value_slices=2)),
+                                 (131072, 20, 64, 128, 64, la.LA_BF16, la.make_opts(seg_len=8192, work_list=2))]:
+        p = la.la_prefill_plan(T, D, H, d, B, dt, o)
+        states = (T // p["seg_len"]) if p["packed"] else p["num_segments"] - 1
+        got = la.la_prefill_backward_workspace_size(T, D, H, d, B, dt, o)
+        assert got == r256(p["workspace_bytes"]) + r256(states * H * d * d * 4), (T, D, H, p)
+        assert got > la.la_prefill_workspace_size_ex(T, D, H, d, B, dt, o)
+    # no segment states (one segment; every document one piece), generic loop: the forward's size
+    assert la.la_prefill_backward_workspace_size(256, 1, 2, 16, 32, la.LA_FP32) == 0
+    p = la.la_prefill_plan(131072, 20, 64, 128, 64, la.LA_BF16)
+    assert la.la_prefill_backward_workspace_size(131072, 20, 64, 128, 64, la.LA_BF16) == \
+        r256(p["workspace_bytes"]) + r256((131072 // p["seg_len"]) * 64 * 128 * 128 * 4)
+    o = la.make_opts(variant=1, seg_len=512)
+    assert la.la_prefill_backward_workspace_size(8192, 1, 8, 128, 64, la.LA_BF16, o) == \
+        la.la_prefill_workspace_size_ex(8192, 1, 8, 128, 64, la.LA_BF16, o)
+    assert la.la_prefill_backward_workspace_size(8192, 1, 8, 48, 64, la.LA_BF16) == 0
+
+
 def test_host_validation_under_sanitizers(tmp_path):
     exe = str(tmp_path / "hvc")
     src = [os.path.join(ROOT, "tests", "native", "host_validation_check.cpp"),

@@ -133,6 +133,40 @@ def test_backward_with_forward_states(opts, with_states):
         assert np.array_equal(a, to_host(b)), "only the dq pass may change"
 
 
+PAIR_CASES = [(128, dict()), (128, dict(seg_len=192)), (128, dict(seg_len=128, force_scan=True)),
+              (128, dict(seg_len=256, value_slices=2)), (128, dict(seg_len=1024, value_slices=2, slots=3)),
+              (128, dict(seg_len=1024, slots=3)), (128, dict(seg_len=384, work_list=2)), (64, dict(seg_len=128))]
+
+
+@pytest.mark.parametrize("d,opts", PAIR_CASES, ids=[f"d{d}-{o}" for d, o in PAIR_CASES])
+def test_paired_reverse_passes(d, opts):
+    """With a workspace of la_prefill_backward_workspace_size bytes the dv and
+    dk passes share one launch (la_prefill_pair_v2); with the forward's size
+    they run one after the other.  Same kernels, same states: the gradients
+    must agree bit for bit, and match the oracle."""
+    import torch
+
+    lens = [700, 0, 1, 1563, 64, 0, 437, 2100]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    T, H = int(cu[-1]), 3
+    q, k, v, dout = inputs(331, T, H, d, "bf16")
+    kv_in = states(332, 7, len(lens), H, d, float(np.sqrt(300)) / d)
+    dkv_out = states(333, 9, len(lens), H, d, 0.1)
+    mo = la.make_opts(**opts)
+    fwd_ws = la.la_prefill_workspace_size_ex(T, len(lens), H, d, 64, la.LA_BF16, mo)
+    bwd_ws = la.la_prefill_backward_workspace_size(T, len(lens), H, d, 64, la.LA_BF16, mo)
+    plan = la.la_prefill_plan(T, len(lens), H, d, 64, la.LA_BF16, mo)
+    log(f"  paired {d} {opts} plan={plan} ws {fwd_ws} / {bwd_ws}")
+    assert bwd_ws >= fwd_ws
+    outs = []
+    for nbytes in (fwd_ws, bwd_ws):
+        ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device="cuda")
+        outs.append(run(q, k, v, dout, cu, 64, kv_in, dkv_out, workspace=ws, **opts))
+    for name, a, b in zip(("dq", "dk", "dv", "dkv_in"), outs[0], outs[1]):
+        assert np.array_equal(a.view(np.uint8), b.view(np.uint8)), f"paired {name} differs from sequential"
+    check(q, k, v, dout, cu, kv_in, dkv_out, outs[1], False, f"paired d={d} {opts}")
+
+
 def test_forward_states_are_claimed_once():
     """forward_states reuses the forward's segment states only while the
     workspace holds the stamp of a forward call on these very inputs, shapes
