@@ -94,6 +94,10 @@ __device__ __forceinline__ f32x4_t zero4() { return f32x4_t{0.f, 0.f, 0.f, 0.f};
 // Decayed variant: lambda^m for m >= 0 from l2 = log2(lambda), as exp2(m l2);
 // lambda^0 = 1 also for lambda = 0 (l2 = -inf).
 __device__ __forceinline__ float decay_pow(float l2, int m) { return m <= 0 ? 1.f : exp2f(l2 * (float)m); }
+// The same divided by 2^lc (lc: log2 of a state's scale, finite).
+__device__ __forceinline__ float decay_pow(float l2, int m, float lc) {
+    return m <= 0 ? exp2f(-lc) : exp2f(l2 * (float)m - lc);
+}
 
 // A bf16 fragment (8 elements) scaled element by element, rounded to nearest
 // even; element e of lo.x, lo.y, hi.x, hi.y is (e % 2 == 0 ? low : high) half.

@@ -210,21 +210,18 @@ struct Geo {
 
 // KV[:, own cols] += K^T V over one block; keeps the V^T fragments (A operands
 // of the intra product).  Decayed variant (DK, l2 = log2 lambda, nb tokens in
-// the block): KV <- lambda^nb KV + sum_c lambda^(nb - 1 - c) k_c^T v_c, the
-// weights applied to a bf16 copy of the V^T fragments (lane group g holds
-// tokens 32 kc + 8 g + e of each chunk); the kept fragments stay unscaled.
+// the block): the state is kept scaled, KV = 2^lc U, so that the fade
+// lambda^nb of each block changes only the scale (the caller's lc, see
+// fade_scale) and this update adds sum_c lambda^(nb - 1 - c) 2^-lc k_c^T v_c to
+// U, the weights applied to a bf16 copy of the V^T fragments (lane group g
+// holds tokens 32 kc + 8 g + e of each chunk); the kept fragments stay
+// unscaled.
 template <int D, int B, int W, bool DK = false, int NA, int NC, int NK>
 __device__ __forceinline__ void state_update(f32x4_t (&kv)[NA][NC], Frag<bf16_t> (&vfr)[NC][NK], const bf16_t* Ks,
-                                             const bf16_t* Vs, int col0, int lane, float l2 = 0.f, int nb = B) {
+                                             const bf16_t* Vs, int col0, int lane, float l2 = 0.f, int nb = B,
+                                             float lc = 0.f) {
     using G = Geo<D, B, W>;
     static_assert(NA == G::NDT && NC == G::NCW && NK == B / 32, "tile counts");
-    if constexpr (DK) {
-        const float f = decay_pow(l2, nb);
-#pragma unroll
-        for (int a = 0; a < G::NDT; ++a)
-#pragma unroll
-            for (int c = 0; c < G::NCW; ++c) kv[a][c] *= f;
-    }
 #pragma unroll
     for (int kc = 0; kc < B / 32; ++kc) {
 #pragma unroll
@@ -238,7 +235,7 @@ __device__ __forceinline__ void state_update(f32x4_t (&kv)[NA][NC], Frag<bf16_t>
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const int tok = 32 * kc + 8 * (lane >> 4) + e;
-                w[e] = tok < nb ? decay_pow(l2, nb - 1 - tok) : 0.f;
+                w[e] = tok < nb ? decay_pow(l2, nb - 1 - tok, lc) : 0.f;
             }
 #pragma unroll
             for (int c = 0; c < G::NCW; ++c) vs[c] = scale_frag(vfr[c][kc], w);
@@ -253,6 +250,29 @@ __device__ __forceinline__ void state_update(f32x4_t (&kv)[NA][NC], Frag<bf16_t>
 #pragma unroll
             for (int c = 0; c < G::NCW; ++c) mma(kv[a][c], kf, vs[c]);
         }
+    }
+}
+
+// Decayed variant: the fade of a block of nb tokens on a state kept as
+// KV = 2^lc U.  It lowers lc by nb log2(1/lambda); only when the scale would
+// fall below 2^-kRescale (every few blocks for lambda near 1, every block for
+// small lambda, lambda = 0 included) is it applied to U, which then holds the
+// state itself again (lc = 0).  The weights of the block's own tokens are then
+// taken relative to the new scale (state_update's lc), so U never grows past
+// 2^kRescale times the state.
+constexpr float kRescale = 24.f;
+template <int NA, int NC>
+__device__ __forceinline__ void fade_scale(f32x4_t (&kv)[NA][NC], float& lc, float l2, int nb) {
+    const float next = lc + l2 * (float)nb;  // -inf for lambda = 0
+    if (next >= -kRescale) {
+        lc = next;
+    } else {
+        const float f = exp2f(next);
+#pragma unroll
+        for (int a = 0; a < NA; ++a)
+#pragma unroll
+            for (int c = 0; c < NC; ++c) kv[a][c] *= f;
+        lc = 0.f;
     }
 }
 
@@ -275,15 +295,18 @@ __device__ __forceinline__ void load_ws(f32x4_t (&kv)[NA][NC], const float* src,
         }
 }
 
-template <int D, int B, int W, int NA, int NC>
-__device__ __forceinline__ void store_ws(const f32x4_t (&kv)[NA][NC], float* dst, int lane) {
+template <int D, int B, int W, bool DK = false, int NA, int NC>
+__device__ __forceinline__ void store_ws(const f32x4_t (&kv)[NA][NC], float* dst, int lane, float f = 1.f) {
     using G = Geo<D, B, W>;
     static_assert(NA == G::NDT && NC == G::NCW, "tile counts");
     f32x4_t* d4 = reinterpret_cast<f32x4_t*>(dst);
 #pragma unroll
     for (int a = 0; a < G::NDT; ++a)
 #pragma unroll
-        for (int c = 0; c < G::NCW; ++c) d4[(a * G::NCW + c) * 64 + lane] = kv[a][c];
+        for (int c = 0; c < G::NCW; ++c) {
+            if constexpr (DK) d4[(a * G::NCW + c) * 64 + lane] = f * kv[a][c];
+            else d4[(a * G::NCW + c) * 64 + lane] = kv[a][c];
+        }
 }
 
 // A wave's block of the workspace state of unit (u, h, s).
@@ -311,8 +334,8 @@ __device__ __forceinline__ void add_state(f32x4_t (&kv)[NA][NC], const float* ba
             }
 }
 
-template <int D, int B, int W, int NA, int NC>
-__device__ __forceinline__ void store_state(const f32x4_t (&kv)[NA][NC], float* dst, int g, int li) {
+template <int D, int B, int W, bool DK = false, int NA, int NC>
+__device__ __forceinline__ void store_state(const f32x4_t (&kv)[NA][NC], float* dst, int g, int li, float f = 1.f) {
     using G = Geo<D, B, W>;
     static_assert(NA == G::NDT && NC == G::NCW, "tile counts");
 #pragma unroll
@@ -320,7 +343,10 @@ __device__ __forceinline__ void store_state(const f32x4_t (&kv)[NA][NC], float* 
 #pragma unroll
         for (int c = 0; c < G::NCW; ++c)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) dst[(int64_t)state_row(a, g, r) * D + state_col<NC>(c, li)] = kv[a][c][r];
+            for (int r = 0; r < 4; ++r) {
+                const float x = DK ? f * kv[a][c][r] : kv[a][c][r];
+                dst[(int64_t)state_row(a, g, r) * D + state_col<NC>(c, li)] = x;
+            }
 }
 
 // ---------------------------------------------------------------------------
@@ -367,6 +393,7 @@ __global__ __launch_bounds__(kThreads, 1) void la_segment_state_v2(PrefillParams
     const int col0 = wave * G::CW;
     // decayed variant: the state is faded to the end of the piece
     const float l2 = DK ? log2f(p.decay[h]) : 0.f;
+    float lc = 0.f;  // decayed: the state is 2^lc kv (fade_scale)
     DmaTile<D> dk;
     DmaTile<W> dv;
     dk.init(wave, lane, row_bytes);
@@ -415,9 +442,16 @@ __global__ __launch_bounds__(kThreads, 1) void la_segment_state_v2(PrefillParams
             // tokens in the two blocks of pair i - 1 (0 past the end)
             const int b0 = first + 2 * (i - 1) * B;
             const int nb0 = max(0, min(B, t_end - b0)), nb1 = max(0, min(B, t_end - b0 - B));
-            state_update<D, B, W, DK>(kv, vfr, kbuf(Slot<1 - SLOT>{}), vbuf(Slot<1 - SLOT>{}), col0, lane, l2, nb0);
+            if constexpr (DK) {
+                if (nb0 > 0) fade_scale(kv, lc, l2, nb0);
+            }
+            state_update<D, B, W, DK>(kv, vfr, kbuf(Slot<1 - SLOT>{}), vbuf(Slot<1 - SLOT>{}), col0, lane, l2, nb0,
+                                      lc);
+            if constexpr (DK) {
+                if (nb1 > 0) fade_scale(kv, lc, l2, nb1);
+            }
             state_update<D, B, W, DK>(kv, vfr, kbuf(Slot<1 - SLOT>{}) + B * D, vbuf(Slot<1 - SLOT>{}) + B * W, col0,
-                                      lane, l2, nb1);
+                                      lane, l2, nb1, lc);
         }
         ++i;
     };
@@ -427,7 +461,7 @@ __global__ __launch_bounds__(kThreads, 1) void la_segment_state_v2(PrefillParams
         step(Slot<1>{});
         if (i > npairs) break;
     }
-    store_ws<D, B, W>(kv, p.ws + ws_offset<D, W>(p, u, h, s, wave), lane);
+    store_ws<D, B, W, DK>(kv, p.ws + ws_offset<D, W>(p, u, h, s, wave), lane, DK ? exp2f(lc) : 1.f);
     vm_wait<0>();  // no tile load may still be writing into this workgroup's LDS when it ends
 }
 
@@ -576,6 +610,7 @@ __device__ __forceinline__ void main_v2(const PrefillParams& p, const int64_t wg
     // (0 above the diagonal: the causal mask), lambda^(query + 1) on the inter
     // product of query row 16 b + li.
     float l2 = 0.f, sfac[DK ? NQT : 1][4], ifac[DK ? NQT : 1];
+    float lc = 0.f;  // decayed: the state is 2^lc kv (fade_scale)
     if constexpr (DK) {
         l2 = log2f(p.decay[h]);
 #pragma unroll
@@ -816,19 +851,22 @@ __device__ __forceinline__ void main_v2(const PrefillParams& p, const int64_t wg
                 }
             }
         }
-        // decayed: the state reaches query row r faded r + 1 times
+        // decayed: the state reaches query row r faded r + 1 times, and kv
+        // holds it divided by 2^lc
         if constexpr (DK) {
+            const float sc = exp2f(lc);
 #pragma unroll
             for (int b = 0; b < NQT; ++b)
 #pragma unroll
-                for (int c = 0; c < NCW; ++c) oacc[b][c] *= ifac[b];
+                for (int c = 0; c < NCW; ++c) oacc[b][c] *= ifac[b] * sc;
         }
         issue_tile(cf, Slot<FILL>{}, Slot<2>{});
         // block j-1's rows leave after this iteration's loads: the next
         // iteration's wait for those loads lets these stores stay in flight
         if constexpr (LATE) finish_store(pb0, pnb);
         // state: KV += K^T V (after the inter product read it)
-        state_update<D, B, W, DK>(kv, vfr, Ks, Vs, col0, lane, l2, c0.nb);
+        if constexpr (DK) fade_scale(kv, lc, l2, c0.nb);
+        state_update<D, B, W, DK>(kv, vfr, Ks, Vs, col0, lane, l2, c0.nb, lc);
 
         // P[query][key] for keys of band w: causal mask (key <= query), the
         // tiles above the diagonal come out as zeros
@@ -845,12 +883,14 @@ __device__ __forceinline__ void main_v2(const PrefillParams& p, const int64_t wg
         if (c0.b0 + c0.nb == c0.doc_end) {  // the document ends with this block
             vm_wait<0>();  // rare path: keeps the loop's wait bookkeeping exact
             if (p.kv_out)
-                store_state<D, B, W>(kv, p.kv_out + (((int64_t)phys_doc(p, c0.doc) * p.H + h) * D) * D + s * W + col0,
-                                     g, li);
+                store_state<D, B, W, DK>(kv,
+                                         p.kv_out + (((int64_t)phys_doc(p, c0.doc) * p.H + h) * D) * D + s * W + col0,
+                                         g, li, DK ? exp2f(lc) : 1.f);
 #pragma unroll
             for (int a = 0; a < NDT; ++a)
 #pragma unroll
                 for (int c = 0; c < NCW; ++c) kv[a][c] = zero4();
+            lc = 0.f;
             const Cursor& cn = NS == 2 ? cf : c1;  // block j + 1
             if (p.kv_in && cn.nb > 0 && cn.first_of_doc) {  // the next document starts here
                 add_state<D, B, W>(kv, p.kv_in + (((int64_t)phys_doc(p, cn.doc) * p.H + h) * D) * D, s * W + col0,
