@@ -52,6 +52,11 @@ DECODE_SAMPLE = {}  # host copy of a few decode states for the oracle's timing
 KERNEL_SOURCES = ["la_prefill_kernels.h", "la_prefill_v2.h", "la_device.h", "la_tiles.h", "la_prefill_launch.inl",
                   "la_prefill_bf16.hip", "la_host.cpp"]
 MAIN_KERNEL = {1: "la_prefill_main_kernel", 2: "la_prefill_main_v2"}  # by the plan's block-loop variant
+
+
+def main_kernel(plan: dict, block: int) -> str:
+    """The block-loop kernel a plan runs (128-token blocks have a transpose-read loop of their own)."""
+    return "la_prefill_main_v2_b128" if plan["variant"] == 2 and block == 128 else MAIN_KERNEL[plan["variant"]]
 DECODE_SOURCES = ["la_decode_kernels.h", "la_device.h", "la_decode.hip"]
 METRIC = "prefill tokens·heads/s (bf16, d=128) + % roofline; decode steps/s"
 GIB = 1 << 30
@@ -279,7 +284,7 @@ def bench_prefill(name, args, la, torch, hip, steps: int, warmup: int, graph: bo
     avg_kernel_s = float(np.mean(kernel_ms)) / 1e3
     achieved = algo_bytes / avg_kernel_s / 1e9
     sha = sources_sha(KERNEL_SOURCES)
-    kname = MAIN_KERNEL[plan["variant"]]
+    kname = main_kernel(plan, block)
     roof_th = HBM_PEAK_GBS * 1e9 / (algo_bytes / (T * H))  # token-heads/s with every byte at HBM peak
     value = T * H * steps / elapsed
     rec = {
@@ -335,7 +340,7 @@ def bench_block(la, torch, hip, w, block: int, steps: int) -> dict:
     return {"workload": w["name"], "block": block, "value": T * H / s, "unit": "token·heads/s",
             "gpu_ms_per_step": s * 1e3, "steps": steps,
             "plan": {k2: plan[k2] for k2 in ("seg_len", "value_slices", "num_segments", "scan", "variant", "units")},
-            "block_loop": {"kernel": MAIN_KERNEL[plan["variant"]], "kernel_ms": kms,
+            "block_loop": {"kernel": main_kernel(plan, block), "kernel_ms": kms,
                            "frac": algo / (kms / 1e3) / 1e9 / HBM_PEAK_GBS},
             "whole_call_frac": T * H / s / roof_th}
 
@@ -368,7 +373,7 @@ def bench_decay(la, torch, hip, w, steps: int) -> dict:
     roof_th = HBM_PEAK_GBS * 1e9 / (8 * d)
     return {"workload": w["name"], "lambda": "1 - 2^-(5 + h)", "value": T * H / s, "unit": "token·heads/s",
             "gpu_ms_per_step": s * 1e3, "steps": steps,
-            "block_loop": {"kernel": MAIN_KERNEL[plan["variant"]], "kernel_ms": kms,
+            "block_loop": {"kernel": main_kernel(plan, 64), "kernel_ms": kms,
                            "frac": algo / (kms / 1e3) / 1e9 / HBM_PEAK_GBS},
             "whole_call_frac": T * H / s / roof_th}
 

@@ -276,7 +276,7 @@ la_status la_prefill_backward(const void* q, const void* k, const void* v, const
     // each unit's two workgroups side by side on one XCD (la_prefill_pair_v2),
     // and the tiles one of them loads come from L2 for the other.
     hipStream_t hs = static_cast<hipStream_t>(stream);
-    if (dtype == LA_BF16 && p2.variant == 2 && same_plan(p2, p3) &&
+    if (dtype == LA_BF16 && block == 64 && p2.variant == 2 && same_plan(p2, p3) &&
         (p3.states() == 0 || workspace_bytes >= p3.bwd_ws_bytes)) {
         la::PrefillParams pv = make_params(p3, k, q, dout, dv, cu_seqlens, H, d, block, dkv_state_out, 0,
                                            dkv_state_in, 1, num_seqs, total_tokens, dtype, workspace, 0, false,

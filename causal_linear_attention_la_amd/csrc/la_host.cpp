@@ -73,11 +73,14 @@ la_status make_plan(int64_t T, int32_t num_seqs, int32_t H, int32_t d, int32_t b
         if (S < 1 || d % S != 0) return false;
         return main_fits((int)es, d, block, d / S);
     };
-    // the transpose-read block loop: bf16, d >= 64, 64-token blocks, slices >= 64 columns, and a
-    // block of rows (64 rows of H * d bf16) addressable with 32-bit offsets
+    // the transpose-read block loops: bf16, d >= 64, 64-token blocks with slices >= 64 columns or
+    // (plain variant) 128-token blocks with slices of exactly 64, and 64 rows of H * d bf16 (a
+    // tile) addressable with 32-bit offsets
     auto v2_ok = [&](int32_t S) {
-        return dtype == LA_BF16 && d >= 64 && block == 64 && d / S >= 64 &&
-               (int64_t)H * d * 2 * block <= kMaxBlockBytes;
+        if (dtype != LA_BF16 || d < 64 || S < 1 || d % S != 0 || (int64_t)H * d * 2 * 64 > kMaxBlockBytes)
+            return false;
+        if (block == 64) return d / S >= 64;
+        return block == 128 && !decay && d / S == 64;
     };
     const int32_t variant = opts ? opts->variant : 0;
     if (variant < 0 || variant > 2) return LA_ERR_UNSUPPORTED;
@@ -85,8 +88,12 @@ la_status make_plan(int64_t T, int32_t num_seqs, int32_t H, int32_t d, int32_t b
     Plan p;
     const int64_t work = T * (int64_t)H;
     if (opts && opts->value_slices != 0) {
-        if (!is_pow2_in(opts->value_slices, 1, 4) || !slice_ok(opts->value_slices)) return LA_ERR_UNSUPPORTED;
+        if (!is_pow2_in(opts->value_slices, 1, 4) ||
+            !(slice_ok(opts->value_slices) || (variant != 1 && v2_ok(opts->value_slices))))
+            return LA_ERR_UNSUPPORTED;
         p.S = opts->value_slices;
+    } else if (block == 128 && variant != 1 && v2_ok(d / 64)) {
+        p.S = d / 64;  // the 128-token transpose-read loop takes 64-column slices
     } else {
         int32_t chosen = 0;
         const bool want_v2 = variant != 1 && v2_ok(1);
@@ -175,12 +182,18 @@ la_status make_plan(int64_t T, int32_t num_seqs, int32_t H, int32_t d, int32_t b
     if (p.scan && (int64_t)H * d * d / 4 > (((int64_t)1 << 32) - 1)) return LA_ERR_UNSUPPORTED;
     const int32_t slots = opts ? opts->slots : 0;
     if (!(slots == 0 || slots == 2 || slots == 3)) return LA_ERR_UNSUPPORTED;
-    // (the decayed full-width loop has no registers for a third slot)
-    const bool three_ok = p.variant == 2 && d == 128 && !(decay && p.W == 128);
-    if (slots == 3 && !three_ok) return LA_ERR_UNSUPPORTED;
-    if (slots != 0) p.slots = slots;
-    else p.slots = three_ok && p.L / block >= kThreeSlotMinBlocks ? 3 : 2;
-    if (p.variant != 2) p.slots = 2;  // (the generic loop has no slot choice)
+    if (p.variant == 2 && block == 128) {
+        // the 128-token loop always runs three slots (one block's two halves and the next block's first)
+        if (slots == 2) return LA_ERR_UNSUPPORTED;
+        p.slots = 3;
+    } else {
+        // (the decayed full-width loop has no registers for a third slot)
+        const bool three_ok = p.variant == 2 && d == 128 && !(decay && p.W == 128);
+        if (slots == 3 && !three_ok) return LA_ERR_UNSUPPORTED;
+        if (slots != 0) p.slots = slots;
+        else p.slots = three_ok && p.L / block >= kThreeSlotMinBlocks ? 3 : 2;
+        if (p.variant != 2) p.slots = 2;  // (the generic loop has no slot choice)
+    }
 
     // Workspace: a 256-byte header at offset 0 whatever the plan (the stamp of
     // the forward call whose segment states it holds, and a backward's reuse

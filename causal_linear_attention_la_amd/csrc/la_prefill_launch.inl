@@ -4,11 +4,12 @@
 namespace la {
 namespace {
 
-// The transpose-read block loop (la_prefill_v2.h) covers bf16, d >= 64,
-// 64-token blocks and slices of at least 64 value columns.
+// The transpose-read block loops (la_prefill_v2.h) cover bf16, d >= 64, and
+// 64-token blocks with slices of at least 64 value columns or 128-token
+// blocks with slices of exactly 64.
 template <typename T, int D, int B, int W>
 constexpr bool has_v2() {
-    return sizeof(T) == 2 && D >= 64 && B == 64 && W >= 64;
+    return sizeof(T) == 2 && D >= 64 && ((B == 64 && W >= 64) || (B == 128 && W == 64));
 }
 
 // Launches the block-loop kernel; with events, through hipExtLaunchKernel, so
@@ -24,7 +25,10 @@ inline hipError_t launch_main(void (*kernel)(PrefillParams), dim3 grid, dim3 blo
 // The kernels of one plan, without (DK = false) or with the decay.
 template <typename T, int D, int B, int W, bool DK>
 hipError_t run_prefill_k(const PrefillParams& p, int variant, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
-    if constexpr (!main_fits((int)sizeof(T), D, B, W)) {
+    // (the generic loop's tiles do not fit every shape the transpose-read loops take)
+    constexpr bool GEN = main_fits((int)sizeof(T), D, B, W);
+    constexpr bool V2 = has_v2<T, D, B, W>();
+    if constexpr (!GEN && !V2) {
         return hipErrorInvalidValue;
     } else {
         const dim3 block(kThreads);
@@ -32,11 +36,14 @@ hipError_t run_prefill_k(const PrefillParams& p, int variant, hipStream_t st, hi
         // pieces: one per table entry (head, slice), in table order
         const dim3 grid((unsigned)(p.packed ? p.units : 8 * p.per_xcd));
         bool use_v2 = false;
-        if constexpr (has_v2<T, D, B, W>()) use_v2 = (variant != 1);
+        if constexpr (V2) use_v2 = (variant != 1);
         if (variant == 2 && !use_v2) return hipErrorInvalidValue;
-        void (*seg_kernel)(PrefillParams) = la_segment_state_kernel<T, D, B, W, DK>;
-        if constexpr (has_v2<T, D, B, W>()) {
-            if (use_v2) seg_kernel = v2::la_segment_state_v2<D, B, W, DK>;
+        if (!GEN && !use_v2) return hipErrorInvalidValue;
+        void (*seg_kernel)(PrefillParams) = nullptr;
+        if constexpr (GEN) seg_kernel = la_segment_state_kernel<T, D, B, W, DK>;
+        if constexpr (V2) {
+            // (a segment state is a sum over its piece: the 64-token state kernel serves both block sizes)
+            if (use_v2) seg_kernel = v2::la_segment_state_v2<D, 64, W, DK>;
         }
         if (p.packed) {
             hipError_t e = launch_kernel(la_plan_pieces_kernel<kPlanThreads>, dim3(1), dim3(kPlanThreads), st, p);
@@ -59,10 +66,15 @@ hipError_t run_prefill_k(const PrefillParams& p, int variant, hipStream_t st, hi
             }
         }
         if (p.prefix_only) return hipSuccess;
-        void (*main_kernel)(PrefillParams) = la_prefill_main_kernel<T, D, B, W, DK>;
-        if constexpr (has_v2<T, D, B, W>()) {
+        void (*main_kernel)(PrefillParams) = nullptr;
+        if constexpr (GEN) main_kernel = la_prefill_main_kernel<T, D, B, W, DK>;
+        if constexpr (V2) {
             if (use_v2) {
-                if constexpr (D == 128 && DK && W == 128) {
+                if constexpr (B == 128) {
+                    // (no decayed form: the planner gives decayed 128-token blocks the generic loop)
+                    if constexpr (DK) return hipErrorInvalidValue;
+                    else main_kernel = v2::la_prefill_main_v2_b128<D, W>;
+                } else if constexpr (D == 128 && DK && W == 128) {
                     // (the decayed full-width loop has no registers for a third slot: the planner gives it two)
                     if (p.slots == 3) return hipErrorInvalidValue;
                     main_kernel = v2::la_prefill_main_v2<D, B, W, 2, DK>;

@@ -927,6 +927,318 @@ __device__ __forceinline__ void main_v2(const PrefillParams& p, const int64_t wg
     vm_wait<0>();  // no tile load may still be writing into this workgroup's LDS when it ends
 }
 
+// ---------------------------------------------------------------------------
+// The block loop for 128-token blocks (bf16, 64-column slices, plain variant).
+// A block of 128 tokens runs as two halves of 64 rows, a and c, on the tiles,
+// fragments and LDS layout of the 64-token loop.  Both halves take the inter
+// product against the state at the block's start, so the state update
+// (KV += K_a^T V_a + K_c^T V_c) waits for the end of c; c's intra product adds,
+// to its own masked scores P_cc = mask(Q_c K_c^T), the unmasked scores of its
+// queries against a's keys, P_ca = Q_c K_a^T, times V_a: together the block's
+// left product (Q K^T (.) M) V over all 128 tokens.  Blocks restart at each
+// document start (a document whose length is an odd number of halves ends with
+// an empty c half, which keeps the halves' order fixed).
+//
+// Slots: a halves alternate between slots 0 and 2, c halves use slot 1, so
+// a's tiles stay in place while c runs.  Iteration a loads the same block's c
+// half (one iteration ahead) and the next block's a half (two ahead); iteration
+// c loads nothing.  The loop is unrolled over two blocks, so every slot and
+// every wait count is fixed at compile time.
+template <int D, int W>
+__device__ __forceinline__ void main_v2_b128(const PrefillParams& p, const int64_t wg) {
+    constexpr int B = 64;  // rows of a half
+    using G = Geo<D, B, W>;
+    constexpr int NQT = G::NQT, NCW = G::NCW, NDT = G::NDT;
+    static_assert(NQT == kWaves && NCW == 1, "64-column slices, key band w per wave");
+    constexpr int PP = B;
+    constexpr int QN = B * D, VN = B * W;
+    __shared__ __align__(16) bf16_t Q0[QN], Q1[QN], Q2[QN];
+    __shared__ __align__(16) bf16_t K0[QN], K1[QN], K2[QN];
+    __shared__ __align__(16) bf16_t V0[VN], V1[VN], V2[VN];
+    __shared__ __align__(16) bf16_t Ps[B * PP];  // masked scores of the half (P_aa or P_cc)
+    __shared__ __align__(16) bf16_t Px[B * PP];  // c's queries against a's keys (P_ca)
+    constexpr int NST = G::STORES, LOADS = G::LOADS;
+    auto qbuf = [&](auto slot) -> bf16_t* {
+        constexpr int X = decltype(slot)::value;
+        if constexpr (X == 0) return Q0;
+        else if constexpr (X == 1) return Q1;
+        else return Q2;
+    };
+    auto kbuf = [&](auto slot) -> bf16_t* {
+        constexpr int X = decltype(slot)::value;
+        if constexpr (X == 0) return K0;
+        else if constexpr (X == 1) return K1;
+        else return K2;
+    };
+    auto vbuf = [&](auto slot) -> bf16_t* {
+        constexpr int X = decltype(slot)::value;
+        if constexpr (X == 0) return V0;
+        else if constexpr (X == 1) return V1;
+        else return V2;
+    };
+
+    stamp_key(p, wg);
+    int u = 0, h, s, t0, t1;
+    int lb0 = 0, lb1 = 0;
+    const int tid = threadIdx.x, lane = tid & 63, li = lane & 15, g = lane >> 4;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    if (p.packed) {
+        Piece pc;
+        if (!piece_of(p, wg, pc, h, s)) return;
+        if (pc.len == 0) {
+            if (p.kv_out) one_empty_doc_state<D, W>(p, pc.doc, h, s, tid);
+            return;
+        }
+        t0 = pc.t0;
+        t1 = pc.t0 + pc.len;
+        lb0 = pc.base;
+        lb1 = pc.base + (t0 - cu_view(p)[pc.doc]) / p.L;
+    } else {
+        if (!unit_of(p, wg, u, h, s)) return;
+        t0 = u * p.L;
+        t1 = min(p.T, t0 + p.L);
+    }
+    const int col0 = wave * G::CW;
+    const bf16_t* qg = static_cast<const bf16_t*>(p.q);
+    const bf16_t* kg = static_cast<const bf16_t*>(p.k);
+    const bf16_t* vg = static_cast<const bf16_t*>(p.v);
+    bf16_t* og = static_cast<bf16_t*>(p.o);
+    const uint32_t row_bytes = (uint32_t)(p.H * D * 2);
+
+    DmaTile<D> dq;
+    DmaTile<W> dv;
+    dq.init(wave, lane, row_bytes);
+    dv.init(wave, lane, row_bytes);
+
+    const CuView cuv = cu_view(p);
+    Cursor c0;  // the current 128-token block
+    cursor_first(c0, cuv, p.num_seqs, t0, t1, 2 * B);
+
+    f32x4_t kv[NDT][NCW];
+#pragma unroll
+    for (int a = 0; a < NDT; ++a) kv[a][0] = zero4();
+    f32x4_t oacc[NQT][NCW];
+#pragma unroll
+    for (int b = 0; b < NQT; ++b) oacc[b][0] = zero4();
+    Frag<bf16_t> vfa[NCW][B / 32];  // V_a^T fragments: a's intra product and c's cross term
+    Frag<bf16_t> vfc[NCW][B / 32];  // V_c^T fragments
+    u32x4_t opk[NQT];
+
+    // Half HF (0 = a, 1 = c) of block c: its first token and length (0 past the end).
+    auto half = [&](const Cursor& c, int hf, int& b0h, int& nbh) {
+        const int nb = max(c.nb, 0);
+        b0h = c.b0 + B * hf;
+        nbh = hf == 0 ? min(B, nb) : max(0, nb - B);
+    };
+    auto issue_tile = [&](const Cursor& c, auto hf, auto slot, auto tile) {
+        constexpr int TILE = decltype(tile)::value;
+        int b0h, nbh;
+        half(c, decltype(hf)::value, b0h, nbh);
+        const int64_t e0 = ((int64_t)(nbh > 0 ? phys_block(p, b0h, nbh) : 0) * p.H + h) * D;
+        const uint32_t bytes = (uint32_t)nbh * row_bytes;
+        const uint32_t last = (uint32_t)(nbh - 1) * row_bytes;
+        if constexpr (TILE == 0) dq.issue(make_rsrc(qg + e0, bytes), qbuf(slot), p.rev, last);
+        else if constexpr (TILE == 1) dq.issue(make_rsrc(kg + e0, bytes), kbuf(slot), p.rev, last);
+        else dv.issue(make_rsrc(vg + e0 + s * W, bytes), vbuf(slot), p.rev, last);
+    };
+    // O^T += V^T P^T for the previous half (and, after a c half, + V_a^T P_ca^T),
+    // then its rows are packed for the late stores.
+    auto finish = [&](auto cross) {
+        Frag<bf16_t> pfs[6];  // (band, chunk) = (0,0) (1,0) (2,0) (2,1) (3,0) (3,1)
+#pragma unroll
+        for (int b = 0, n = 0; b < NQT; ++b)
+#pragma unroll
+            for (int kc = 0; kc <= b / 2; ++kc, ++n) load_row<PP>(pfs[n], Ps, 16 * b + li, 32 * kc, g);
+        if constexpr (decltype(cross)::value) {
+#pragma unroll
+            for (int b = 0, n = 0; b < NQT; ++b)
+#pragma unroll
+                for (int kc = 0; kc <= b / 2; ++kc, ++n) mma(oacc[b][0], vfc[0][kc], pfs[n]);
+#pragma unroll
+            for (int b = 0; b < NQT; ++b) {
+                Frag<bf16_t> xf[2];
+                load_row<PP>(xf[0], Px, 16 * b + li, 0, g);
+                load_row<PP>(xf[1], Px, 16 * b + li, 32, g);
+                mma(oacc[b][0], vfa[0][0], xf[0]);
+                mma(oacc[b][0], vfa[0][1], xf[1]);
+            }
+        } else {
+#pragma unroll
+            for (int b = 0, n = 0; b < NQT; ++b)
+#pragma unroll
+                for (int kc = 0; kc <= b / 2; ++kc, ++n) mma(oacc[b][0], vfa[0][kc], pfs[n]);
+        }
+#pragma unroll
+        for (int b = 0; b < NQT; ++b) {
+            opk[b].x = pack2(oacc[b][0][0], oacc[b][0][1]);
+            opk[b].y = pack2(oacc[b][0][2], oacc[b][0][3]);
+            oacc[b][0] = zero4();
+        }
+    };
+    auto finish_store = [&](int pb0, int pnb) {
+        const __amdgpu_buffer_rsrc_t ro =
+            make_rsrc(og + ((int64_t)phys_block(p, pb0, pnb) * p.H + h) * D + s * W + col0, (uint32_t)pnb * row_bytes);
+#pragma unroll
+        for (int b = 0; b < NQT; ++b) {
+            const int r = 16 * b + li;
+            const uint32_t off = (uint32_t)(p.rev ? pnb - 1 - r : r) * row_bytes;
+            u32x2_t v;
+            v.x = opk[b].x;
+            v.y = opk[b].y;
+            __builtin_amdgcn_raw_buffer_store_b64(v, ro, off + (4 * g) * 2, 0, 0);
+        }
+    };
+    // inter product O^T += KV^T Q^T of the half in Qs, with its masked scores
+    // S^T = K_w Q^T (key band w of Ks), and, with Ka, the unmasked scores of
+    // the same queries against key band w of Ka
+    auto inter = [&](const bf16_t* Qs, const bf16_t* Ks, const bf16_t* Ka, f32x4_t (&sacc)[NQT],
+                     f32x4_t (&xacc)[NQT], auto with_cross) {
+#pragma unroll
+        for (int b = 0; b < NQT; ++b) {
+            sacc[b] = zero4();
+            if constexpr (decltype(with_cross)::value) xacc[b] = zero4();
+        }
+#pragma unroll
+        for (int m = 0; m < D / 32; ++m) {
+            Frag<bf16_t> kvf;
+            kvf.lo = make_uint2(pack2(kv[2 * m][0][0], kv[2 * m][0][1]), pack2(kv[2 * m][0][2], kv[2 * m][0][3]));
+            kvf.hi = make_uint2(pack2(kv[2 * m + 1][0][0], kv[2 * m + 1][0][1]),
+                                pack2(kv[2 * m + 1][0][2], kv[2 * m + 1][0][3]));
+            Frag<bf16_t> kf, kx;
+            load_row<D>(kf, Ks, 16 * wave + li, 32 * m, g);
+            if constexpr (decltype(with_cross)::value) load_row<D>(kx, Ka, 16 * wave + li, 32 * m, g);
+            Frag<bf16_t> qfs[NQT];
+#pragma unroll
+            for (int b = 0; b < NQT; ++b) load_row<D>(qfs[b], Qs, 16 * b + li, 32 * m, g);
+#pragma unroll
+            for (int b = 0; b < NQT; ++b) {
+                mma(oacc[b][0], kvf, qfs[b]);
+                mma(sacc[b], kf, qfs[b]);
+                if constexpr (decltype(with_cross)::value) mma(xacc[b], kx, qfs[b]);
+            }
+        }
+    };
+    // P[query][key] for keys of band w (masked: key <= query) into buffer P
+    auto store_scores = [&](bf16_t* P, f32x4_t (&acc)[NQT], bool masked) {
+#pragma unroll
+        for (int b = 0; b < NQT; ++b) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                if (masked && 16 * wave + 4 * g + r > 16 * b + li) acc[b][r] = 0.f;
+            store4(P + soff<PP>(16 * b + li, 16 * wave + 4 * g), acc[b][0], acc[b][1], acc[b][2], acc[b][3]);
+        }
+    };
+    // V_a^T fragments (as state_update loads them)
+    auto load_vf = [&](Frag<bf16_t> (&vf)[NCW][B / 32], const bf16_t* Vs) {
+#pragma unroll
+        for (int kc = 0; kc < B / 32; ++kc) load_tr<W, 4>(vf[0][kc], Vs, 32 * kc, col0, 0, lane);
+    };
+    // KV += K^T V with the V^T fragments already loaded
+    auto kv_add = [&](const bf16_t* Ks, const Frag<bf16_t> (&vf)[NCW][B / 32]) {
+#pragma unroll
+        for (int kc = 0; kc < B / 32; ++kc)
+#pragma unroll
+            for (int a = 0; a < NDT; ++a) {
+                Frag<bf16_t> kf;
+                load_tr<D, 8>(kf, Ks, 32 * kc, 32 * (a >> 1), 4 * (a & 1), lane);
+                mma(kv[a][0], kf, vf[0][kc]);
+            }
+    };
+
+    if (c0.nb > 0) {  // the first block's a half, before the prefix loads, so the two overlap
+        issue_tile(c0, Slot<0>{}, Slot<0>{}, Slot<0>{});
+        issue_tile(c0, Slot<0>{}, Slot<0>{}, Slot<1>{});
+        issue_tile(c0, Slot<0>{}, Slot<0>{}, Slot<2>{});
+    }
+    if (c0.nb > 0 && !c0.first_of_doc) {
+        const int u_first = p.packed ? lb0 : p.scan ? u - 1 : cuv[c0.doc] / p.L;
+        const int u_end = p.packed ? lb1 : u;
+        for (int uu = u_first; uu < u_end; ++uu) load_ws<D, B, W>(kv, p.ws + ws_offset<D, W>(p, uu, h, s, wave), lane);
+    }
+    if (p.kv_in && c0.nb > 0)
+        add_state<D, B, W>(kv, p.kv_in + (((int64_t)phys_doc(p, c0.doc) * p.H + h) * D) * D, s * W + col0, p.kv_in_t,
+                           g, li);
+    int pb0 = t0, pnb = 0;  // the half whose rows the next finish stores
+    bool first = true;
+    Cursor cn = c0;  // the next block
+    // Half a of block c0, in slot AS; the next block's a half goes to slot NAS.
+    auto step_a = [&](auto as, auto nas) {
+        cn = c0;
+        cursor_next(cn, cuv, p.num_seqs, t1, 2 * B);
+        // a's loads were issued before the previous block's two halves stored
+        // their rows (one late store group each); the first block's, by the
+        // prologue alone
+        if (first) vm_wait<0>();
+        else vm_wait<2 * NST>();
+        first = false;
+        lds_barrier();  // (A) a visible; the previous block's tiles no longer read
+        issue_tile(c0, Slot<1>{}, Slot<1>{}, Slot<0>{});
+        issue_tile(c0, Slot<1>{}, Slot<1>{}, Slot<1>{});
+        finish(Slot<1>{});  // the previous c half (nothing stored before the first)
+        issue_tile(c0, Slot<1>{}, Slot<1>{}, Slot<2>{});
+        issue_tile(cn, Slot<0>{}, nas, Slot<0>{});
+        lds_barrier();  // (B) scores of the previous half consumed
+        f32x4_t sacc[NQT], xacc[NQT];
+        inter(qbuf(as), kbuf(as), nullptr, sacc, xacc, Slot<0>{});
+        issue_tile(cn, Slot<0>{}, nas, Slot<1>{});
+        issue_tile(cn, Slot<0>{}, nas, Slot<2>{});
+        finish_store(pb0, pnb);
+        load_vf(vfa, vbuf(as));
+        store_scores(Ps, sacc, true);
+        half(c0, 0, pb0, pnb);
+    };
+    // Half c of block c0 (in slot 1; its a half in slot AS), then the state
+    // update of the whole block.
+    auto step_c = [&](auto as) {
+        // c's loads were followed by the next a half's and one late store group
+        vm_wait<LOADS + NST>();
+        lds_barrier();  // (A)
+        finish(Slot<0>{});  // a's intra product
+        lds_barrier();  // (B)
+        f32x4_t sacc[NQT], xacc[NQT];
+        inter(qbuf(Slot<1>{}), kbuf(Slot<1>{}), kbuf(as), sacc, xacc, Slot<1>{});
+        finish_store(pb0, pnb);
+        kv_add(kbuf(as), vfa);                                        // K_a^T V_a
+        state_update<D, B, W>(kv, vfc, kbuf(Slot<1>{}), vbuf(Slot<1>{}), col0, lane);  // K_c^T V_c
+        store_scores(Ps, sacc, true);
+        store_scores(Px, xacc, false);
+        half(c0, 1, pb0, pnb);
+        if (c0.b0 + c0.nb == c0.doc_end) {  // the document ends with this block
+            vm_wait<0>();  // rare path: keeps the loop's wait bookkeeping exact
+            if (p.kv_out)
+                store_state<D, B, W>(kv, p.kv_out + (((int64_t)phys_doc(p, c0.doc) * p.H + h) * D) * D + s * W + col0,
+                                     g, li);
+#pragma unroll
+            for (int a = 0; a < NDT; ++a) kv[a][0] = zero4();
+            if (p.kv_in && cn.nb > 0 && cn.first_of_doc) {
+                add_state<D, B, W>(kv, p.kv_in + (((int64_t)phys_doc(p, cn.doc) * p.H + h) * D) * D, s * W + col0,
+                                   p.kv_in_t, g, li);
+                vm_wait<0>();
+            }
+        }
+        c0 = cn;
+    };
+    while (c0.nb > 0) {
+        step_a(Slot<0>{}, Slot<2>{});
+        step_c(Slot<0>{});
+        if (c0.nb <= 0) break;
+        step_a(Slot<2>{}, Slot<0>{});
+        step_c(Slot<2>{});
+    }
+    if (!first) {
+        lds_barrier();  // scores of the last half visible
+        finish(Slot<1>{});
+        finish_store(pb0, pnb);
+    }
+    if (p.kv_out && !p.packed) empty_doc_states<D, W>(p, u, h, s, t0, t1, tid);
+    vm_wait<0>();  // no tile load may still be writing into this workgroup's LDS when it ends
+}
+
+template <int D, int W>
+__global__ __launch_bounds__(kThreads, 1) void la_prefill_main_v2_b128(PrefillParams p) {
+    main_v2_b128<D, W>(p, blockIdx.x);
+}
+
 template <int D, int B, int W, int NS, bool DK = false>
 __global__ __launch_bounds__(kThreads, 1) void la_prefill_main_v2(PrefillParams p) {
     main_v2<D, B, W, NS, DK>(p, blockIdx.x);

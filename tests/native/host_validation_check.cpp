@@ -32,7 +32,28 @@ int main() {
     EXPECT(make_plan(8192, 1, 8, 128, 64, LA_BF16, nullptr, &p) == LA_OK);
     EXPECT(p.L % 64 == 0 && p.units == (int64_t)p.nseg * 8 * p.S && p.W * p.S == 128);
     EXPECT(make_plan(256, 1, 2, 16, 32, LA_FP32, nullptr, &p) == LA_OK && p.nseg == 1 && p.ws_bytes == 0);
-    EXPECT(make_plan(1048576, 1, 8, 128, 128, LA_BF16, nullptr, &p) == LA_OK && p.W == 32);
+    // 128-token blocks: the transpose-read loop with 64-column slices and three slots; the generic
+    // loop (32-column slices, the widest whose tiles fit) when asked for, or for the decayed variant
+    EXPECT(make_plan(1048576, 1, 8, 128, 128, LA_BF16, nullptr, &p) == LA_OK && p.W == 64 && p.variant == 2 &&
+           p.slots == 3 && p.L % 128 == 0);
+    {
+        la_prefill_opts o1{};
+        o1.variant = 1;
+        EXPECT(make_plan(1048576, 1, 8, 128, 128, LA_BF16, &o1, &p) == LA_OK && p.W == 32 && p.variant == 1);
+        EXPECT(make_plan(1048576, 1, 8, 128, 128, LA_BF16, nullptr, &p, true) == LA_OK && p.variant == 1);
+        la_prefill_opts o2{};
+        o2.slots = 2;
+        EXPECT(make_plan(1048576, 1, 8, 128, 128, LA_BF16, &o2, &p) == LA_ERR_UNSUPPORTED);
+        la_prefill_opts o3{};
+        o3.value_slices = 1;  // 128-column slices: the generic loop's tiles do not fit at 128 tokens
+        EXPECT(make_plan(8192, 1, 8, 128, 128, LA_BF16, &o3, &p) == LA_ERR_UNSUPPORTED);
+        EXPECT(make_plan(8192, 1, 8, 64, 128, LA_BF16, nullptr, &p) == LA_OK && p.W == 64 && p.variant == 2);
+        la_prefill_opts o4{};
+        o4.value_slices = 2;
+        EXPECT(make_plan(8192, 1, 8, 128, 128, LA_BF16, &o4, &p) == LA_OK && p.W == 64 && p.variant == 2);
+        o4.variant = 1;
+        EXPECT(make_plan(8192, 1, 8, 128, 128, LA_BF16, &o4, &p) == LA_ERR_UNSUPPORTED);
+    }
     EXPECT(make_plan(0, 3, 4, 64, 64, LA_BF16, nullptr, &p) == LA_OK && p.nseg == 1 && p.units == 4 * p.S);
     // every (d, block, dtype) combination has some plan
     for (int d : {16, 32, 64, 128})

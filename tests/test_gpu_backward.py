@@ -60,7 +60,8 @@ def check(q, k, v, dout, cu, kv_in, dkv_out, got, fp32, what):
 
 
 CASES = [(d, block, dtype, opts, with_states)
-         for d, block, dtype in ((128, 64, "bf16"), (64, 64, "bf16"), (128, 32, "bf16"), (32, 64, "fp32"))
+         for d, block, dtype in ((128, 64, "bf16"), (64, 64, "bf16"), (128, 128, "bf16"), (128, 32, "bf16"),
+                                 (32, 64, "fp32"))
          for opts in (dict(), dict(seg_len=2 * block, value_slices=2), dict(seg_len=block, force_scan=True),
                       dict(seg_len=max(128, 2 * block), work_list=2))
          for with_states in (False, True)]
