@@ -1,5 +1,8 @@
-// Prefill kernels for bf16 with d in {64, 128}, 64-token blocks and
-// value-column slices of at least 64 columns (the d = 128 hot path).
+// Prefill kernels for bf16 with d in {64, 128}: 64-token blocks with
+// value-column slices of at least 64 columns (the d = 128 hot path), and
+// 128-token blocks with 64-column slices (main_v2_b128, run as two 64-row
+// halves per block on the same tiles); the backward's two reverse passes can
+// share one launch (la_prefill_pair_v2).
 //
 // Same work decomposition and results contract as la_prefill_kernels.h; the
 // block loop is organised for gfx950:
