@@ -153,8 +153,10 @@ typedef struct {
     int32_t value_slices;   /* 1, 2 or 4 value-column slices per head; 0 = automatic */
     int32_t force_scan;     /* 1 = always run the separate prefix-scan kernel */
     int32_t variant;        /* block-loop kernel: 0 = automatic, 1 = the generic loop
-                               (every dtype/d/block), 2 = the transpose-read loop
-                               (bf16, d >= 64, block 64, slices of >= 64 columns);
+                               (every dtype/d/block), 2 = the transpose-read loops
+                               (bf16, d >= 64: block 64 with slices of >= 64 columns,
+                               or block 128 with slices of exactly 64 columns, plain
+                               variant only; automatic picks them whenever they apply);
                                an unavailable choice returns LA_ERR_UNSUPPORTED */
     void* main_begin_event; /* hipEvent_t stamped when the block-loop kernel starts
                                executing, or NULL (the kernel is then launched with
@@ -162,7 +164,8 @@ typedef struct {
     void* main_end_event;   /* hipEvent_t stamped when it completes, or NULL */
     int32_t slots;          /* tile slots of the transpose-read loop: 0 = automatic
                                (3 on segments of 16 blocks or more), 2, or 3 (loads
-                               two blocks ahead; d = 128 only) */
+                               two blocks ahead; d = 128 only).  The 128-token loop
+                               always runs 3 (2 returns LA_ERR_UNSUPPORTED) */
     int32_t forward_states; /* la_prefill_backward only (the forward entry points
                                ignore it): 1 = `workspace` may hold the segment states
                                of a forward call (la_prefill / _ex / _resume) on the
