@@ -20,6 +20,7 @@ template __global__ void v2::la_prefill_main_v2<64, 64, 64, 2, true>(PrefillPara
 template __global__ void v2::la_segment_state_v2<128, 64, 128, true>(PrefillParams);
 template __global__ void v2::la_segment_state_v2<128, 64, 64, true>(PrefillParams);
 template __global__ void v2::la_segment_state_v2<64, 64, 64, true>(PrefillParams);
+template __global__ void v2::la_prefill_main_v2_b128<128, 128>(PrefillParams);
 template __global__ void v2::la_prefill_main_v2_b128<128, 64>(PrefillParams);
 template __global__ void v2::la_prefill_main_v2_b128<64, 64>(PrefillParams);
 template __global__ void v2::la_prefill_pair_v2<128, 64, 128, 2>(PrefillParams, PrefillParams);

@@ -5,11 +5,10 @@ namespace la {
 namespace {
 
 // The transpose-read block loops (la_prefill_v2.h) cover bf16, d >= 64, and
-// 64-token blocks with slices of at least 64 value columns or 128-token
-// blocks with slices of exactly 64.
+// 64-token or 128-token blocks with slices of at least 64 value columns.
 template <typename T, int D, int B, int W>
 constexpr bool has_v2() {
-    return sizeof(T) == 2 && D >= 64 && ((B == 64 && W >= 64) || (B == 128 && W == 64));
+    return sizeof(T) == 2 && D >= 64 && ((B == 64 && W >= 64) || (B == 128 && (W == 64 || W == 128)));
 }
 
 // Launches the block-loop kernel; with events, through hipExtLaunchKernel, so

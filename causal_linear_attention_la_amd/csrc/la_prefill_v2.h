@@ -952,7 +952,7 @@ __device__ __forceinline__ void main_v2_b128(const PrefillParams& p, const int64
     constexpr int B = 64;  // rows of a half
     using G = Geo<D, B, W>;
     constexpr int NQT = G::NQT, NCW = G::NCW, NDT = G::NDT;
-    static_assert(NQT == kWaves && NCW == 1, "64-column slices, key band w per wave");
+    static_assert(NQT == kWaves && (NCW == 1 || NCW == 2), "key band w per wave; one or two column tiles");
     constexpr int PP = B;
     constexpr int QN = B * D, VN = B * W;
     __shared__ __align__(16) bf16_t Q0[QN], Q1[QN], Q2[QN];
@@ -961,6 +961,11 @@ __device__ __forceinline__ void main_v2_b128(const PrefillParams& p, const int64
     __shared__ __align__(16) bf16_t Ps[B * PP];  // masked scores of the half (P_aa or P_cc)
     __shared__ __align__(16) bf16_t Px[B * PP];  // c's queries against a's keys (P_ca)
     constexpr int NST = G::STORES, LOADS = G::LOADS;
+    // Full width (two column tiles per wave) has no registers to keep V^T
+    // fragments or packed rows from one iteration to the next: there the
+    // intra product reads its V^T fragments from LDS (a half's tiles stay in
+    // place until after it) and stores its rows at once.
+    constexpr bool LIGHT = NCW == 2;
     auto qbuf = [&](auto slot) -> bf16_t* {
         constexpr int X = decltype(slot)::value;
         if constexpr (X == 0) return Q0;
@@ -1019,14 +1024,19 @@ __device__ __forceinline__ void main_v2_b128(const PrefillParams& p, const int64
 
     f32x4_t kv[NDT][NCW];
 #pragma unroll
-    for (int a = 0; a < NDT; ++a) kv[a][0] = zero4();
+    for (int a = 0; a < NDT; ++a)
+#pragma unroll
+        for (int c = 0; c < NCW; ++c) kv[a][c] = zero4();
     f32x4_t oacc[NQT][NCW];
 #pragma unroll
-    for (int b = 0; b < NQT; ++b) oacc[b][0] = zero4();
+    for (int b = 0; b < NQT; ++b)
+#pragma unroll
+        for (int c = 0; c < NCW; ++c) oacc[b][c] = zero4();
     Frag<bf16_t> vfa[NCW][B / 32];  // V_a^T fragments: a's intra product and c's cross term
     Frag<bf16_t> vfc[NCW][B / 32];  // V_c^T fragments
     u32x4_t opk[NQT];
 
+    int pb0 = t0, pnb = 0;  // the half whose rows the next finish stores
     // Half HF (0 = a, 1 = c) of block c: its first token and length (0 past the end).
     auto half = [&](const Cursor& c, int hf, int& b0h, int& nbh) {
         const int nb = max(c.nb, 0);
@@ -1046,38 +1056,6 @@ __device__ __forceinline__ void main_v2_b128(const PrefillParams& p, const int64
     };
     // O^T += V^T P^T for the previous half (and, after a c half, + V_a^T P_ca^T),
     // then its rows are packed for the late stores.
-    auto finish = [&](auto cross) {
-        Frag<bf16_t> pfs[6];  // (band, chunk) = (0,0) (1,0) (2,0) (2,1) (3,0) (3,1)
-#pragma unroll
-        for (int b = 0, n = 0; b < NQT; ++b)
-#pragma unroll
-            for (int kc = 0; kc <= b / 2; ++kc, ++n) load_row<PP>(pfs[n], Ps, 16 * b + li, 32 * kc, g);
-        if constexpr (decltype(cross)::value) {
-#pragma unroll
-            for (int b = 0, n = 0; b < NQT; ++b)
-#pragma unroll
-                for (int kc = 0; kc <= b / 2; ++kc, ++n) mma(oacc[b][0], vfc[0][kc], pfs[n]);
-#pragma unroll
-            for (int b = 0; b < NQT; ++b) {
-                Frag<bf16_t> xf[2];
-                load_row<PP>(xf[0], Px, 16 * b + li, 0, g);
-                load_row<PP>(xf[1], Px, 16 * b + li, 32, g);
-                mma(oacc[b][0], vfa[0][0], xf[0]);
-                mma(oacc[b][0], vfa[0][1], xf[1]);
-            }
-        } else {
-#pragma unroll
-            for (int b = 0, n = 0; b < NQT; ++b)
-#pragma unroll
-                for (int kc = 0; kc <= b / 2; ++kc, ++n) mma(oacc[b][0], vfa[0][kc], pfs[n]);
-        }
-#pragma unroll
-        for (int b = 0; b < NQT; ++b) {
-            opk[b].x = pack2(oacc[b][0][0], oacc[b][0][1]);
-            opk[b].y = pack2(oacc[b][0][2], oacc[b][0][3]);
-            oacc[b][0] = zero4();
-        }
-    };
     auto finish_store = [&](int pb0, int pnb) {
         const __amdgpu_buffer_rsrc_t ro =
             make_rsrc(og + ((int64_t)phys_block(p, pb0, pnb) * p.H + h) * D + s * W + col0, (uint32_t)pnb * row_bytes);
@@ -1085,11 +1063,77 @@ __device__ __forceinline__ void main_v2_b128(const PrefillParams& p, const int64
         for (int b = 0; b < NQT; ++b) {
             const int r = 16 * b + li;
             const uint32_t off = (uint32_t)(p.rev ? pnb - 1 - r : r) * row_bytes;
-            u32x2_t v;
-            v.x = opk[b].x;
-            v.y = opk[b].y;
-            __builtin_amdgcn_raw_buffer_store_b64(v, ro, off + (4 * g) * 2, 0, 0);
+            if constexpr (NCW == 2) {
+                __builtin_amdgcn_raw_buffer_store_b128(opk[b], ro, off + (8 * g) * 2, 0, 0);
+            } else {
+                u32x2_t v;
+                v.x = opk[b].x;
+                v.y = opk[b].y;
+                __builtin_amdgcn_raw_buffer_store_b64(v, ro, off + (4 * g) * 2, 0, 0);
+            }
         }
+    };
+    auto load_vf = [&](Frag<bf16_t> (&vf)[NCW][B / 32], const bf16_t* Vs) {
+#pragma unroll
+        for (int kc = 0; kc < B / 32; ++kc)
+#pragma unroll
+            for (int c = 0; c < NCW; ++c) {
+                if constexpr (NCW == 2) load_tr<W, 8>(vf[c][kc], Vs, 32 * kc, col0, 4 * c, lane);
+                else load_tr<W, 4>(vf[c][kc], Vs, 32 * kc, col0 + 16 * c, 0, lane);
+            }
+    };
+    // (LIGHT: the previous half's rows are stored here; Va = its block's a half's V tile)
+    auto finish = [&](auto cross, const bf16_t* Va) {
+        constexpr bool X = decltype(cross)::value;
+        if constexpr (LIGHT) {
+            load_vf(vfa, Va);
+            if constexpr (X) load_vf(vfc, vbuf(Slot<1>{}));
+        }
+        auto& vf = X ? vfc : vfa;  // the half's own V^T fragments
+        if constexpr (NCW == 1) {  // registers to fetch every P fragment first
+            Frag<bf16_t> pfs[6];  // (band, chunk) = (0,0) (1,0) (2,0) (2,1) (3,0) (3,1)
+#pragma unroll
+            for (int b = 0, n = 0; b < NQT; ++b)
+#pragma unroll
+                for (int kc = 0; kc <= b / 2; ++kc, ++n) load_row<PP>(pfs[n], Ps, 16 * b + li, 32 * kc, g);
+#pragma unroll
+            for (int b = 0, n = 0; b < NQT; ++b)
+#pragma unroll
+                for (int kc = 0; kc <= b / 2; ++kc, ++n) mma(oacc[b][0], vf[0][kc], pfs[n]);
+        } else {
+#pragma unroll
+            for (int b = 0; b < NQT; ++b)
+#pragma unroll
+                for (int kc = 0; kc <= b / 2; ++kc) {
+                    Frag<bf16_t> pf;
+                    load_row<PP>(pf, Ps, 16 * b + li, 32 * kc, g);
+#pragma unroll
+                    for (int c = 0; c < NCW; ++c) mma(oacc[b][c], vf[c][kc], pf);
+                }
+        }
+        if constexpr (X) {  // c's queries against a's keys
+#pragma unroll
+            for (int b = 0; b < NQT; ++b)
+#pragma unroll
+                for (int kc = 0; kc < 2; ++kc) {
+                    Frag<bf16_t> xf;
+                    load_row<PP>(xf, Px, 16 * b + li, 32 * kc, g);
+#pragma unroll
+                    for (int c = 0; c < NCW; ++c) mma(oacc[b][c], vfa[c][kc], xf);
+                }
+        }
+#pragma unroll
+        for (int b = 0; b < NQT; ++b) {
+            opk[b].x = pack2(oacc[b][0][0], oacc[b][0][1]);
+            opk[b].y = pack2(oacc[b][0][2], oacc[b][0][3]);
+            if constexpr (NCW == 2) {
+                opk[b].z = pack2(oacc[b][1][0], oacc[b][1][1]);
+                opk[b].w = pack2(oacc[b][1][2], oacc[b][1][3]);
+            }
+#pragma unroll
+            for (int c = 0; c < NCW; ++c) oacc[b][c] = zero4();
+        }
+        if constexpr (LIGHT) finish_store(pb0, pnb);
     };
     // inter product O^T += KV^T Q^T of the half in Qs, with its masked scores
     // S^T = K_w Q^T (key band w of Ks), and, with Ka, the unmasked scores of
@@ -1103,21 +1147,36 @@ __device__ __forceinline__ void main_v2_b128(const PrefillParams& p, const int64
         }
 #pragma unroll
         for (int m = 0; m < D / 32; ++m) {
-            Frag<bf16_t> kvf;
-            kvf.lo = make_uint2(pack2(kv[2 * m][0][0], kv[2 * m][0][1]), pack2(kv[2 * m][0][2], kv[2 * m][0][3]));
-            kvf.hi = make_uint2(pack2(kv[2 * m + 1][0][0], kv[2 * m + 1][0][1]),
-                                pack2(kv[2 * m + 1][0][2], kv[2 * m + 1][0][3]));
+            Frag<bf16_t> kvf[NCW];
+#pragma unroll
+            for (int c = 0; c < NCW; ++c) {
+                kvf[c].lo = make_uint2(pack2(kv[2 * m][c][0], kv[2 * m][c][1]), pack2(kv[2 * m][c][2], kv[2 * m][c][3]));
+                kvf[c].hi = make_uint2(pack2(kv[2 * m + 1][c][0], kv[2 * m + 1][c][1]),
+                                       pack2(kv[2 * m + 1][c][2], kv[2 * m + 1][c][3]));
+            }
             Frag<bf16_t> kf, kx;
             load_row<D>(kf, Ks, 16 * wave + li, 32 * m, g);
             if constexpr (decltype(with_cross)::value) load_row<D>(kx, Ka, 16 * wave + li, 32 * m, g);
-            Frag<bf16_t> qfs[NQT];
+            if constexpr (NCW == 1) {  // all Q fragments of the chunk first
+                Frag<bf16_t> qfs[NQT];
 #pragma unroll
-            for (int b = 0; b < NQT; ++b) load_row<D>(qfs[b], Qs, 16 * b + li, 32 * m, g);
+                for (int b = 0; b < NQT; ++b) load_row<D>(qfs[b], Qs, 16 * b + li, 32 * m, g);
 #pragma unroll
-            for (int b = 0; b < NQT; ++b) {
-                mma(oacc[b][0], kvf, qfs[b]);
-                mma(sacc[b], kf, qfs[b]);
-                if constexpr (decltype(with_cross)::value) mma(xacc[b], kx, qfs[b]);
+                for (int b = 0; b < NQT; ++b) {
+                    mma(oacc[b][0], kvf[0], qfs[b]);
+                    mma(sacc[b], kf, qfs[b]);
+                    if constexpr (decltype(with_cross)::value) mma(xacc[b], kx, qfs[b]);
+                }
+            } else {
+#pragma unroll
+                for (int b = 0; b < NQT; ++b) {
+                    Frag<bf16_t> qf;
+                    load_row<D>(qf, Qs, 16 * b + li, 32 * m, g);
+#pragma unroll
+                    for (int c = 0; c < NCW; ++c) mma(oacc[b][c], kvf[c], qf);
+                    mma(sacc[b], kf, qf);
+                    if constexpr (decltype(with_cross)::value) mma(xacc[b], kx, qf);
+                }
             }
         }
     };
@@ -1131,11 +1190,6 @@ __device__ __forceinline__ void main_v2_b128(const PrefillParams& p, const int64
             store4(P + soff<PP>(16 * b + li, 16 * wave + 4 * g), acc[b][0], acc[b][1], acc[b][2], acc[b][3]);
         }
     };
-    // V_a^T fragments (as state_update loads them)
-    auto load_vf = [&](Frag<bf16_t> (&vf)[NCW][B / 32], const bf16_t* Vs) {
-#pragma unroll
-        for (int kc = 0; kc < B / 32; ++kc) load_tr<W, 4>(vf[0][kc], Vs, 32 * kc, col0, 0, lane);
-    };
     // KV += K^T V with the V^T fragments already loaded
     auto kv_add = [&](const bf16_t* Ks, const Frag<bf16_t> (&vf)[NCW][B / 32]) {
 #pragma unroll
@@ -1144,7 +1198,8 @@ __device__ __forceinline__ void main_v2_b128(const PrefillParams& p, const int64
             for (int a = 0; a < NDT; ++a) {
                 Frag<bf16_t> kf;
                 load_tr<D, 8>(kf, Ks, 32 * kc, 32 * (a >> 1), 4 * (a & 1), lane);
-                mma(kv[a][0], kf, vf[0][kc]);
+#pragma unroll
+                for (int c = 0; c < NCW; ++c) mma(kv[a][c], kf, vf[c][kc]);
             }
     };
 
@@ -1161,23 +1216,23 @@ __device__ __forceinline__ void main_v2_b128(const PrefillParams& p, const int64
     if (p.kv_in && c0.nb > 0)
         add_state<D, B, W>(kv, p.kv_in + (((int64_t)phys_doc(p, c0.doc) * p.H + h) * D) * D, s * W + col0, p.kv_in_t,
                            g, li);
-    int pb0 = t0, pnb = 0;  // the half whose rows the next finish stores
     bool first = true;
     Cursor cn = c0;  // the next block
-    // Half a of block c0, in slot AS; the next block's a half goes to slot NAS.
+    // Half a of block c0, in slot AS; the next block's a half goes to slot NAS
+    // (where the previous block's a half was).
     auto step_a = [&](auto as, auto nas) {
         cn = c0;
         cursor_next(cn, cuv, p.num_seqs, t1, 2 * B);
-        // a's loads were issued before the previous block's two halves stored
-        // their rows (one late store group each); the first block's, by the
-        // prologue alone
+        // a's loads were issued before the previous block's halves stored their
+        // rows (one store group each, or only c's at once with LIGHT); the
+        // first block's, by the prologue alone
         if (first) vm_wait<0>();
-        else vm_wait<2 * NST>();
+        else vm_wait<LIGHT ? NST : 2 * NST>();
         first = false;
         lds_barrier();  // (A) a visible; the previous block's tiles no longer read
         issue_tile(c0, Slot<1>{}, Slot<1>{}, Slot<0>{});
         issue_tile(c0, Slot<1>{}, Slot<1>{}, Slot<1>{});
-        finish(Slot<1>{});  // the previous c half (nothing stored before the first)
+        finish(Slot<1>{}, vbuf(nas));  // the previous c half (nothing stored before the first)
         issue_tile(c0, Slot<1>{}, Slot<1>{}, Slot<2>{});
         issue_tile(cn, Slot<0>{}, nas, Slot<0>{});
         lds_barrier();  // (B) scores of the previous half consumed
@@ -1185,26 +1240,58 @@ __device__ __forceinline__ void main_v2_b128(const PrefillParams& p, const int64
         inter(qbuf(as), kbuf(as), nullptr, sacc, xacc, Slot<0>{});
         issue_tile(cn, Slot<0>{}, nas, Slot<1>{});
         issue_tile(cn, Slot<0>{}, nas, Slot<2>{});
-        finish_store(pb0, pnb);
-        load_vf(vfa, vbuf(as));
+        if constexpr (!LIGHT) {
+            finish_store(pb0, pnb);
+            load_vf(vfa, vbuf(as));
+        }
         store_scores(Ps, sacc, true);
         half(c0, 0, pb0, pnb);
     };
     // Half c of block c0 (in slot 1; its a half in slot AS), then the state
     // update of the whole block.
     auto step_c = [&](auto as) {
-        // c's loads were followed by the next a half's and one late store group
-        vm_wait<LOADS + NST>();
+        // c's loads were followed by the next a half's (and one late store group)
+        vm_wait<LIGHT ? LOADS : LOADS + NST>();
         lds_barrier();  // (A)
-        finish(Slot<0>{});  // a's intra product
+        finish(Slot<0>{}, vbuf(as));  // a's intra product
         lds_barrier();  // (B)
-        f32x4_t sacc[NQT], xacc[NQT];
-        inter(qbuf(Slot<1>{}), kbuf(Slot<1>{}), kbuf(as), sacc, xacc, Slot<1>{});
-        finish_store(pb0, pnb);
-        kv_add(kbuf(as), vfa);                                        // K_a^T V_a
-        state_update<D, B, W>(kv, vfc, kbuf(Slot<1>{}), vbuf(Slot<1>{}), col0, lane);  // K_c^T V_c
-        store_scores(Ps, sacc, true);
-        store_scores(Px, xacc, false);
+        if constexpr (LIGHT) {
+            // (full width: the cross scores in a second pass over Q_c, so that
+            // the two score sets are never live together)
+            {
+                f32x4_t sacc[NQT], xacc[NQT];
+                inter(qbuf(Slot<1>{}), kbuf(Slot<1>{}), nullptr, sacc, xacc, Slot<0>{});
+                store_scores(Ps, sacc, true);
+            }
+            {
+                f32x4_t xacc[NQT];
+#pragma unroll
+                for (int b = 0; b < NQT; ++b) xacc[b] = zero4();
+#pragma unroll
+                for (int m = 0; m < D / 32; ++m) {
+                    Frag<bf16_t> kx;
+                    load_row<D>(kx, kbuf(as), 16 * wave + li, 32 * m, g);
+#pragma unroll
+                    for (int b = 0; b < NQT; ++b) {
+                        Frag<bf16_t> qf;
+                        load_row<D>(qf, qbuf(Slot<1>{}), 16 * b + li, 32 * m, g);
+                        mma(xacc[b], kx, qf);
+                    }
+                }
+                store_scores(Px, xacc, false);
+            }
+            load_vf(vfa, vbuf(as));
+            kv_add(kbuf(as), vfa);                                                         // K_a^T V_a
+            state_update<D, B, W>(kv, vfc, kbuf(Slot<1>{}), vbuf(Slot<1>{}), col0, lane);  // K_c^T V_c
+        } else {
+            f32x4_t sacc[NQT], xacc[NQT];
+            inter(qbuf(Slot<1>{}), kbuf(Slot<1>{}), kbuf(as), sacc, xacc, Slot<1>{});
+            finish_store(pb0, pnb);
+            kv_add(kbuf(as), vfa);                                                         // K_a^T V_a
+            state_update<D, B, W>(kv, vfc, kbuf(Slot<1>{}), vbuf(Slot<1>{}), col0, lane);  // K_c^T V_c
+            store_scores(Ps, sacc, true);
+            store_scores(Px, xacc, false);
+        }
         half(c0, 1, pb0, pnb);
         if (c0.b0 + c0.nb == c0.doc_end) {  // the document ends with this block
             vm_wait<0>();  // rare path: keeps the loop's wait bookkeeping exact
@@ -1212,7 +1299,9 @@ __device__ __forceinline__ void main_v2_b128(const PrefillParams& p, const int64
                 store_state<D, B, W>(kv, p.kv_out + (((int64_t)phys_doc(p, c0.doc) * p.H + h) * D) * D + s * W + col0,
                                      g, li);
 #pragma unroll
-            for (int a = 0; a < NDT; ++a) kv[a][0] = zero4();
+            for (int a = 0; a < NDT; ++a)
+#pragma unroll
+                for (int c = 0; c < NCW; ++c) kv[a][c] = zero4();
             if (p.kv_in && cn.nb > 0 && cn.first_of_doc) {
                 add_state<D, B, W>(kv, p.kv_in + (((int64_t)phys_doc(p, cn.doc) * p.H + h) * D) * D, s * W + col0,
                                    p.kv_in_t, g, li);
@@ -1221,17 +1310,27 @@ __device__ __forceinline__ void main_v2_b128(const PrefillParams& p, const int64
         }
         c0 = cn;
     };
-    while (c0.nb > 0) {
-        step_a(Slot<0>{}, Slot<2>{});
-        step_c(Slot<0>{});
-        if (c0.nb <= 0) break;
-        step_a(Slot<2>{}, Slot<0>{});
-        step_c(Slot<2>{});
-    }
-    if (!first) {
+    // the last block's c half (its a half in slot AS)
+    auto last = [&](auto as) {
         lds_barrier();  // scores of the last half visible
-        finish(Slot<1>{});
-        finish_store(pb0, pnb);
+        finish(Slot<1>{}, vbuf(as));
+        if constexpr (!LIGHT) finish_store(pb0, pnb);
+    };
+    if (c0.nb > 0) {
+        while (true) {
+            step_a(Slot<0>{}, Slot<2>{});
+            step_c(Slot<0>{});
+            if (c0.nb <= 0) {
+                last(Slot<0>{});
+                break;
+            }
+            step_a(Slot<2>{}, Slot<0>{});
+            step_c(Slot<2>{});
+            if (c0.nb <= 0) {
+                last(Slot<2>{});
+                break;
+            }
+        }
     }
     if (p.kv_out && !p.packed) empty_doc_states<D, W>(p, u, h, s, t0, t1, tid);
     vm_wait<0>();  // no tile load may still be writing into this workgroup's LDS when it ends

@@ -32,9 +32,9 @@ int main() {
     EXPECT(make_plan(8192, 1, 8, 128, 64, LA_BF16, nullptr, &p) == LA_OK);
     EXPECT(p.L % 64 == 0 && p.units == (int64_t)p.nseg * 8 * p.S && p.W * p.S == 128);
     EXPECT(make_plan(256, 1, 2, 16, 32, LA_FP32, nullptr, &p) == LA_OK && p.nseg == 1 && p.ws_bytes == 0);
-    // 128-token blocks: the transpose-read loop with 64-column slices and three slots; the generic
-    // loop (32-column slices, the widest whose tiles fit) when asked for, or for the decayed variant
-    EXPECT(make_plan(1048576, 1, 8, 128, 128, LA_BF16, nullptr, &p) == LA_OK && p.W == 64 && p.variant == 2 &&
+    // 128-token blocks: the transpose-read loop at full width with three slots; the generic loop
+    // (32-column slices, the widest whose tiles fit) when asked for, or for the decayed variant
+    EXPECT(make_plan(1048576, 1, 8, 128, 128, LA_BF16, nullptr, &p) == LA_OK && p.W == 128 && p.variant == 2 &&
            p.slots == 3 && p.L % 128 == 0);
     {
         la_prefill_opts o1{};
@@ -45,7 +45,10 @@ int main() {
         o2.slots = 2;
         EXPECT(make_plan(1048576, 1, 8, 128, 128, LA_BF16, &o2, &p) == LA_ERR_UNSUPPORTED);
         la_prefill_opts o3{};
-        o3.value_slices = 1;  // 128-column slices: the generic loop's tiles do not fit at 128 tokens
+        o3.value_slices = 1;  // full width: the transpose-read loop only (the generic loop's tiles do not fit)
+        EXPECT(make_plan(8192, 1, 8, 128, 128, LA_BF16, &o3, &p) == LA_OK && p.W == 128 && p.variant == 2 &&
+               p.slots == 3);
+        o3.variant = 1;
         EXPECT(make_plan(8192, 1, 8, 128, 128, LA_BF16, &o3, &p) == LA_ERR_UNSUPPORTED);
         EXPECT(make_plan(8192, 1, 8, 64, 128, LA_BF16, nullptr, &p) == LA_OK && p.W == 64 && p.variant == 2);
         la_prefill_opts o4{};
