@@ -945,8 +945,10 @@ __device__ __forceinline__ void main_v2(const PrefillParams& p, const int64_t wg
 // Slots: a halves alternate between slots 0 and 2, c halves use slot 1, so
 // a's tiles stay in place while c runs.  Iteration a loads the same block's c
 // half (one iteration ahead) and the next block's a half (two ahead); iteration
-// c loads nothing.  The loop is unrolled over two blocks, so every slot and
-// every wait count is fixed at compile time.
+// c loads nothing.  A tile load into a slot is issued only after the barrier
+// past which no wave reads that slot's previous contents.  The loop is
+// unrolled over two blocks, so every slot and every wait count is fixed at
+// compile time.
 template <int D, int W>
 __device__ __forceinline__ void main_v2_b128(const PrefillParams& p, const int64_t wg) {
     constexpr int B = 64;  // rows of a half
@@ -1233,9 +1235,13 @@ __device__ __forceinline__ void main_v2_b128(const PrefillParams& p, const int64
         issue_tile(c0, Slot<1>{}, Slot<1>{}, Slot<0>{});
         issue_tile(c0, Slot<1>{}, Slot<1>{}, Slot<1>{});
         finish(Slot<1>{}, vbuf(nas));  // the previous c half (nothing stored before the first)
+        // c's V tile goes where the previous c half's was, which finish may
+        // read (full width): only once every wave is past it.  The next a
+        // half's Q follows it, so that a's three tiles stay the last loads
+        // issued before the c half's wait.
+        lds_barrier();  // (B) scores and V tiles of the previous half consumed
         issue_tile(c0, Slot<1>{}, Slot<1>{}, Slot<2>{});
         issue_tile(cn, Slot<0>{}, nas, Slot<0>{});
-        lds_barrier();  // (B) scores of the previous half consumed
         f32x4_t sacc[NQT], xacc[NQT];
         inter(qbuf(as), kbuf(as), nullptr, sacc, xacc, Slot<0>{});
         issue_tile(cn, Slot<0>{}, nas, Slot<1>{});
