@@ -154,8 +154,9 @@ def cpu_model() -> str:
 
 def stream_ceilings(la, torch, hip) -> dict:
     """Bandwidth (GB/s of bytes read + written) of the contiguous streams in
-    la_bench_stream over 1 GiB per source: the best of 128 to 1024
-    workgroups, plain and non-temporal accesses, two rounds of 20 passes."""
+    la_bench_stream over 1 GiB per source: the best of 128 to 65536
+    workgroups (up to a few resident per CU, as the decode step runs, and
+    beyond), plain and non-temporal accesses, two rounds of 20 passes."""
     lib = la.load()
     bufs = [torch.empty(GIB, dtype=torch.uint8, device="cuda").fill_(i + 1) for i in range(4)]
     P = lambda t: ctypes.c_void_p(t.data_ptr())
@@ -164,7 +165,7 @@ def stream_ceilings(la, torch, hip) -> dict:
     for mode, name, nbytes in ((0, "copy_1r1w", 2 * GIB), (1, "stream_3r1w", 4 * GIB)):
         best, how = 0.0, None
         for _ in range(2):
-            for wgs in (128, 256, 512, 1024):
+            for wgs in (128, 256, 512, 1024, 2048, 4096, 16384, 65536):
                 for nt in (0, 1):
                     def fn():
                         st = lib.la_bench_stream(mode, P(bufs[0]), P(bufs[1]), P(bufs[2]), P(bufs[3]), GIB, wgs, nt,
