@@ -806,13 +806,23 @@ __device__ __forceinline__ void main_v2(const PrefillParams& p, const int64_t wg
             else vm_wait<G::LOADS + NST>();
         }
         lds_barrier();  // (A) block j visible; block j-1's tiles no longer read
-        issue_tile(cf, Slot<FILL>{}, Slot<0>{});
+        // Where the next tiles' Q and K go out: around the intra product with
+        // three slots (tiles two blocks ahead), after it with two, where that
+        // measured faster on short segments (plain loop; the decayed one keeps
+        // the first placement).  Either way after (A), past which no wave reads
+        // their slot.
+        constexpr bool QK_AFTER = NS == 2 && !DK;
+        if constexpr (!QK_AFTER) issue_tile(cf, Slot<FILL>{}, Slot<0>{});
         // block j-1's intra product (and its rows, unless they are stored
         // late); in the first iteration pnb = 0 and the stores (of whatever
         // the accumulators hold) fall outside the buffer range
         finish(pb0, pnb);
-        issue_tile(cf, Slot<FILL>{}, Slot<1>{});
+        if constexpr (!QK_AFTER) issue_tile(cf, Slot<FILL>{}, Slot<1>{});
         lds_barrier();  // (B) scores of block j-1 consumed
+        if constexpr (QK_AFTER) {
+            issue_tile(cf, Slot<FILL>{}, Slot<0>{});
+            issue_tile(cf, Slot<FILL>{}, Slot<1>{});
+        }
 
         const bf16_t* Qs = qbuf(slot);
         const bf16_t* Ks = kbuf(slot);
