@@ -211,6 +211,14 @@ struct Geo {
     static_assert(W == 64 || W == 128, "row widths");
 };
 
+// The token part of a full block's decay weights for state_update: lane
+// group g holds tokens 32 kc + 8 g + e, and lambda^(31 - 8 g - e) is the
+// weight of that token within its 32-token chunk.
+__device__ __forceinline__ void full_weights(float (&wfull)[8], float l2, int lane) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) wfull[e] = decay_pow(l2, 31 - 8 * (lane >> 4) - e);
+}
+
 // KV[:, own cols] += K^T V over one block; keeps the V^T fragments (A operands
 // of the intra product).  Decayed variant (DK, l2 = log2 lambda, nb tokens in
 // the block): the state is kept scaled, KV = 2^lc U, so that the fade
@@ -218,11 +226,13 @@ struct Geo {
 // fade_scale) and this update adds sum_c lambda^(nb - 1 - c) 2^-lc k_c^T v_c to
 // U, the weights applied to a bf16 copy of the V^T fragments (lane group g
 // holds tokens 32 kc + 8 g + e of each chunk); the kept fragments stay
-// unscaled.
+// unscaled.  wfull (optional): the lane's lambda^(31 - 8 g - e) (full_weights),
+// so that a full block's weights take one power per chunk instead of one per
+// token: lambda^(B - 1 - tok) 2^-lc = wfull[e] lambda^(32 (B/32 - 1 - kc)) 2^-lc.
 template <int D, int B, int W, bool DK = false, int NA, int NC, int NK>
 __device__ __forceinline__ void state_update(f32x4_t (&kv)[NA][NC], Frag<bf16_t> (&vfr)[NC][NK], const bf16_t* Ks,
                                              const bf16_t* Vs, int col0, int lane, float l2 = 0.f, int nb = B,
-                                             float lc = 0.f) {
+                                             float lc = 0.f, const float* wfull = nullptr) {
     using G = Geo<D, B, W>;
     static_assert(NA == G::NDT && NC == G::NCW && NK == B / 32, "tile counts");
 #pragma unroll
@@ -235,10 +245,16 @@ __device__ __forceinline__ void state_update(f32x4_t (&kv)[NA][NC], Frag<bf16_t>
         Frag<bf16_t> vs[G::NCW];
         if constexpr (DK) {
             float w[8];
+            if (wfull && nb == B) {
+                const float sc = decay_pow(l2, 32 * (B / 32 - 1 - kc), lc);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int tok = 32 * kc + 8 * (lane >> 4) + e;
-                w[e] = tok < nb ? decay_pow(l2, nb - 1 - tok, lc) : 0.f;
+                for (int e = 0; e < 8; ++e) w[e] = wfull[e] * sc;
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int tok = 32 * kc + 8 * (lane >> 4) + e;
+                    w[e] = tok < nb ? decay_pow(l2, nb - 1 - tok, lc) : 0.f;
+                }
             }
 #pragma unroll
             for (int c = 0; c < G::NCW; ++c) vs[c] = scale_frag(vfr[c][kc], w);
@@ -397,6 +413,8 @@ __global__ __launch_bounds__(kThreads, 1) void la_segment_state_v2(PrefillParams
     // decayed variant: the state is faded to the end of the piece
     const float l2 = DK ? log2f(p.decay[h]) : 0.f;
     float lc = 0.f;  // decayed: the state is 2^lc kv (fade_scale)
+    float wfull[8];
+    if constexpr (DK) full_weights(wfull, l2, lane);
     DmaTile<D> dk;
     DmaTile<W> dv;
     dk.init(wave, lane, row_bytes);
@@ -449,12 +467,12 @@ __global__ __launch_bounds__(kThreads, 1) void la_segment_state_v2(PrefillParams
                 if (nb0 > 0) fade_scale(kv, lc, l2, nb0);
             }
             state_update<D, B, W, DK>(kv, vfr, kbuf(Slot<1 - SLOT>{}), vbuf(Slot<1 - SLOT>{}), col0, lane, l2, nb0,
-                                      lc);
+                                      lc, DK ? wfull : nullptr);
             if constexpr (DK) {
                 if (nb1 > 0) fade_scale(kv, lc, l2, nb1);
             }
             state_update<D, B, W, DK>(kv, vfr, kbuf(Slot<1 - SLOT>{}) + B * D, vbuf(Slot<1 - SLOT>{}) + B * W, col0,
-                                      lane, l2, nb1, lc);
+                                      lane, l2, nb1, lc, DK ? wfull : nullptr);
         }
         ++i;
     };
@@ -612,10 +630,11 @@ __device__ __forceinline__ void main_v2(const PrefillParams& p, const int64_t wg
     // do not change from block to block: lambda^(query - key) on the scores
     // (0 above the diagonal: the causal mask), lambda^(query + 1) on the inter
     // product of query row 16 b + li.
-    float l2 = 0.f, sfac[DK ? NQT : 1][4], ifac[DK ? NQT : 1];
+    float l2 = 0.f, sfac[DK ? NQT : 1][4], ifac[DK ? NQT : 1], wfull[8];
     float lc = 0.f;  // decayed: the state is 2^lc kv (fade_scale)
     if constexpr (DK) {
         l2 = log2f(p.decay[h]);
+        full_weights(wfull, l2, lane);
 #pragma unroll
         for (int b = 0; b < NQT; ++b) {
             ifac[b] = decay_pow(l2, 16 * b + li + 1);
@@ -879,7 +898,7 @@ __device__ __forceinline__ void main_v2(const PrefillParams& p, const int64_t wg
         if constexpr (LATE) finish_store(pb0, pnb);
         // state: KV += K^T V (after the inter product read it)
         if constexpr (DK) fade_scale(kv, lc, l2, c0.nb);
-        state_update<D, B, W, DK>(kv, vfr, Ks, Vs, col0, lane, l2, c0.nb, lc);
+        state_update<D, B, W, DK>(kv, vfr, Ks, Vs, col0, lane, l2, c0.nb, lc, DK ? wfull : nullptr);
 
         // P[query][key] for keys of band w: causal mask (key <= query), the
         // tiles above the diagonal come out as zeros
