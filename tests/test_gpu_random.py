@@ -1,7 +1,8 @@
 """Randomised parity: seeded draws of shapes, packed-document layouts and
 every decomposition knob (segment length, value slices, scan, tile slots,
 block loop, work list, incoming states), each prefill checked against the fp64 oracle,
-and a share of them through the backward as well.  Draws whose options the
+and a share of them through the backward and the decayed prefill (per-head
+factors drawn from 0, 1, (0.9, 1] and [0, 1)) as well.  Draws whose options the
 planner rejects must be rejected (LA_ERR_UNSUPPORTED) before anything runs."""
 import numpy as np
 import pytest
@@ -53,7 +54,13 @@ def draw(seed):
     backward = r.random() < 0.35
     if r.random() < 0.35:  # drawn last: the earlier knobs of every seed stay as they were
         opts["work_list"] = int(r.choice([1, 2]))
-    return dict(d=d, dtype=dtype, block=block, H=H, lens=lens, opts=opts, kv_in=kv_in, backward=backward)
+    decay = None
+    if r.random() < 0.3:  # (after the work list, for the same reason)
+        kind = r.integers(0, 4, H)
+        near_one, anywhere = 1.0 - 0.1 * r.random(H), r.random(H)
+        lam = np.where(kind == 0, 1.0, np.where(kind == 1, 0.0, np.where(kind == 2, near_one, anywhere)))
+        decay = [float(np.float32(x)) for x in lam]
+    return dict(d=d, dtype=dtype, block=block, H=H, lens=lens, opts=opts, kv_in=kv_in, backward=backward, decay=decay)
 
 
 SEEDS = list(range(1000, 2000))
@@ -103,3 +110,22 @@ def test_random_configuration(seed):
         for name, g, r in zip(("dq", "dk", "dv"), got[:3], ref[:3]):
             ErrAcc().add(to_host(g), r).check(fp32, f"seed {seed} {name}")
         ErrAcc().add(to_host(got[3]), ref[3]).check(True, f"seed {seed} dkv_in")
+    if c["decay"] is not None:
+        lam = np.array(c["decay"], np.float32)
+        try:
+            od, kvd = la.prefill(qd, kd, vd, cud, block=block, kv_state_in=kin, decay=to_dev(lam), **opts)
+        except la.LAError as e:
+            # The decayed kernels differ from the plain ones only where they have no room:
+            # no 128-token transpose-read loop (so options chosen for it may not fit the
+            # generic one) and no third tile slot at full width (d = 128, one slice).
+            assert e.status == la.LA_ERR_UNSUPPORTED
+            at_b128 = block == 128 and any(x in opts for x in ("variant", "value_slices", "slots", "seg_len",
+                                                                "work_list"))
+            three_wide = opts.get("slots") == 3 and d == 128
+            assert at_b128 or three_wide, f"seed {seed}: decayed call rejected {c}"
+            log(f"  seed {seed}: decayed call rejected")
+            return
+        torch.cuda.synchronize()
+        o_ref, kv_ref = oracle.recurrent(q, k, v, cu, kv_in=kv_in, decay=lam.astype(np.float64))
+        ErrAcc().add(to_host(od), o_ref).check(fp32, f"seed {seed} decayed o")
+        ErrAcc().add(to_host(kvd), kv_ref).check(fp32, f"seed {seed} decayed kv_state")
