@@ -382,7 +382,7 @@ __global__ __launch_bounds__(kThreads, 1) void la_segment_state_v2(PrefillParams
     auto vbuf = [&](auto slot) -> bf16_t* { if constexpr (decltype(slot)::value == 0) return Vb0; else return Vb1; };
     if (states_reused(p)) return;
     int u, h, s, first, t_end;
-    const int tid = threadIdx.x, lane = tid & 63, li = lane & 15, g = lane >> 4;
+    const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     if (p.packed) {  // state slot u: a whole piece [first, t_end) of one document
         int len;
