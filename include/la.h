@@ -155,8 +155,9 @@ typedef struct {
     int32_t variant;        /* block-loop kernel: 0 = automatic, 1 = the generic loop
                                (every dtype/d/block), 2 = the transpose-read loops
                                (bf16, d >= 64: block 64 with slices of >= 64 columns,
-                               or block 128 with slices of exactly 64 columns, plain
-                               variant only; automatic picks them whenever they apply);
+                               or block 128 with slices of 64 or 128 columns, plain
+                               variant only; automatic picks them whenever they apply,
+                               at block 128 with one slice);
                                an unavailable choice returns LA_ERR_UNSUPPORTED */
     void* main_begin_event; /* hipEvent_t stamped when the block-loop kernel starts
                                executing, or NULL (the kernel is then launched with
